@@ -1,0 +1,12 @@
+"""DFlash draft-verify hot path on AMD MI355X (gfx950).
+
+Python surface of libdflash.so; see include/dflash.h for the contract of each
+call.  Importing does not load the library; the first call does, and raises
+DFlashError if it has not been built.
+"""
+
+from ._lib import (DFlashError, load, ctx_fuse, block_attn, spec_verify,
+                   prepare_ctx_fuse, prepare_block_attn, prepare_spec_verify, EXPORTS)
+
+__all__ = ["DFlashError", "load", "ctx_fuse", "block_attn", "spec_verify",
+           "prepare_ctx_fuse", "prepare_block_attn", "prepare_spec_verify", "EXPORTS"]

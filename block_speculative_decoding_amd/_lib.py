@@ -1,0 +1,320 @@
+"""ctypes binding of libdflash.so (include/dflash.h).
+
+Argument marshalling only: every step of the hot path runs in the HIP
+kernels of the library.  PyTorch provides device memory and the stream.
+The library must be built (``__graft_entry__.build()``); importing works
+without it, but every call raises DFlashError if it is missing.
+"""
+
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdflash.so")
+
+DFLASH_BF16, DFLASH_F32 = 0, 1
+D, NCAPTURE, HQ, HKV, HEAD_DIM, BLOCK, PAGE = 2560, 5, 32, 8, 128, 8, 16
+
+_P = ctypes.c_void_p
+_I32, _I64, _U64, _F32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
+
+
+class DFlashError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"dflash error {code}: {msg}")
+        self.code = code
+
+
+class FuseArgs(ctypes.Structure):
+    _fields_ = [("dtype", _I32), ("num_layers", _I32), ("M", _I64),
+                ("hs", _P * 5), ("hs_stride", _I64),
+                ("wc", _P), ("gc", _P), ("wkv", _P), ("gk", _P),
+                ("eps", _F32), ("rope_theta", _F32),
+                ("pos", _P), ("slot", _P),
+                ("k_cache", _P * 5), ("v_cache", _P * 5), ("num_pages", _I64),
+                ("ht_out", _P)]
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [("dtype", _I32), ("B", _I32),
+                ("q", _P), ("k_blk", _P), ("v_blk", _P), ("gq", _P), ("gk", _P),
+                ("eps", _F32), ("rope_theta", _F32),
+                ("k_cache", _P), ("v_cache", _P), ("num_pages", _I64),
+                ("block_table", _P), ("max_pages", _I32), ("ctx_len", _P),
+                ("page_size", _I32), ("block_len", _I32), ("window", _I32), ("split_tokens", _I32),
+                ("out", _P), ("lse_out", _P)]
+
+
+class VerifyArgs(ctypes.Structure):
+    _fields_ = [("dtype", _I32), ("B", _I32), ("V", _I64),
+                ("target_logits", _P), ("t_batch_stride", _I64), ("t_row_stride", _I64),
+                ("draft_logits", _P), ("d_batch_stride", _I64), ("d_row_stride", _I64),
+                ("draft_tokens", _P), ("temperature", _P),
+                ("seed", _U64), ("offset", _U64),
+                ("out_tokens", _P), ("out_len", _P), ("near_ties", _P)]
+
+
+EXPORTS = ["dflash_version", "dflash_last_error", "dflash_args_size",
+           "dflash_fuse_workspace_size", "dflash_attn_workspace_size", "dflash_verify_workspace_size",
+           "dflash_ctx_fuse", "dflash_block_attn", "dflash_spec_verify"]
+
+_lib = None
+
+
+def load():
+    """Load libdflash.so once; raise DFlashError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise DFlashError(-100, f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.dflash_version.restype = ctypes.c_int
+    lib.dflash_last_error.restype = ctypes.c_char_p
+    lib.dflash_args_size.restype = ctypes.c_size_t
+    lib.dflash_args_size.argtypes = [ctypes.c_int]
+    for name, st in (("fuse", FuseArgs), ("attn", AttnArgs), ("verify", VerifyArgs)):
+        f = getattr(lib, f"dflash_{name}_workspace_size")
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.POINTER(st), ctypes.POINTER(ctypes.c_size_t)]
+    for name, st in (("dflash_ctx_fuse", FuseArgs), ("dflash_block_attn", AttnArgs),
+                     ("dflash_spec_verify", VerifyArgs)):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.POINTER(st), _P, ctypes.c_size_t, _P]
+    for kind, st in enumerate((FuseArgs, AttnArgs, VerifyArgs)):
+        got = lib.dflash_args_size(kind)
+        if got != ctypes.sizeof(st):
+            raise DFlashError(-101, f"struct mirror {st.__name__} is {ctypes.sizeof(st)} bytes, library has {got}")
+    _lib = lib
+    return lib
+
+
+def _check(rc):
+    if rc != 0:
+        raise DFlashError(rc, load().dflash_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return DFLASH_BF16
+    if t.dtype == torch.float32:
+        return DFLASH_F32
+    raise DFlashError(-2, f"unsupported tensor dtype {t.dtype}")
+
+
+def _need(t, name, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise DFlashError(-1, f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise DFlashError(-1, f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise DFlashError(-1, f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise DFlashError(-1, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise DFlashError(-1, f"{name} must be contiguous")
+    return t
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(nbytes, workspace, device):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise DFlashError(-4, f"workspace holds {workspace.numel() * workspace.element_size()} bytes, {nbytes} needed")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+class Prepared:
+    """A validated argument struct plus its workspace: call it to enqueue."""
+
+    def __init__(self, fn, args, workspace, ws_bytes, keep):
+        self._fn, self.args, self.workspace, self.ws_bytes = fn, args, workspace, ws_bytes
+        self._keep = keep  # tensors the struct points into
+
+    def __call__(self, stream=None):
+        _check(self._fn(ctypes.byref(self.args), _ptr(self.workspace), self.ws_bytes, _stream(stream)))
+
+
+# ---------------------------------------------------------------- ctx_fuse
+def prepare_ctx_fuse(hs, wc, gc, wkv, gk, pos, slot, k_caches, v_caches, eps=1e-6, rope_theta=1e6,
+                     ht_out=None, workspace=None):
+    """Context fusion + K/V injection (include/dflash.h, dflash_ctx_fuse).
+
+    hs: 5 tensors [M, >=2560] (row stride from the tensor); wc [2560, 12800];
+    gc [2560]; wkv [L*2048, 2560]; gk [L, 128]; pos int32 [M]; slot int64 [M];
+    k_caches / v_caches: L tensors [num_pages, 8, 2048] in the page layout.
+    """
+    lib = load()
+    if len(hs) != NCAPTURE:
+        raise DFlashError(-1, "hs must hold five tensors")
+    dt = hs[0].dtype
+    M = hs[0].shape[0]
+    for i, h in enumerate(hs):
+        if not h.is_cuda or h.dtype != dt or h.dim() != 2 or h.shape[0] != M or h.stride(1) != 1 \
+                or h.stride(0) != hs[0].stride(0) or h.shape[1] < D:
+            raise DFlashError(-1, f"hs[{i}] must be a device [M, >=2560] tensor with unit column stride, "
+                                  "dtype and row stride equal to hs[0]")
+    L = len(k_caches)
+    if len(v_caches) != L or not 1 <= L <= 5:
+        raise DFlashError(-1, "k_caches and v_caches need the same length in 1..5")
+    _need(wc, "wc", dt, (D, NCAPTURE * D))
+    _need(gc, "gc", dt, (D,))
+    _need(wkv, "wkv", dt, (L * 2048, D))
+    _need(gk, "gk", dt, (L, HEAD_DIM))
+    _need(pos, "pos", torch.int32, (M,))
+    _need(slot, "slot", torch.int64, (M,))
+    npages = k_caches[0].shape[0]
+    for i in range(L):
+        _need(k_caches[i], f"k_caches[{i}]", dt, (npages, HKV, 2048))
+        _need(v_caches[i], f"v_caches[{i}]", dt, (npages, HKV, 2048))
+    if ht_out is not None:
+        _need(ht_out, "ht_out", dt, (M, D))
+    a = FuseArgs()
+    a.dtype = _dtype_code(hs[0])
+    a.num_layers = L
+    a.M = M
+    for i in range(5):
+        a.hs[i] = hs[i].data_ptr()
+    a.hs_stride = hs[0].stride(0)
+    a.wc, a.gc, a.wkv, a.gk = wc.data_ptr(), gc.data_ptr(), wkv.data_ptr(), gk.data_ptr()
+    a.eps, a.rope_theta = eps, rope_theta
+    a.pos, a.slot = pos.data_ptr(), slot.data_ptr()
+    for i in range(L):
+        a.k_cache[i] = k_caches[i].data_ptr()
+        a.v_cache[i] = v_caches[i].data_ptr()
+    a.num_pages = npages
+    a.ht_out = None if ht_out is None else ht_out.data_ptr()
+    nbytes = ctypes.c_size_t()
+    _check(lib.dflash_fuse_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
+    ws, wsb = _workspace(nbytes.value, workspace, hs[0].device)
+    return Prepared(lib.dflash_ctx_fuse, a, ws, wsb,
+                    (list(hs), wc, gc, wkv, gk, pos, slot, list(k_caches), list(v_caches), ht_out))
+
+
+def ctx_fuse(*args, stream=None, **kw):
+    prepare_ctx_fuse(*args, **kw)(stream)
+
+
+# ---------------------------------------------------------------- block_attn
+def prepare_block_attn(q, k_blk, v_blk, gq, gk, k_cache, v_cache, block_table, ctx_len, out=None,
+                       lse_out=None, eps=1e-6, rope_theta=1e6, window=0, split_tokens=0, workspace=None):
+    """One draft layer's block attention (include/dflash.h, dflash_block_attn).
+
+    q [B,32,8,128]; k_blk, v_blk [B,8,8,128]; gq, gk [128]; caches
+    [num_pages, 8, 2048] in the page layout; block_table int32 [B, max_pages];
+    ctx_len int32 [B]; out [B,32,8,128] (allocated if None); lse_out float32
+    [B,32,8] or None.
+    """
+    lib = load()
+    dt = q.dtype
+    B = q.shape[0]
+    _need(q, "q", dt, (B, HQ, BLOCK, HEAD_DIM))
+    _need(k_blk, "k_blk", dt, (B, HKV, BLOCK, HEAD_DIM))
+    _need(v_blk, "v_blk", dt, (B, HKV, BLOCK, HEAD_DIM))
+    _need(gq, "gq", dt, (HEAD_DIM,))
+    _need(gk, "gk", dt, (HEAD_DIM,))
+    npages = k_cache.shape[0]
+    _need(k_cache, "k_cache", dt, (npages, HKV, 2048))
+    _need(v_cache, "v_cache", dt, (npages, HKV, 2048))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise DFlashError(-1, "block_table must be [B, max_pages]")
+    _need(ctx_len, "ctx_len", torch.int32, (B,))
+    if out is None:
+        out = torch.empty((B, HQ, BLOCK, HEAD_DIM), dtype=dt, device=q.device)
+    _need(out, "out", dt, (B, HQ, BLOCK, HEAD_DIM))
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, (B, HQ, BLOCK))
+    a = AttnArgs()
+    a.dtype = _dtype_code(q)
+    a.B = B
+    a.q, a.k_blk, a.v_blk = q.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr()
+    a.gq, a.gk = gq.data_ptr(), gk.data_ptr()
+    a.eps, a.rope_theta = eps, rope_theta
+    a.k_cache, a.v_cache, a.num_pages = k_cache.data_ptr(), v_cache.data_ptr(), npages
+    a.block_table, a.max_pages, a.ctx_len = block_table.data_ptr(), block_table.shape[1], ctx_len.data_ptr()
+    a.page_size, a.block_len, a.window, a.split_tokens = PAGE, BLOCK, window, split_tokens
+    a.out = out.data_ptr()
+    a.lse_out = None if lse_out is None else lse_out.data_ptr()
+    nbytes = ctypes.c_size_t()
+    _check(lib.dflash_attn_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
+    ws, wsb = _workspace(nbytes.value, workspace, q.device)
+    prep = Prepared(lib.dflash_block_attn, a, ws, wsb,
+                    (q, k_blk, v_blk, gq, gk, k_cache, v_cache, block_table, ctx_len, out, lse_out))
+    prep.out = out
+    return prep
+
+
+def block_attn(*args, stream=None, **kw):
+    prep = prepare_block_attn(*args, **kw)
+    prep(stream)
+    return prep.out
+
+
+# ---------------------------------------------------------------- spec_verify
+def prepare_spec_verify(target_logits, draft_logits, draft_tokens, temperature, seed=0, offset=0,
+                        out_tokens=None, out_len=None, near_ties=None, workspace=None):
+    """Exact speculative verification (include/dflash.h, dflash_spec_verify).
+
+    target_logits [B, 8, V] and draft_logits [B, 7, V] (last dim contiguous;
+    any 16-byte-aligned row/batch strides); draft_tokens int32 [B, 7];
+    temperature float32 [B] (<= 0: greedy).  Outputs int32 [B, 8], int32 [B]
+    and a uint64-sized int64 [1] near-tie counter (allocated if None).
+    """
+    lib = load()
+    dt = target_logits.dtype
+    B, R, V = target_logits.shape
+    if R != 8 or tuple(draft_logits.shape) != (B, 7, V) or draft_logits.dtype != dt:
+        raise DFlashError(-1, "target_logits must be [B, 8, V] and draft_logits [B, 7, V] of one dtype")
+    for n, t in (("target_logits", target_logits), ("draft_logits", draft_logits)):
+        if not t.is_cuda or t.stride(2) != 1:
+            raise DFlashError(-1, f"{n} must be a device tensor with a contiguous last dim")
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, 7))
+    _need(temperature, "temperature", torch.float32, (B,))
+    dev = target_logits.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, 8), dtype=torch.int32, device=dev)
+    if out_len is None:
+        out_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if near_ties is None:
+        near_ties = torch.zeros((1,), dtype=torch.int64, device=dev)
+    _need(out_tokens, "out_tokens", torch.int32, (B, 8))
+    _need(out_len, "out_len", torch.int32, (B,))
+    _need(near_ties, "near_ties", torch.int64, (1,))
+    a = VerifyArgs()
+    a.dtype = _dtype_code(target_logits)
+    a.B, a.V = B, V
+    a.target_logits = target_logits.data_ptr()
+    a.t_batch_stride, a.t_row_stride = target_logits.stride(0), target_logits.stride(1)
+    a.draft_logits = draft_logits.data_ptr()
+    a.d_batch_stride, a.d_row_stride = draft_logits.stride(0), draft_logits.stride(1)
+    a.draft_tokens, a.temperature = draft_tokens.data_ptr(), temperature.data_ptr()
+    a.seed, a.offset = int(seed), int(offset)
+    a.out_tokens, a.out_len, a.near_ties = out_tokens.data_ptr(), out_len.data_ptr(), near_ties.data_ptr()
+    nbytes = ctypes.c_size_t()
+    _check(lib.dflash_verify_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
+    ws, wsb = _workspace(nbytes.value, workspace, dev)
+    prep = Prepared(lib.dflash_spec_verify, a, ws, wsb,
+                    (target_logits, draft_logits, draft_tokens, temperature, out_tokens, out_len, near_ties))
+    prep.outputs = (out_tokens, out_len, near_ties)
+    return prep
+
+
+def spec_verify(*args, stream=None, **kw):
+    prep = prepare_spec_verify(*args, **kw)
+    prep(stream)
+    return prep.outputs

@@ -1,0 +1,62 @@
+"""Build libdflash.so (gfx950) in-tree with hipcc.
+
+Every call recompiles: each source in csrc/ becomes an object under _build/,
+then the objects are linked into block_speculative_decoding_amd/libdflash.so.
+"""
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OUT_DIR = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libdflash.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+# Packed fp32 VALU ops are disabled for all device code.
+DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I" + os.path.join(ROOT, "include")]
+
+SOURCES = ["api.cpp", "verify.hip", "attn.hip", "fuse.hip"]
+
+
+def _compile(src):
+    obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC] + COMMON
+    if src.endswith(".hip"):
+        cmd += DEVICE_FLAGS
+    cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the device-only feature flag; drop that note.
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    return src, obj, r.returncode, err
+
+
+def build_library(verbose=True):
+    os.makedirs(OUT_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+        results = list(ex.map(_compile, SOURCES))
+    objs = []
+    for src, obj, rc, err in results:
+        if err.strip() and verbose:
+            print(f"[build] {src}:\n{err}", file=sys.stderr)
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{err}")
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"[build] wrote {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build_library()

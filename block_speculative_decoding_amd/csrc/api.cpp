@@ -1,0 +1,215 @@
+// C ABI of libdflash: argument validation, workspace sizing and launch.
+// The operations themselves are documented in include/dflash.h.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/dflash.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return DFLASH_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                                  \
+    do {                                                                                \
+        if (!(p)) return fail(DFLASH_EINVAL, "%s: null pointer " #p, fn);               \
+        if (!aligned16(p)) return fail(DFLASH_EINVAL, "%s: " #p " is not 16-byte aligned", fn); \
+    } while (0)
+
+int check_dtype(const char* fn, int dtype) {
+    if (dtype != DFLASH_BF16 && dtype != DFLASH_F32)
+        return fail(DFLASH_EUNSUPPORTED, "%s: unsupported dtype %d", fn, dtype);
+    return DFLASH_OK;
+}
+
+int check_ws(const char* fn, size_t need, const void* ws, size_t have) {
+    if (need == 0) return DFLASH_OK;
+    if (!ws) return fail(DFLASH_EWORKSPACE, "%s: workspace of %zu bytes required, got NULL", fn, need);
+    if (have < need) return fail(DFLASH_EWORKSPACE, "%s: workspace of %zu bytes required, got %zu", fn, need, have);
+    if (!aligned16(ws)) return fail(DFLASH_EWORKSPACE, "%s: workspace is not 16-byte aligned", fn);
+    return DFLASH_OK;
+}
+
+int launched(const char* fn, hipError_t e) {
+    if (e != hipSuccess) return fail(DFLASH_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+// ---------------------------------------------------------------- sizes
+int validate_fuse_sizes(const char* fn, const dflash_fuse_args* a) {
+    if (!a) return fail(DFLASH_EINVAL, "%s: null args", fn);
+    int rc = check_dtype(fn, a->dtype);
+    if (rc) return rc;
+    if (a->num_layers < 1 || a->num_layers > DFLASH_MAX_LAYERS)
+        return fail(DFLASH_EINVAL, "%s: num_layers %d outside [1, %d]", fn, a->num_layers, DFLASH_MAX_LAYERS);
+    if (a->M < 0 || a->M > (1 << 24)) return fail(DFLASH_EINVAL, "%s: M %lld outside [0, 2^24]", fn, (long long)a->M);
+    return DFLASH_OK;
+}
+
+int validate_attn_sizes(const char* fn, const dflash_attn_args* a) {
+    if (!a) return fail(DFLASH_EINVAL, "%s: null args", fn);
+    int rc = check_dtype(fn, a->dtype);
+    if (rc) return rc;
+    if (a->B < 1 || a->B > 65535) return fail(DFLASH_EINVAL, "%s: B %d outside [1, 65535]", fn, a->B);
+    if (a->max_pages < 1 || (int64_t)a->max_pages * DFLASH_PAGE > INT_MAX / 2)
+        return fail(DFLASH_EINVAL, "%s: max_pages %d out of range", fn, a->max_pages);
+    if (a->page_size != DFLASH_PAGE) return fail(DFLASH_EINVAL, "%s: page_size must be 16 (got %d)", fn, a->page_size);
+    if (a->block_len != DFLASH_BLOCK) return fail(DFLASH_EINVAL, "%s: block_len must be 8 (got %d)", fn, a->block_len);
+    if (a->window < 0) return fail(DFLASH_EINVAL, "%s: negative window", fn);
+    if (a->split_tokens < 0 || a->split_tokens % 128 != 0)
+        return fail(DFLASH_EINVAL, "%s: split_tokens must be 0 or a positive multiple of 128 (got %d)", fn,
+                    a->split_tokens);
+    return DFLASH_OK;
+}
+
+int validate_verify_sizes(const char* fn, const dflash_verify_args* a) {
+    if (!a) return fail(DFLASH_EINVAL, "%s: null args", fn);
+    int rc = check_dtype(fn, a->dtype);
+    if (rc) return rc;
+    if (a->B < 1 || a->B > (1 << 20)) return fail(DFLASH_EINVAL, "%s: B %d outside [1, 2^20]", fn, a->B);
+    if (a->V < 8 || a->V > INT_MAX / 2 || a->V % 8 != 0)
+        return fail(DFLASH_EINVAL, "%s: V %lld must be a positive multiple of 8 below 2^30", fn, (long long)a->V);
+    return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dflash_version(void) { return DFLASH_VERSION; }
+
+const char* dflash_last_error(void) { return g_err.c_str(); }
+
+size_t dflash_args_size(int kind) {
+    switch (kind) {
+        case 0: return sizeof(dflash_fuse_args);
+        case 1: return sizeof(dflash_attn_args);
+        case 2: return sizeof(dflash_verify_args);
+        default: return 0;
+    }
+}
+
+int dflash_fuse_workspace_size(const dflash_fuse_args* a, size_t* bytes) {
+    const char* fn = "dflash_fuse_workspace_size";
+    if (!bytes) return fail(DFLASH_EINVAL, "%s: null output", fn);
+    int rc = validate_fuse_sizes(fn, a);
+    if (rc) return rc;
+    *bytes = a->M == 0 ? 0 : dflash::fuse_plan(*a).ws_bytes;
+    return ok();
+}
+
+int dflash_attn_workspace_size(const dflash_attn_args* a, size_t* bytes) {
+    const char* fn = "dflash_attn_workspace_size";
+    if (!bytes) return fail(DFLASH_EINVAL, "%s: null output", fn);
+    int rc = validate_attn_sizes(fn, a);
+    if (rc) return rc;
+    *bytes = dflash::attn_plan(*a).ws_bytes;
+    return ok();
+}
+
+int dflash_verify_workspace_size(const dflash_verify_args* a, size_t* bytes) {
+    const char* fn = "dflash_verify_workspace_size";
+    if (!bytes) return fail(DFLASH_EINVAL, "%s: null output", fn);
+    int rc = validate_verify_sizes(fn, a);
+    if (rc) return rc;
+    *bytes = dflash::verify_workspace_bytes(a->B, a->V);
+    return ok();
+}
+
+int dflash_ctx_fuse(const dflash_fuse_args* a, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "dflash_ctx_fuse";
+    int rc = validate_fuse_sizes(fn, a);
+    if (rc) return rc;
+    if (a->M == 0) return ok();
+    for (int i = 0; i < DFLASH_NCAPTURE; ++i)
+        if (!a->hs[i] || !aligned16(a->hs[i])) return fail(DFLASH_EINVAL, "%s: hs[%d] null or not 16-byte aligned", fn, i);
+    if (a->hs_stride < DFLASH_D || a->hs_stride % 8 != 0)
+        return fail(DFLASH_EINVAL, "%s: hs_stride %lld must be >= 2560 and a multiple of 8", fn, (long long)a->hs_stride);
+    REQUIRE_PTR(a->wc);
+    REQUIRE_PTR(a->gc);
+    REQUIRE_PTR(a->wkv);
+    REQUIRE_PTR(a->gk);
+    REQUIRE_PTR(a->pos);
+    REQUIRE_PTR(a->slot);
+    for (int l = 0; l < a->num_layers; ++l)
+        if (!a->k_cache[l] || !a->v_cache[l] || !aligned16(a->k_cache[l]) || !aligned16(a->v_cache[l]))
+            return fail(DFLASH_EINVAL, "%s: cache pointers of layer %d null or not 16-byte aligned", fn, l);
+    if (a->ht_out && !aligned16(a->ht_out)) return fail(DFLASH_EINVAL, "%s: ht_out is not 16-byte aligned", fn);
+    if (a->num_pages < 1) return fail(DFLASH_EINVAL, "%s: num_pages must be >= 1", fn);
+    if (!(a->eps > 0.f)) return fail(DFLASH_EINVAL, "%s: eps must be > 0", fn);
+    if (!(a->rope_theta > 1.f)) return fail(DFLASH_EINVAL, "%s: rope_theta must be > 1", fn);
+    const dflash::FusePlan pl = dflash::fuse_plan(*a);
+    rc = check_ws(fn, pl.ws_bytes, ws, ws_bytes);
+    if (rc) return rc;
+    return launched(fn, dflash::launch_fuse(*a, pl, ws, static_cast<hipStream_t>(stream)));
+}
+
+int dflash_block_attn(const dflash_attn_args* a, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "dflash_block_attn";
+    int rc = validate_attn_sizes(fn, a);
+    if (rc) return rc;
+    REQUIRE_PTR(a->q);
+    REQUIRE_PTR(a->k_blk);
+    REQUIRE_PTR(a->v_blk);
+    REQUIRE_PTR(a->gq);
+    REQUIRE_PTR(a->gk);
+    REQUIRE_PTR(a->k_cache);
+    REQUIRE_PTR(a->v_cache);
+    REQUIRE_PTR(a->block_table);
+    REQUIRE_PTR(a->ctx_len);
+    REQUIRE_PTR(a->out);
+    if (a->lse_out && !aligned16(a->lse_out)) return fail(DFLASH_EINVAL, "%s: lse_out is not 16-byte aligned", fn);
+    if (a->num_pages < 1) return fail(DFLASH_EINVAL, "%s: num_pages must be >= 1", fn);
+    if (!(a->eps > 0.f)) return fail(DFLASH_EINVAL, "%s: eps must be > 0", fn);
+    if (!(a->rope_theta > 1.f)) return fail(DFLASH_EINVAL, "%s: rope_theta must be > 1", fn);
+    const dflash::AttnPlan pl = dflash::attn_plan(*a);
+    rc = check_ws(fn, pl.ws_bytes, ws, ws_bytes);
+    if (rc) return rc;
+    return launched(fn, dflash::launch_attn(*a, pl, ws, static_cast<hipStream_t>(stream)));
+}
+
+int dflash_spec_verify(const dflash_verify_args* a, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "dflash_spec_verify";
+    int rc = validate_verify_sizes(fn, a);
+    if (rc) return rc;
+    REQUIRE_PTR(a->target_logits);
+    REQUIRE_PTR(a->draft_logits);
+    REQUIRE_PTR(a->draft_tokens);
+    REQUIRE_PTR(a->temperature);
+    REQUIRE_PTR(a->out_tokens);
+    REQUIRE_PTR(a->out_len);
+    if (!a->near_ties) return fail(DFLASH_EINVAL, "%s: null pointer near_ties", fn);
+    if (a->t_row_stride < a->V || a->d_row_stride < a->V)
+        return fail(DFLASH_EINVAL, "%s: row strides must be >= V", fn);
+    if (a->t_batch_stride < 0 || a->d_batch_stride < 0)
+        return fail(DFLASH_EINVAL, "%s: negative batch stride", fn);
+    if ((a->t_row_stride | a->d_row_stride | a->t_batch_stride | a->d_batch_stride) % 8 != 0)
+        return fail(DFLASH_EINVAL, "%s: strides must be multiples of 8 elements", fn);
+    const size_t need = dflash::verify_workspace_bytes(a->B, a->V);
+    rc = check_ws(fn, need, ws, ws_bytes);
+    if (rc) return rc;
+    return launched(fn, dflash::launch_verify(*a, ws, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

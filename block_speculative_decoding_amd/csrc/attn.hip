@@ -1,0 +1,527 @@
+// Non-causal draft block attention over a paged, injected KV cache (gfx950).
+//
+// Follows "Nemotron 3.5 Bolt E4B: Block-Parallel Speculation with DFlash",
+// section "Five target states become persistent draft context": Q [B,32,8,128],
+// K/V [B,8,8,128], four query heads per KV head, per-head Q/K RMSNorm before
+// RoPE; the block attends bidirectionally over the cached context followed
+// by its own eight keys ("DFlash & DFlash2" 4.1: K = [K_ctx ; K_blk]).
+//
+// bf16 design.  One workgroup (4 waves) owns (sequence b, KV head g, split c).
+// The 4 query heads x 8 positions of KV head g form 32 query rows, so each
+// 32-token tile is two dense 32x32 products on the matrix cores:
+//     S^T[32 tok x 32 rows] = K[32 x 128] . Q^T        (8 x mfma 32x32x16)
+//     O^T[128 x 32 rows]   += V^T[128 x 32] . P^T      (8 x mfma 32x32x16)
+// The page layouts (see include/dflash.h) put each lane's operand bytes in
+// one 16-byte run and make each wave-wide load one contiguous 512 B / 1 KiB
+// run, so K and V go from HBM straight into operand registers.  A lane of
+// S^T owns one query row and 16 of the 32 tokens, so the softmax row
+// reductions need a single cross-half exchange.  Waves take tiles
+// round-robin; the block's own 8 keys are one extra (masked) tile of the
+// last split.  Waves merge through LDS; splits merge with a log-sum-exp
+// kernel.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace dflash {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kTile = 32;
+constexpr int kQStride = 136;    // bf16 per LDS row of q^ / k^blk (padded)
+constexpr int kAccStride = 132;  // floats per LDS row in the wave merge
+constexpr int kPartFloats = 64 + 32 * 128;  // m[32], l[32], acc[32][128]
+
+struct AttnParams {
+    const void* q; const void* kb; const void* vb; const void* gq; const void* gk;
+    float eps; float theta;
+    const void* kc; const void* vc; int64_t num_pages;
+    const int32_t* bt; int max_pages;
+    const int32_t* ctx_len;
+    int window; int split; int nsplit;
+    void* out; float* lse;
+    float* part;
+};
+
+struct SeqRange { int S, t0, a0, nspl; };
+
+__device__ __forceinline__ SeqRange seq_range(const AttnParams& p, int b) {
+    SeqRange r;
+    int S = p.ctx_len[b];
+    const int cap = p.max_pages * 16;
+    S = S < 0 ? 0 : (S > cap ? cap : S);
+    r.S = S;
+    r.t0 = p.window > 0 ? max(0, S - p.window) : 0;
+    r.a0 = r.t0 & ~(kTile - 1);
+    const int n = S - r.a0;
+    r.nspl = n <= 0 ? 1 : (n + p.split - 1) / p.split;
+    return r;
+}
+
+// cos/sin of pos * theta^(-i/64): angle and range reduction in fp64, then fp32.
+__device__ __forceinline__ void rope_cs(int pos, int i, double log2_theta, float& c, float& s) {
+    const double inv_freq = exp2(-(double)i * (1.0 / 64.0) * log2_theta);
+    double ang = (double)pos * inv_freq;
+    const double two_pi = 6.283185307179586;
+    ang -= rint(ang * (1.0 / two_pi)) * two_pi;
+    sincosf((float)ang, &s, &c);
+}
+
+// Normalise + rotate one 128-wide row spread over 8 consecutive lanes; lane
+// part p holds dims [8p, 8p+8) in x[0..7] and [64+8p, 64+8p+8) in x[8..15].
+__device__ __forceinline__ void norm_rope_16(float* x, const float* g, int part, int pos,
+                                             float eps, double log2_theta) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ss += x[e] * x[e];
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    ss += __shfl_xor(ss, 4);
+    const float rinv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + eps);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float a = x[e] * rinv * g[e];
+        const float bb = x[8 + e] * rinv * g[8 + e];
+        float c, s;
+        rope_cs(pos, 8 * part + e, log2_theta, c, s);
+        x[e] = a * c - bb * s;
+        x[8 + e] = bb * c + a * s;
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void load_row16(const T* row, int part, float* x) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        x[e] = Elem<T>::load(row, 8 * part + e);
+        x[8 + e] = Elem<T>::load(row, 64 + 8 * part + e);
+    }
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+// ---------------------------------------------------------------- bf16 MFMA kernel
+__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnParams p) {
+    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const SeqRange sr = seq_range(p, b);
+    if (c >= sr.nspl) return;
+    const int tb = sr.a0 + c * p.split;
+    const int te = min(sr.S, tb + p.split);
+    const bool last = c == sr.nspl - 1;
+    const int ntiles = te > tb ? (te - tb + kTile - 1) / kTile : 0;
+    const int nwork = ntiles + (last ? 1 : 0);
+
+    __shared__ __attribute__((aligned(16))) float smem[kWaves * (64 + 32 * kAccStride)];
+    uint16_t* qs = reinterpret_cast<uint16_t*>(smem);          // [32][kQStride]
+    uint16_t* kbs = qs + 32 * kQStride;                         // [8][kQStride]
+    uint16_t* vbs = kbs + 8 * kQStride;                         // [8][128]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const double log2_theta = log2((double)p.theta);
+    const uint16_t* gq = static_cast<const uint16_t*>(p.gq);
+    const uint16_t* gk = static_cast<const uint16_t*>(p.gk);
+
+    // ---- prologue: q^ for 32 rows, k^blk / v_blk of head g into LDS
+    {
+        const int n = tid >> 3, part = tid & 7;  // row n = hh*8 + j
+        const int hh = n >> 3, j = n & 7;
+        const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
+                               ((((int64_t)b * 32 + 4 * g + hh) * 8 + j) * 128);
+        float x[16], gw[16];
+        load_row16(qrow, part, x);
+        load_row16(gq, part, gw);
+        norm_rope_16(x, gw, part, sr.S + j, p.eps, log2_theta);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            qs[n * kQStride + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[e]);
+            qs[n * kQStride + 64 + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[8 + e]);
+        }
+        if (tid < 64) {
+            const int jj = tid >> 3;
+            const uint16_t* krow = static_cast<const uint16_t*>(p.kb) + ((((int64_t)b * 8 + g) * 8 + jj) * 128);
+            load_row16(krow, part, x);
+            load_row16(gk, part, gw);
+            norm_rope_16(x, gw, part, sr.S + jj, p.eps, log2_theta);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kbs[jj * kQStride + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[e]);
+                kbs[jj * kQStride + 64 + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[8 + e]);
+            }
+        } else if (tid < 128) {
+            const int t2 = tid - 64;  // 64 threads x 16 B = 2 KiB of v_blk
+            const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.vb) +
+                                                              (((int64_t)b * 8 + g) * 8 * 128));
+            reinterpret_cast<uint4*>(vbs)[t2] = src[t2];
+        }
+    }
+    __syncthreads();
+
+    const int m32 = lane & 31, hl = lane >> 5;
+    bf16x8 qop[8];
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+        qop[kb] = *reinterpret_cast<const bf16x8*>(qs + m32 * kQStride + 64 * hl + 8 * kb);
+
+    const float sl2 = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
+    const uint16_t* kc = static_cast<const uint16_t*>(p.kc);
+    const uint16_t* vc = static_cast<const uint16_t*>(p.vc);
+    const int32_t* bt = p.bt + (int64_t)b * p.max_pages;
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[db] = (f32x16){};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    for (int it = wave; it < nwork; it += kWaves) {
+        bf16x8 kop[8], vop[2][4];
+        const bool blk = it >= ntiles;  // the block's own keys
+        const int T0 = tb + it * kTile;
+        if (!blk) {
+            int phys[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int pg = (T0 >> 4) + h2;
+                int ph = -1;
+                if (pg * 16 < te) ph = bt[pg];
+                phys[h2] = (ph >= 0 && (int64_t)ph < p.num_pages) ? ph : -1;
+            }
+            const int myk = phys[m32 >> 4];
+            if (myk >= 0) {
+                const uint4* kp = reinterpret_cast<const uint4*>(
+                    kc + ((int64_t)myk * 8 + g) * 2048 + 8 * ((m32 & 15) + 16 * hl));
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) kop[kb] = as_bf16x8(kp[32 * kb]);
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) kop[kb] = as_bf16x8(make_uint4(0, 0, 0, 0));
+            }
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                const int ph = phys[kb2];
+                if (ph >= 0) {
+                    const uint4* vp = reinterpret_cast<const uint4*>(
+                        vc + ((int64_t)ph * 8 + g) * 2048 + 256 * hl + 8 * m32);
+                    uint4 w[4];
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) w[db] = vp[64 * db];
+                    // Slots at or past the sequence end may hold garbage: zero them.
+                    const int tbase = T0 + 16 * kb2 + 4 * hl;  // tokens tbase+{0,1,2,3}, tbase+8+{0..3}
+                    if (tbase + 11 >= te) {
+#pragma unroll
+                        for (int db = 0; db < 4; ++db) {
+                            if (tbase + 0 >= te) w[db].x &= 0xFFFF0000u;
+                            if (tbase + 1 >= te) w[db].x &= 0x0000FFFFu;
+                            if (tbase + 2 >= te) w[db].y &= 0xFFFF0000u;
+                            if (tbase + 3 >= te) w[db].y &= 0x0000FFFFu;
+                            if (tbase + 8 >= te) w[db].z &= 0xFFFF0000u;
+                            if (tbase + 9 >= te) w[db].z &= 0x0000FFFFu;
+                            if (tbase + 10 >= te) w[db].w &= 0xFFFF0000u;
+                            if (tbase + 11 >= te) w[db].w &= 0x0000FFFFu;
+                        }
+                    }
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) vop[kb2][db] = as_bf16x8(w[db]);
+                } else {
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) vop[kb2][db] = as_bf16x8(make_uint4(0, 0, 0, 0));
+                }
+            }
+        } else {
+            if (m32 < 8) {
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb)
+                    kop[kb] = *reinterpret_cast<const bf16x8*>(kbs + m32 * kQStride + 64 * hl + 8 * kb);
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) kop[kb] = as_bf16x8(make_uint4(0, 0, 0, 0));
+            }
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const int d = 32 * db + m32;
+                uint4 w;
+                w.x = (uint32_t)vbs[(4 * hl + 0) * 128 + d] | ((uint32_t)vbs[(4 * hl + 1) * 128 + d] << 16);
+                w.y = (uint32_t)vbs[(4 * hl + 2) * 128 + d] | ((uint32_t)vbs[(4 * hl + 3) * 128 + d] << 16);
+                w.z = 0;
+                w.w = 0;
+                vop[0][db] = as_bf16x8(w);
+                vop[1][db] = as_bf16x8(make_uint4(0, 0, 0, 0));
+            }
+        }
+
+        // S^T = K . Q^T  (rows: tokens of the tile, columns: the 32 query rows)
+        f32x16 s = {};
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kb], qop[kb], s, 0, 0, 0);
+
+        // Lane holds query row m32 and tokens 8*jj + 4*hl + r  (register 4*jj + r).
+        float pv[16];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int tok = 8 * (r >> 2) + 4 * hl + (r & 3);
+            bool valid;
+            if (blk) valid = tok < 8;
+            else {
+                const int t = T0 + tok;
+                valid = t >= sr.t0 && t < te;
+            }
+            pv[r] = valid ? s[r] * sl2 : -INFINITY;
+            tmax = fmaxf(tmax, pv[r]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_new = fmaxf(m_run, tmax);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        uint32_t pk[8];
+        float rs = 0.f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(pv[2 * r] - m_use),
+                                           __builtin_amdgcn_exp2f(pv[2 * r + 1] - m_use));
+            pk[r] = w;
+            rs += lo_bf16(w) + hi_bf16(w);
+        }
+        rs += __shfl_xor(rs, 32);
+        l_run = l_run * alpha + rs;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+        const bf16x8 pb0 = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+        const bf16x8 pb1 = as_bf16x8(make_uint4(pk[4], pk[5], pk[6], pk[7]));
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[0][db], pb0, acc[db], 0, 0, 0);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[1][db], pb1, acc[db], 0, 0, 0);
+        }
+    }
+
+    // ---- merge the four waves through LDS
+    __syncthreads();
+    float* wm = smem + wave * (64 + 32 * kAccStride);
+    if (hl == 0) { wm[m32] = m_run; wm[32 + m32] = l_run; }
+    float* wacc = wm + 64;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            wacc[m32 * kAccStride + 32 * db + 8 * (r >> 2) + 4 * hl + (r & 3)] = acc[db][r];
+    __syncthreads();
+
+    const int n = tid >> 3, d0 = 16 * (tid & 7);
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, smem[w * (64 + 32 * kAccStride) + n]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float L = 0.f, o[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const float* base = smem + w * (64 + 32 * kAccStride);
+        const float f = __builtin_amdgcn_exp2f(base[n] - Mu);
+        L += base[32 + n] * f;
+        const float4* av = reinterpret_cast<const float4*>(base + 64 + n * kAccStride + d0);
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const float4 v = av[e4];
+            o[4 * e4 + 0] += f * v.x; o[4 * e4 + 1] += f * v.y;
+            o[4 * e4 + 2] += f * v.z; o[4 * e4 + 3] += f * v.w;
+        }
+    }
+    if (sr.nspl == 1) {
+        const float inv = 1.0f / L;
+        uint16_t* orow = static_cast<uint16_t*>(p.out) + ((((int64_t)b * 32 + 4 * g + (n >> 3)) * 8 + (n & 7)) * 128) + d0;
+        uint4 w0, w1;
+        w0.x = pack_bf16x2(o[0] * inv, o[1] * inv);   w0.y = pack_bf16x2(o[2] * inv, o[3] * inv);
+        w0.z = pack_bf16x2(o[4] * inv, o[5] * inv);   w0.w = pack_bf16x2(o[6] * inv, o[7] * inv);
+        w1.x = pack_bf16x2(o[8] * inv, o[9] * inv);   w1.y = pack_bf16x2(o[10] * inv, o[11] * inv);
+        w1.z = pack_bf16x2(o[12] * inv, o[13] * inv); w1.w = pack_bf16x2(o[14] * inv, o[15] * inv);
+        reinterpret_cast<uint4*>(orow)[0] = w0;
+        reinterpret_cast<uint4*>(orow)[1] = w1;
+        if (p.lse && (tid & 7) == 0)
+            p.lse[((int64_t)b * 32 + 4 * g + (n >> 3)) * 8 + (n & 7)] = (Mu + log2f(L)) * kLn2;
+    } else {
+        float* pp = p.part + (((int64_t)b * 8 + g) * p.nsplit + c) * kPartFloats;
+        if ((tid & 7) == 0) { pp[n] = M; pp[32 + n] = L; }
+        float4* dst = reinterpret_cast<float4*>(pp + 64 + n * 128 + d0);
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+            dst[e4] = make_float4(o[4 * e4], o[4 * e4 + 1], o[4 * e4 + 2], o[4 * e4 + 3]);
+    }
+}
+
+// ---------------------------------------------------------------- split merge
+template <typename T>
+__global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnParams p) {
+    const int g = blockIdx.x, b = blockIdx.y;
+    const SeqRange sr = seq_range(p, b);
+    if (sr.nspl <= 1) return;
+    const int tid = threadIdx.x;
+    const int n = tid >> 3, d0 = 16 * (tid & 7);
+    const float* base = p.part + ((int64_t)b * 8 + g) * p.nsplit * kPartFloats;
+    float M = -INFINITY;
+    for (int c = 0; c < sr.nspl; ++c) M = fmaxf(M, base[c * kPartFloats + n]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float L = 0.f, o[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] = 0.f;
+    for (int c = 0; c < sr.nspl; ++c) {
+        const float* pc = base + c * kPartFloats;
+        const float f = __builtin_amdgcn_exp2f(pc[n] - Mu);
+        L += pc[32 + n] * f;
+        const float4* av = reinterpret_cast<const float4*>(pc + 64 + n * 128 + d0);
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const float4 v = av[e4];
+            o[4 * e4 + 0] += f * v.x; o[4 * e4 + 1] += f * v.y;
+            o[4 * e4 + 2] += f * v.z; o[4 * e4 + 3] += f * v.w;
+        }
+    }
+    const float inv = 1.0f / L;
+    T* orow = static_cast<T*>(p.out) + ((((int64_t)b * 32 + 4 * g + (n >> 3)) * 8 + (n & 7)) * 128) + d0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Elem<T>::store(orow, e, o[e] * inv);
+    if (p.lse && (tid & 7) == 0)
+        p.lse[((int64_t)b * 32 + 4 * g + (n >> 3)) * 8 + (n & 7)] = (Mu + log2f(L)) * kLn2;
+}
+
+// ---------------------------------------------------------------- fp32 VALU kernel
+// Plain fp32 path (small fp32 workloads): one workgroup per (b, g), eight lanes
+// per query row, scalar loads through the page layout, no split.
+__global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnParams p) {
+    const int g = blockIdx.x, b = blockIdx.y;
+    const SeqRange sr = seq_range(p, b);
+    const int tid = threadIdx.x;
+    const int n = tid >> 3, part = tid & 7, hh = n >> 3, j = n & 7;
+    const double log2_theta = log2((double)p.theta);
+    __shared__ float kbs[8][128];
+
+    const float* gq = static_cast<const float*>(p.gq);
+    const float* gk = static_cast<const float*>(p.gk);
+    float x[16], gw[16];
+    if (tid < 64) {
+        const int jj = tid >> 3;
+        const float* krow = static_cast<const float*>(p.kb) + ((((int64_t)b * 8 + g) * 8 + jj) * 128);
+        load_row16(krow, part, x);
+        load_row16(gk, part, gw);
+        norm_rope_16(x, gw, part, sr.S + jj, p.eps, log2_theta);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { kbs[jj][8 * part + e] = x[e]; kbs[jj][64 + 8 * part + e] = x[8 + e]; }
+    }
+    const float* qrow = static_cast<const float*>(p.q) + ((((int64_t)b * 32 + 4 * g + hh) * 8 + j) * 128);
+    float q[16];
+    load_row16(qrow, part, q);
+    load_row16(gq, part, gw);
+    norm_rope_16(q, gw, part, sr.S + j, p.eps, log2_theta);
+    __syncthreads();
+
+    const float* kc = static_cast<const float*>(p.kc);
+    const float* vc = static_cast<const float*>(p.vc);
+    const float* vb = static_cast<const float*>(p.vb) + ((int64_t)b * 8 + g) * 8 * 128;
+    const float sl2 = kLog2e * 0.08838834764831845f;
+    float m = -INFINITY, l = 0.f, o[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] = 0.f;
+    const int ntok = sr.S - sr.t0 + 8;
+    for (int i = 0; i < ntok; ++i) {
+        const bool ctx = i < sr.S - sr.t0;
+        float kx[16], vx[16];
+        if (ctx) {
+            const int t = sr.t0 + i;
+            const int ph = p.bt[(int64_t)b * p.max_pages + (t >> 4)];
+            const bool okp = ph >= 0 && (int64_t)ph < p.num_pages;
+            const int tt = t & 15;
+            const float* kp = kc + ((int64_t)(okp ? ph : 0) * 8 + g) * 2048;
+            const float* vp = vc + ((int64_t)(okp ? ph : 0) * 8 + g) * 2048;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int d = e < 8 ? 8 * part + e : 64 + 8 * part + (e - 8);
+                const int ko = 256 * ((d & 63) >> 3) + 8 * (tt + 16 * (d >> 6)) + (d & 7);
+                const int vo = 512 * (d >> 5) + 256 * ((tt >> 2) & 1) + 8 * (d & 31) + (((tt >> 3) << 2) | (tt & 3));
+                kx[e] = okp ? kp[ko] : 0.f;
+                vx[e] = okp ? vp[vo] : 0.f;
+            }
+        } else {
+            const int jb = i - (sr.S - sr.t0);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int d = e < 8 ? 8 * part + e : 64 + 8 * part + (e - 8);
+                kx[e] = kbs[jb][d];
+                vx[e] = vb[jb * 128 + d];
+            }
+        }
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dot += q[e] * kx[e];
+        dot += __shfl_xor(dot, 1);
+        dot += __shfl_xor(dot, 2);
+        dot += __shfl_xor(dot, 4);
+        const float sc = dot * sl2;
+        const float mn = fmaxf(m, sc);
+        const float a = exp2f(m - mn), pw = exp2f(sc - mn);
+        l = l * a + pw;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[e] = o[e] * a + pw * vx[e];
+        m = mn;
+    }
+    const float inv = 1.0f / l;
+    float* orow = static_cast<float*>(p.out) + ((((int64_t)b * 32 + 4 * g + hh) * 8 + j) * 128);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { orow[8 * part + e] = o[e] * inv; orow[64 + 8 * part + e] = o[8 + e] * inv; }
+    if (p.lse && part == 0) p.lse[((int64_t)b * 32 + 4 * g + hh) * 8 + j] = (m + log2f(l)) * kLn2;
+}
+
+}  // namespace
+
+AttnPlan attn_plan(const dflash_attn_args& a) {
+    AttnPlan pl;
+    int64_t cap = (int64_t)a.max_pages * 16;
+    if (a.window > 0 && a.window < cap) cap = a.window;
+    cap += kTile;  // alignment slack of the first tile
+    if (a.dtype == DFLASH_F32) {
+        pl.split_tokens = 0;
+        pl.nsplit = 1;
+        pl.ws_bytes = 0;
+        return pl;
+    }
+    int split;
+    if (a.split_tokens > 0) {
+        split = a.split_tokens;
+    } else {
+        // Aim for ~2048 workgroups (8 per CU on 256 CUs) over B x 8 heads.
+        const int64_t pairs = (int64_t)a.B * 8;
+        int64_t want = (2048 + pairs - 1) / pairs;
+        if (want < 1) want = 1;
+        int64_t s = (cap + want - 1) / want;
+        s = (s + 127) / 128 * 128;
+        if (s < 128) s = 128;
+        if (s > (1 << 30)) s = 1 << 30;
+        split = (int)s;
+    }
+    pl.split_tokens = split;
+    pl.nsplit = (int)((cap + split - 1) / split);
+    if (pl.nsplit < 1) pl.nsplit = 1;
+    pl.ws_bytes = pl.nsplit > 1 ? (size_t)a.B * 8 * pl.nsplit * kPartFloats * sizeof(float) : 0;
+    return pl;
+}
+
+hipError_t launch_attn(const dflash_attn_args& a, const AttnPlan& pl, void* ws, hipStream_t s) {
+    AttnParams p;
+    p.q = a.q; p.kb = a.k_blk; p.vb = a.v_blk; p.gq = a.gq; p.gk = a.gk;
+    p.eps = a.eps; p.theta = a.rope_theta;
+    p.kc = a.k_cache; p.vc = a.v_cache; p.num_pages = a.num_pages;
+    p.bt = a.block_table; p.max_pages = a.max_pages; p.ctx_len = a.ctx_len;
+    p.window = a.window; p.split = pl.split_tokens > 0 ? pl.split_tokens : (1 << 30); p.nsplit = pl.nsplit;
+    p.out = a.out; p.lse = a.lse_out;
+    p.part = static_cast<float*>(ws);
+    if (a.dtype == DFLASH_F32) {
+        attn_f32_kernel<<<dim3(8, a.B), kThreads, 0, s>>>(p);
+        return hipGetLastError();
+    }
+    attn_bf16_kernel<<<dim3(pl.nsplit, 8, a.B), kThreads, 0, s>>>(p);
+    if (pl.nsplit > 1) attn_merge_kernel<uint16_t><<<dim3(8, a.B), kThreads, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace dflash

@@ -1,0 +1,90 @@
+// Device-side helpers shared by the DFlash kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dflash {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// bfloat16 is stored as raw uint16 bits; widening is exact.
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Round-to-nearest-even narrowing of a finite fp32 value to bf16 bits.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Low / high bf16 of a 32-bit word widened to fp32.
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+
+// Element loads for the two storage types.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
+    static __device__ __forceinline__ void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {  // bf16 bits
+    static __device__ __forceinline__ float load(const uint16_t* p, int64_t i) {
+        return bf16_bits_to_f32(p[i]);
+    }
+    static __device__ __forceinline__ void store(uint16_t* p, int64_t i, float v) {
+        p[i] = (uint16_t)f32_to_bf16_bits(v);
+    }
+};
+
+// ---- Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11) ----
+struct U64x4 { uint64_t x0, x1, x2, x3; };
+
+__device__ __forceinline__ U64x4 philox4x64_10(U64x4 c, uint64_t k0, uint64_t k1) {
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        uint64_t hi0 = __umul64hi(M0, c.x0), lo0 = M0 * c.x0;
+        uint64_t hi1 = __umul64hi(M1, c.x2), lo1 = M1 * c.x2;
+        U64x4 n;
+        n.x0 = hi1 ^ c.x1 ^ k0;
+        n.x1 = lo1;
+        n.x2 = hi0 ^ c.x3 ^ k1;
+        n.x3 = lo0;
+        c = n;
+        k0 += W0;
+        k1 += W1;
+    }
+    return c;
+}
+
+// u = ((w >> 41) + 0.5) * 2^-23 : exact in fp32, strictly inside (0, 1).
+__device__ __forceinline__ float word_to_uniform(uint64_t w) {
+    return ((float)(uint32_t)(w >> 41) + 0.5f) * 1.1920928955078125e-07f;
+}
+
+// ---- wave64 reductions ----
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+}  // namespace dflash

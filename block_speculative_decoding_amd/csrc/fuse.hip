@@ -1,0 +1,362 @@
+// Context fusion + K/V injection (gfx950).
+//
+// Follows "DFlash & DFlash2: Block-Diffusion LLM-Speedup", section 4.1
+// (H_t = RMSNorm(W_c [H1; ...; H5]); every draft layer's K/V cache receives
+// W_K H_t / W_V H_t) and "Nemotron 3.5 Bolt E4B", section "Five target states
+// become persistent draft context" (five 2560-wide states, 8 KV heads of 128,
+// per-head K RMSNorm before RoPE; unquantized K/V projections fused into one
+// matrix multiplication).
+//
+// Launch sequence on one stream:
+//   gemm  (A = the five capture pointers, one K segment each; B = W_c)
+//         -> fp32 split-K partials [ks1][M][2560]
+//   norm  -> sums the partials, RMSNorm with g_c, stores H_t (dtype)
+//   gemm  (A = H_t, B = W_KV of all layers at once, N = layers * 2048)
+//         -> fp32 split-K partials [ks2][M][N]
+//   kv    -> sums the partials; per 128-wide head: K gets k_norm and RoPE,
+//            V is copied; both are scattered into the paged cache layout.
+// The bf16 GEMM is a 128x128x64 tile on the 32x32x16 bf16 matrix
+// instruction, LDS double-buffered with an XOR swizzle, tiles ordered in
+// 8-row groups and laid out contiguously per XCD so neighbouring tiles that
+// share an operand panel run on the same L2.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace dflash {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int kGroupM = 8;
+constexpr int kXcds = 8;
+
+struct GemmParams {
+    const void* aseg[5];  // A segments: columns [s*seg_w, (s+1)*seg_w) come from aseg[s]
+    int64_t a_stride;     // elements between A rows
+    int seg_w;
+    const void* b;        // [N][K] row-major
+    int M, N, K;
+    int ks, kt_per_split;
+    float* part;          // [ks][M][N]
+};
+
+// Tile id for this workgroup: XCD-contiguous ranges, then 8-row M groups.
+struct TileId { int tm, tn, ks; bool valid; };
+__device__ __forceinline__ TileId tile_id(const GemmParams& p, int tiles_m, int tiles_n) {
+    const int total = tiles_m * tiles_n * p.ks;
+    const int nblk = gridDim.x;  // padded to a multiple of kXcds
+    const int bid = blockIdx.x;
+    const int per_xcd = nblk / kXcds;
+    const int L = (bid % kXcds) * per_xcd + bid / kXcds;
+    TileId t;
+    t.valid = L < total;
+    const int per_split = tiles_m * tiles_n;
+    t.ks = L / per_split;
+    const int r = L % per_split;
+    const int in_group = kGroupM * tiles_n;
+    const int grp = r / in_group;
+    const int first_m = grp * kGroupM;
+    const int gm = min(tiles_m - first_m, kGroupM);
+    const int q = r % in_group;
+    t.tm = first_m + q % gm;
+    t.tn = q / gm;
+    return t;
+}
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+
+__global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = p.N / BN;
+    const TileId t = tile_id(p, tiles_m, tiles_n);
+    if (!t.valid) return;
+    const int nk = p.K / BK;
+    const int kt0 = t.ks * p.kt_per_split;
+    const int kt1 = min(nk, kt0 + p.kt_per_split);
+    if (kt0 >= kt1) return;
+
+    __shared__ __attribute__((aligned(16))) uint4 lds[2][2][BM * 8];  // [buf][A/B][row*8+chunk]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m0 = t.tm * BM, n0 = t.tn * BN;
+    const uint16_t* bmat = static_cast<const uint16_t*>(p.b);
+
+    uint4 ra[4], rb[4];
+    auto gload = [&](int kt) {
+        const int kg = kt * BK;
+        const int seg = kg / p.seg_w;
+        const int kc = kg - seg * p.seg_w;
+        const uint16_t* a = static_cast<const uint16_t*>(p.aseg[seg]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int id = tid + kThreads * j;
+            const int row = id >> 3, ch = id & 7;
+            const int gm = m0 + row;
+            ra[j] = gm < p.M ? *reinterpret_cast<const uint4*>(a + (int64_t)gm * p.a_stride + kc + 8 * ch)
+                             : make_uint4(0, 0, 0, 0);
+            rb[j] = *reinterpret_cast<const uint4*>(bmat + (int64_t)(n0 + row) * p.K + kg + 8 * ch);
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int id = tid + kThreads * j;
+            const int row = id >> 3, ch = id & 7;
+            lds[buf][0][swz(row, ch)] = ra[j];
+            lds[buf][1][swz(row, ch)] = rb[j];
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16){};
+
+    const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;
+    const int lr = lane & 31, lh = lane >> 5;
+
+    gload(kt0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = kt0; kt < kt1; ++kt) {
+        const int cur = (kt - kt0) & 1;
+        if (kt + 1 < kt1) gload(kt + 1);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int ch = 2 * s + lh;
+            bf16x8 af[2], bfr[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                af[i] = __builtin_bit_cast(bf16x8, lds[cur][0][swz(wr + 32 * i + lr, ch)]);
+                bfr[i] = __builtin_bit_cast(bf16x8, lds[cur][1][swz(wc + 32 * i + lr, ch)]);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < kt1) lstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    // Lane holds column lr of each 32x32 block, rows 8*jj + 4*lh + r.
+    float* out = p.part + (int64_t)t.ks * p.M * p.N;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int gm = m0 + wr + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                const int gn = n0 + wc + 32 * j + lr;
+                if (gm < p.M) out[(int64_t)gm * p.N + gn] = acc[i][j][r];
+            }
+}
+
+// Plain fp32 GEMM for the fp32 path: 64x64 tile, 4x4 outputs per thread.
+__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
+    const int tm = blockIdx.x, tn = blockIdx.y;
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    __shared__ float as[16][65], bs[16][65];
+    float acc[4][4] = {};
+    const float* bmat = static_cast<const float*>(p.b);
+    for (int k0 = 0; k0 < p.K; k0 += 16) {
+        const int seg = k0 / p.seg_w;
+        const int kc = k0 - seg * p.seg_w;
+        const float* a = static_cast<const float*>(p.aseg[seg]);
+        for (int i = tid; i < 64 * 16; i += kThreads) {
+            const int r = i >> 4, kk = i & 15;
+            const int gm = tm * 64 + r;
+            as[kk][r] = gm < p.M ? a[(int64_t)gm * p.a_stride + kc + kk] : 0.f;
+            bs[kk][r] = bmat[(int64_t)(tn * 64 + r) * p.K + k0 + kk];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] += as[kk][ty * 4 + i] * bs[kk][tx * 4 + j];
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int gm = tm * 64 + ty * 4 + i;
+        if (gm >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p.part[(int64_t)gm * p.N + tn * 64 + tx * 4 + j] = acc[i][j];
+    }
+}
+
+// Sum split-K partials of one row, RMSNorm with g_c, store H_t.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void fuse_norm_kernel(const float* part, int ks, int M, const T* gc,
+                                                            float eps, T* ht, T* ht_out) {
+    constexpr int D = DFLASH_D, PER = D / kThreads;
+    const int m = blockIdx.x, tid = threadIdx.x;
+    float y[PER];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int c = tid + kThreads * e;
+        float v = 0.f;
+        for (int s = 0; s < ks; ++s) v += part[((int64_t)s * M + m) * D + c];
+        y[e] = v;
+        ss += v * v;
+    }
+    ss = wave_sum(ss);
+    __shared__ float red[kThreads / 64];
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    const float tot = red[0] + red[1] + red[2] + red[3];
+    const float rinv = 1.0f / sqrtf(tot * (1.0f / D) + eps);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int c = tid + kThreads * e;
+        const float h = Elem<T>::load(gc, c) * (y[e] * rinv);
+        Elem<T>::store(ht, (int64_t)m * D + c, h);
+        if (ht_out) Elem<T>::store(ht_out, (int64_t)m * D + c, h);
+    }
+}
+
+struct KvParams {
+    const float* part; int ks; int M; int N;
+    const void* gk; float eps; float theta;
+    const int32_t* pos; const int64_t* slot;
+    void* kc[5]; void* vc[5]; int64_t num_pages;
+};
+
+// One wave per (row, 128-wide head of the [K_0 | V_0 | K_1 | ...] output).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void fuse_kv_kernel(KvParams p) {
+    const int m = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int hidx = blockIdx.y * 4 + (threadIdx.x >> 6);  // [layer][K/V][head]
+    const int l = hidx >> 4, kv = (hidx >> 3) & 1, head = hidx & 7;
+    const int64_t slot = p.slot[m];
+    if (slot < 0 || slot >= p.num_pages * 16) return;
+    const int64_t page = slot >> 4;
+    const int t = (int)(slot & 15);
+    const int n0 = hidx * 128;
+    float x0 = 0.f, x1 = 0.f;
+    for (int s = 0; s < p.ks; ++s) {
+        const float* row = p.part + ((int64_t)s * p.M + m) * p.N + n0;
+        x0 += row[lane];
+        x1 += row[lane + 64];
+    }
+    const int d0 = lane, d1 = lane + 64;
+    if (kv == 0) {
+        const float ss = wave_sum(x0 * x0 + x1 * x1);
+        const float rinv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + p.eps);
+        const T* gk = static_cast<const T*>(p.gk) + l * 128;
+        const float a = Elem<T>::load(gk, d0) * (x0 * rinv);
+        const float b = Elem<T>::load(gk, d1) * (x1 * rinv);
+        const double inv_freq = exp2(-(double)lane * (1.0 / 64.0) * log2((double)p.theta));
+        double ang = (double)p.pos[m] * inv_freq;
+        const double two_pi = 6.283185307179586;
+        ang -= rint(ang * (1.0 / two_pi)) * two_pi;
+        float sn, cs;
+        sincosf((float)ang, &sn, &cs);
+        T* kc = static_cast<T*>(p.kc[l]) + (page * 8 + head) * 2048;
+        const int o0 = 256 * ((d0 & 63) >> 3) + 8 * (t + 16 * (d0 >> 6)) + (d0 & 7);
+        const int o1 = 256 * ((d1 & 63) >> 3) + 8 * (t + 16 * (d1 >> 6)) + (d1 & 7);
+        Elem<T>::store(kc, o0, a * cs - b * sn);
+        Elem<T>::store(kc, o1, b * cs + a * sn);
+    } else {
+        T* vc = static_cast<T*>(p.vc[l]) + (page * 8 + head) * 2048;
+        const int te = ((t >> 3) << 2) | (t & 3), th = (t >> 2) & 1;
+        const int o0 = 512 * (d0 >> 5) + 256 * th + 8 * (d0 & 31) + te;
+        const int o1 = 512 * (d1 >> 5) + 256 * th + 8 * (d1 & 31) + te;
+        Elem<T>::store(vc, o0, x0);
+        Elem<T>::store(vc, o1, x1);
+    }
+}
+
+int pick_ks(int M, int N, int K) {
+    const int tiles = ((M + BM - 1) / BM) * (N / BN);
+    const int nk = K / BK;
+    int ks = (512 + tiles - 1) / tiles;  // aim for ~2 workgroups per CU
+    if (ks > nk / 4) ks = nk / 4;        // keep >= 4 k-tiles per split
+    if (ks < 1) ks = 1;
+    // Every split must own at least one k-tile: recount after rounding.
+    const int per = (nk + ks - 1) / ks;
+    return (nk + per - 1) / per;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+hipError_t launch_gemm(const GemmParams& g, int dtype, hipStream_t s) {
+    if (dtype == DFLASH_BF16) {
+        const int tiles = ((g.M + BM - 1) / BM) * (g.N / BN) * g.ks;
+        const int grid = (tiles + kXcds - 1) / kXcds * kXcds;
+        gemm_bf16_kernel<<<grid, kThreads, 0, s>>>(g);
+    } else {
+        gemm_f32_kernel<<<dim3((g.M + 63) / 64, g.N / 64), kThreads, 0, s>>>(g);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+FusePlan fuse_plan(const dflash_fuse_args& a) {
+    FusePlan pl;
+    const int M = (int)a.M;
+    const int N2 = a.num_layers * 2048;
+    const bool bf = a.dtype == DFLASH_BF16;
+    pl.ks1 = bf ? pick_ks(M, DFLASH_D, DFLASH_NCAPTURE * DFLASH_D) : 1;
+    pl.ks2 = bf ? pick_ks(M, N2, DFLASH_D) : 1;
+    const size_t es = bf ? 2 : 4;
+    pl.off_part1 = 0;
+    pl.off_ht = align256((size_t)pl.ks1 * M * DFLASH_D * 4);
+    pl.off_part2 = pl.off_ht + align256((size_t)M * DFLASH_D * es);
+    pl.ws_bytes = pl.off_part2 + align256((size_t)pl.ks2 * M * N2 * 4);
+    return pl;
+}
+
+hipError_t launch_fuse(const dflash_fuse_args& a, const FusePlan& pl, void* ws, hipStream_t s) {
+    const int M = (int)a.M;
+    if (M == 0) return hipSuccess;
+    char* w = static_cast<char*>(ws);
+    float* part1 = reinterpret_cast<float*>(w + pl.off_part1);
+    void* ht = w + pl.off_ht;
+    float* part2 = reinterpret_cast<float*>(w + pl.off_part2);
+    const int N2 = a.num_layers * 2048;
+
+    GemmParams g1 = {};
+    for (int i = 0; i < 5; ++i) g1.aseg[i] = a.hs[i];
+    g1.a_stride = a.hs_stride; g1.seg_w = DFLASH_D;
+    g1.b = a.wc; g1.M = M; g1.N = DFLASH_D; g1.K = DFLASH_NCAPTURE * DFLASH_D;
+    g1.ks = pl.ks1; g1.kt_per_split = (g1.K / BK + pl.ks1 - 1) / pl.ks1;
+    g1.part = part1;
+    hipError_t e = launch_gemm(g1, a.dtype, s);
+    if (e != hipSuccess) return e;
+
+    if (a.dtype == DFLASH_BF16)
+        fuse_norm_kernel<uint16_t><<<M, kThreads, 0, s>>>(part1, pl.ks1, M, static_cast<const uint16_t*>(a.gc),
+                                                          a.eps, static_cast<uint16_t*>(ht),
+                                                          static_cast<uint16_t*>(a.ht_out));
+    else
+        fuse_norm_kernel<float><<<M, kThreads, 0, s>>>(part1, pl.ks1, M, static_cast<const float*>(a.gc), a.eps,
+                                                       static_cast<float*>(ht), static_cast<float*>(a.ht_out));
+
+    GemmParams g2 = {};
+    g2.aseg[0] = ht; g2.a_stride = DFLASH_D; g2.seg_w = DFLASH_D;
+    g2.b = a.wkv; g2.M = M; g2.N = N2; g2.K = DFLASH_D;
+    g2.ks = pl.ks2; g2.kt_per_split = (g2.K / BK + pl.ks2 - 1) / pl.ks2;
+    g2.part = part2;
+    e = launch_gemm(g2, a.dtype, s);
+    if (e != hipSuccess) return e;
+
+    KvParams kp;
+    kp.part = part2; kp.ks = pl.ks2; kp.M = M; kp.N = N2;
+    kp.gk = a.gk; kp.eps = a.eps; kp.theta = a.rope_theta;
+    kp.pos = a.pos; kp.slot = a.slot; kp.num_pages = a.num_pages;
+    for (int i = 0; i < 5; ++i) { kp.kc[i] = a.k_cache[i]; kp.vc[i] = a.v_cache[i]; }
+    const dim3 gkv(M, a.num_layers * 4);
+    if (a.dtype == DFLASH_BF16) fuse_kv_kernel<uint16_t><<<gkv, kThreads, 0, s>>>(kp);
+    else fuse_kv_kernel<float><<<gkv, kThreads, 0, s>>>(kp);
+    return hipGetLastError();
+}
+
+}  // namespace dflash

@@ -1,0 +1,234 @@
+/*
+ * dflash.h -- C ABI of the DFlash draft-verify hot path on AMD MI355X (gfx950).
+ *
+ * Three operations, each one call on a caller-supplied HIP stream:
+ *
+ *   dflash_ctx_fuse    context fusion + K/V injection into the draft caches
+ *   dflash_block_attn  one draft layer's non-causal attention for the 8-token block
+ *   dflash_spec_verify exact speculative verification of the 7 proposals
+ *
+ * Sources (web pages; cited by title and section):
+ *   [E4B] "Nemotron 3.5 Bolt E4B: Block-Parallel Speculation with DFlash"
+ *   [DF2] "DFlash & DFlash2: Block-Diffusion LLM-Speedup"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer named "device" is device memory on the current HIP device,
+ *   owned by the caller.  The library never allocates or frees device memory;
+ *   scratch space comes in through `workspace`, sized by the matching
+ *   *_workspace_size call (0 bytes is valid when that call returns 0).
+ *   Device pointers must be 16-byte aligned.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   Calls only enqueue work: there is no host synchronisation, outputs stay
+ *   on the device, and every pointer must stay valid until the stream has
+ *   reached the call.  Results are deterministic for fixed inputs.
+ * - Element types: dtype DFLASH_BF16 (bfloat16 storage, fp32 arithmetic) or
+ *   DFLASH_F32.  Integer tensors are int32 / int64 as stated.
+ * - Return value: DFLASH_OK (0) or a negative code.  On error nothing is
+ *   enqueued and dflash_last_error() (thread-local) describes the problem.
+ *   Data-dependent conditions that only the device can see never fault: they
+ *   are handled as documented on each field (skipped writes, clamped lengths,
+ *   rejected proposals).
+ * - Calls that share a workspace buffer must be ordered on one stream.
+ *
+ * Paged KV cache layout (owned by the caller; written by dflash_ctx_fuse,
+ * read by dflash_block_attn)
+ * ---------------------------------------------------------------------
+ * A layer's K cache and V cache are each [num_pages][8 kv heads][2048]
+ * elements.  A page holds 16 consecutive tokens; token slot s = page*16 + t.
+ * Inside one (page, head) block of 16 tokens x 128 dims the element of token
+ * t (0..15) and dim d (0..127) sits at
+ *
+ *   K:  256*((d & 63) >> 3) + 8*(t + 16*(d >> 6)) + (d & 7)
+ *   V:  512*(d >> 5) + 256*((t >> 2) & 1) + 8*(d & 31) + (((t >> 3) << 2) | (t & 3))
+ *
+ * Both layouts make every 64-lane load of a 32-token tile one contiguous,
+ * coalesced 512-byte or 1-KiB run whose lanes land directly in the operand
+ * registers of the gfx950 32x32x16 bf16 matrix instruction (keys as the A
+ * operand of S^T = K Q^T, values as the A operand of O^T = V^T P^T).
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define DFLASH_OK            0
+#define DFLASH_EINVAL       (-1)  /* null pointer, bad size/stride, bad constant */
+#define DFLASH_EUNSUPPORTED (-2)  /* dtype or shape outside the supported set */
+#define DFLASH_EHIP         (-3)  /* a HIP launch failed (message has the HIP error) */
+#define DFLASH_EWORKSPACE   (-4)  /* workspace missing or smaller than required */
+
+/* ---- element types ---- */
+#define DFLASH_BF16 0
+#define DFLASH_F32  1
+
+/* ---- fixed model constants ([E4B] "Five target states become persistent
+ *      draft context"; "The released serving cycle") ---- */
+#define DFLASH_D          2560   /* draft width = target width */
+#define DFLASH_NCAPTURE   5      /* captured target states (layers 5,11,17,23,35) */
+#define DFLASH_HQ         32     /* query heads */
+#define DFLASH_HKV        8      /* KV heads; 4 query heads share one */
+#define DFLASH_HEAD_DIM   128
+#define DFLASH_BLOCK      8      /* 1 anchor + 7 mask positions */
+#define DFLASH_PAGE       16     /* tokens per cache page */
+#define DFLASH_MAX_LAYERS 5      /* draft layers */
+
+#define DFLASH_VERSION 10000     /* 1.0.0 */
+
+/*
+ * dflash_ctx_fuse -- context fusion and K/V injection.
+ * [DF2] 4.1 (H_t = RMSNorm(W_c [H1;...;H5]), K_i/V_i = W_i^K/V H_t injected
+ * into every draft layer's cache) and [E4B] "Five target states become
+ * persistent draft context" (five 2560-wide states concatenated and projected
+ * back to 2560; per-head K RMSNorm before RoPE).
+ *
+ * For each of the M rows:
+ *   y    = [hs0 | hs1 | hs2 | hs3 | hs4] . wc^T           (12800 -> 2560)
+ *   H_t  = gc * y / sqrt(mean(y^2) + eps)                  (stored in dtype)
+ *   for layer l < num_layers:
+ *     k  = H_t . wkv[2048 l      : 2048 l + 1024]^T  -> 8 heads x 128
+ *     v  = H_t . wkv[2048 l+1024 : 2048 l + 2048]^T
+ *     k  = RoPE(gk[l] * k / sqrt(mean_head(k^2) + eps), pos[row])
+ *     k_cache[l], v_cache[l] at slot[row] <- k, v          (rounded to dtype)
+ * RoPE is rotate-half over pairs (i, i+64) with angle pos * theta^(-i/64).
+ */
+typedef struct dflash_fuse_args {
+    int32_t dtype;            /* DFLASH_BF16 or DFLASH_F32 (all float tensors) */
+    int32_t num_layers;       /* 1..5 draft layers to write */
+    int64_t M;                /* rows to fuse; 0 is a valid no-op */
+    const void* hs[5];        /* device, each [M][hs_stride], first 2560 used; capture order */
+    int64_t hs_stride;        /* elements between rows, >= 2560, multiple of 8 */
+    const void* wc;           /* device [2560][12800] row-major (out, in) */
+    const void* gc;           /* device [2560] fusion-norm weight */
+    const void* wkv;          /* device [num_layers*2048][2560]; per layer 1024 K rows then 1024 V rows */
+    const void* gk;           /* device [num_layers][128] k_norm weights */
+    float eps;                /* RMSNorm epsilon (> 0) */
+    float rope_theta;         /* RoPE base (> 1) */
+    const int32_t* pos;       /* device [M] RoPE positions */
+    const int64_t* slot;      /* device [M] cache slot page*16+t; slots < 0 or >= num_pages*16 are skipped */
+    void* k_cache[5];         /* device, layer l: [num_pages][8][2048] K layout (entries >= num_layers ignored) */
+    void* v_cache[5];         /* device, layer l: [num_pages][8][2048] V layout */
+    int64_t num_pages;        /* pages in every layer's cache */
+    void* ht_out;             /* optional device [M][2560] copy of H_t (dtype); NULL = not written */
+} dflash_fuse_args;
+
+/*
+ * dflash_block_attn -- one draft layer's block attention.
+ * [E4B] "Five target states become persistent draft context": Q [B,32,8,128],
+ * K/V [B,8,8,128], four query heads per KV head, per-head Q/K RMSNorm before
+ * RoPE; attention over the cached context plus the block, non-causal inside
+ * the block ([E4B] "The released serving cycle"; [DF2] 4.1, K = [K_ctx ; K_blk]).
+ *
+ * For sequence b with S = ctx_len[b] (clamped to [0, max_pages*16]) and query
+ * head h (KV head g = h/4), block position j (0 = anchor) at position S + j:
+ *   q^   = RoPE(gq * q / rms(q), S + j),  k^blk = RoPE(gk * k_blk / rms, S + j)
+ *   keys = cached tokens [t0, S) of head g, then the 8 block keys
+ *          (t0 = 0, or max(0, S - window) when window > 0)
+ *   out  = softmax(q^ . keys^T / sqrt(128)) . values       (no mask)
+ * Cached tokens are read through block_table[b][t / 16]; entries past the
+ * sequence's last page are never read.
+ */
+typedef struct dflash_attn_args {
+    int32_t dtype;            /* DFLASH_BF16 or DFLASH_F32 */
+    int32_t B;                /* sequences, >= 1 */
+    const void* q;            /* device [B][32][8][128] */
+    const void* k_blk;        /* device [B][8][8][128] block keys before norm/RoPE */
+    const void* v_blk;        /* device [B][8][8][128] block values */
+    const void* gq;           /* device [128] q_norm weight */
+    const void* gk;           /* device [128] k_norm weight */
+    float eps;
+    float rope_theta;
+    const void* k_cache;      /* device [num_pages][8][2048] K layout (this layer) */
+    const void* v_cache;      /* device [num_pages][8][2048] V layout */
+    int64_t num_pages;        /* block_table entries must lie in [0, num_pages) */
+    const int32_t* block_table; /* device [B][max_pages] */
+    int32_t max_pages;        /* >= 1 */
+    const int32_t* ctx_len;   /* device [B] cached tokens per sequence */
+    int32_t page_size;        /* must be 16 */
+    int32_t block_len;        /* must be 8 */
+    int32_t window;           /* 0 = full context; > 0 = latest `window` tokens */
+    int32_t split_tokens;     /* 0 = automatic; else tokens per split-K chunk, multiple of 128 */
+    void* out;                /* device [B][32][8][128] (dtype) */
+    float* lse_out;           /* optional device [B][32][8] natural-log LSE; NULL = not written */
+} dflash_attn_args;
+
+/*
+ * dflash_spec_verify -- exact speculative verification of one block.
+ * [E4B] "Why exact verification preserves the target" and [DF2] 4.4:
+ * sampled proposals are accepted with probability min(1, p/q); on rejection
+ * the replacement is drawn from normalize(max(0, p - q)); greedy accepts while
+ * the proposal equals the target argmax; at most 8 tokens per cycle including
+ * the correction or bonus token ([E4B] "The released serving cycle").
+ *
+ * Per sequence b with T = temperature[b] (T <= 0: greedy):
+ *   p_r = softmax(target[b][r] / T) (r = 0..7), q_k = softmax(draft[b][k-1] / T)
+ *   for k = 1..7: greedy  -- accept iff d_k == argmax target[b][k-1] (lowest index on ties)
+ *                 sampled -- accept iff u_k < p_{k-1}(d_k) / q_k(d_k),
+ *                            u_k = U(0, b, k, 0)
+ *   first rejection at k: greedy emits the argmax; sampled emits
+ *       argmax_{i: r_i > 0} ln r_i + G_i,  r = max(0, p_{k-1} - q_k)   (r == 0 -> p_{k-1})
+ *   all accepted: greedy emits argmax target[b][7]; sampled emits
+ *       argmax_i target[b][7][i]/T + G_i  with G from k = 8
+ *   G_i = -ln(-ln U(1, b, k, i)).
+ * U(s, b, k, i) = ((w >> 41) + 0.5) * 2^-23 where w is word (i mod 4) of
+ * Philox4x64-10 (Salmon et al., SC'11) with key (seed, 0) and counter
+ * (i / 4, 8b + k, s, offset).
+ * Proposal ids outside [0, V) are never accepted.  Decisions with
+ * |u - p/q| < 1e-6 are counted into *near_ties (atomically added).
+ */
+typedef struct dflash_verify_args {
+    int32_t dtype;            /* DFLASH_BF16 or DFLASH_F32 logits */
+    int32_t B;                /* sequences, >= 1 */
+    int64_t V;                /* vocabulary, >= 1, multiple of 8 */
+    const void* target_logits;  /* device; row r of sequence b at b*t_batch_stride + r*t_row_stride, 8 rows */
+    int64_t t_batch_stride;   /* elements, multiple of 8 */
+    int64_t t_row_stride;     /* elements, >= V, multiple of 8 */
+    const void* draft_logits;   /* device; row k-1 (proposal k) at b*d_batch_stride + (k-1)*d_row_stride, 7 rows */
+    int64_t d_batch_stride;
+    int64_t d_row_stride;
+    const int32_t* draft_tokens; /* device [B][7] proposals d_1..d_7 */
+    const float* temperature;    /* device [B]; <= 0 means greedy */
+    uint64_t seed;
+    uint64_t offset;             /* per-cycle counter word */
+    int32_t* out_tokens;         /* device [B][8]; emitted tokens, -1 padded */
+    int32_t* out_len;            /* device [B]; 1..8 */
+    unsigned long long* near_ties; /* device [1]; incremented, never cleared */
+} dflash_verify_args;
+
+/* Library version (DFLASH_VERSION of the build). */
+int dflash_version(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* dflash_last_error(void);
+
+/* sizeof of the argument structs as compiled into the library:
+ * kind 0 = dflash_fuse_args, 1 = dflash_attn_args, 2 = dflash_verify_args;
+ * returns 0 for any other kind.  Lets bindings check their struct mirrors. */
+size_t dflash_args_size(int kind);
+
+/* Workspace bytes the matching call needs for these arguments (only sizes,
+ * dtype and flags are read; pointers may be NULL).  Returns a status code. */
+int dflash_fuse_workspace_size(const dflash_fuse_args* args, size_t* bytes);
+int dflash_attn_workspace_size(const dflash_attn_args* args, size_t* bytes);
+int dflash_verify_workspace_size(const dflash_verify_args* args, size_t* bytes);
+
+/* The three operations.  `workspace` must hold at least the size returned
+ * above (it may be NULL when that size is 0); its contents are scratch. */
+int dflash_ctx_fuse(const dflash_fuse_args* args, void* workspace,
+                    size_t workspace_bytes, void* stream);
+int dflash_block_attn(const dflash_attn_args* args, void* workspace,
+                      size_t workspace_bytes, void* stream);
+int dflash_spec_verify(const dflash_verify_args* args, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H */

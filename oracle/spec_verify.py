@@ -18,7 +18,7 @@ Follows [E4B] "Why exact verification preserves the target" and [DF2] 4.4
 Temperature: [DF2] 9 (FAQ Q3) says temperature scaling is applied to both the
 draft and the target logits before the ratio is formed; its printed formula
 (a ratio of p^(1/T)) is not normalised, so the reading used here is
-p = softmax(z_target / T), q = softmax(z_draft / T); T = 0 means greedy.
+p = softmax(z_target / T), q = softmax(z_draft / T); T <= 0 means greedy.
 
 Row alignment (reading): draft row k-1 holds q for proposal d_k (k = 1..7);
 target row k-1 holds p for the position of d_k; target row 7 is the bonus
@@ -72,13 +72,15 @@ def _top2(keys):
     return i, float(best - second)
 
 
-def spec_verify_ref(zt, zd, d, temperature, seed=0, offset=0, seq_block=4):
+def spec_verify_ref(zt, zd, d, temperature, seed=0, offset=0, seq_block=4, batch_offset=0):
     """Verify one draft block per sequence.
 
     zt: target logits [B, 8, V]; zd: draft logits [B, 7, V]; d: proposals
     [B, 7]; temperature: [B] (0 = greedy).  Logits are taken as the exact
     stored values.  Sequences are processed ``seq_block`` at a time to bound
     memory; each sequence follows the sequential rule independently.
+    ``batch_offset`` is the batch index of row 0 (it enters the random
+    counters), so a slice of a batch can be verified on its own.
     """
     B, _, V = zt.shape
     d = np.asarray(d, dtype=np.int64)
@@ -95,21 +97,22 @@ def spec_verify_ref(zt, zd, d, temperature, seed=0, offset=0, seq_block=4):
         sample_gap=np.full(B, np.inf),
     )
     # Acceptance uniforms U(0, b, k, 0) for every sequence and k = 1..7.
-    bb, kk = np.meshgrid(np.arange(B), np.arange(1, BLOCK), indexing="ij")
+    bb, kk = np.meshgrid(batch_offset + np.arange(B), np.arange(1, BLOCK), indexing="ij")
     u_all = uniforms(seed, offset, 0, bb, kk, np.zeros_like(bb))
 
     for s0 in range(0, B, seq_block):
         for b in range(s0, min(B, s0 + seq_block)):
-            _verify_one(b, np.asarray(zt[b], np.float64), np.asarray(zd[b], np.float64),
+            _verify_one(b, batch_offset + b, np.asarray(zt[b], np.float64), np.asarray(zd[b], np.float64),
                         d[b], float(temperature[b]), seed, offset, u_all[b], tr)
     return tr
 
 
-def _verify_one(b, zt, zd, d, T, seed, offset, u_b, tr):
+def _verify_one(b, gb, zt, zd, d, T, seed, offset, u_b, tr):
+    """Sequence at trace row b; gb is its batch index in the random counters."""
     V = zt.shape[-1]
     emitted = []
-    if T == 0.0:
-        # Greedy: accept while d_k equals the target argmax of row k-1.
+    if not T > 0.0:
+        # Greedy (T <= 0): accept while d_k equals the target argmax of row k-1.
         n = 0
         for k in range(1, BLOCK):
             a = int(np.argmax(zt[k - 1]))
@@ -147,7 +150,7 @@ def _verify_one(b, zt, zd, d, T, seed, offset, u_b, tr):
             r = np.maximum(0.0, p - q)
             if not np.any(r > 0):
                 r = p
-            g = gumbel(uniforms(seed, offset, 1, b, k, np.arange(V)))
+            g = gumbel(uniforms(seed, offset, 1, gb, k, np.arange(V)))
             with np.errstate(divide="ignore"):
                 keys = np.where(r > 0, np.log(r) + g, -np.inf)
             x_new, gap = _top2(keys)
@@ -157,7 +160,7 @@ def _verify_one(b, zt, zd, d, T, seed, offset, u_b, tr):
             done = True
             break
         if not done:
-            g = gumbel(uniforms(seed, offset, 1, b, BLOCK, np.arange(V)))
+            g = gumbel(uniforms(seed, offset, 1, gb, BLOCK, np.arange(V)))
             keys = zt[BLOCK - 1] / T + g
             x_new, gap = _top2(keys)
             emitted.append(x_new)

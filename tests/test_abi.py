@@ -1,0 +1,190 @@
+"""CPU tests of the C ABI: the library loads, exports every function the
+header declares, its struct sizes match the binding, and invalid calls are
+rejected before anything reaches the GPU.  Also checks the page-layout
+formulas of the header are permutations (every slot used once)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from tests.layout import k_offsets, v_offsets
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from block_speculative_decoding_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_speculative_decoding_amd.build import build_library
+        build_library(verbose=False)
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(dflash_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_three_operations():
+    fns = declared_functions()
+    for f in ("dflash_ctx_fuse", "dflash_block_attn", "dflash_spec_verify",
+              "dflash_fuse_workspace_size", "dflash_attn_workspace_size",
+              "dflash_verify_workspace_size", "dflash_last_error", "dflash_version",
+              "dflash_args_size"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from block_speculative_decoding_amd import _lib
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s+(\w+)$", out, re.M))
+    for f in declared_functions():
+        assert f in exported, f
+        assert hasattr(lib, f)
+    assert sorted(declared_functions()) == sorted(_lib.EXPORTS)
+
+
+def test_struct_sizes_and_version(lib):
+    from block_speculative_decoding_amd import _lib
+    assert lib.dflash_version() == 10000
+    assert lib.dflash_args_size(0) == ctypes.sizeof(_lib.FuseArgs)
+    assert lib.dflash_args_size(1) == ctypes.sizeof(_lib.AttnArgs)
+    assert lib.dflash_args_size(2) == ctypes.sizeof(_lib.VerifyArgs)
+    assert lib.dflash_args_size(3) == 0
+
+
+def test_page_layouts_are_permutations():
+    for off in (k_offsets(), v_offsets()):
+        assert sorted(off.reshape(-1).tolist()) == list(range(2048))
+
+
+# ---------------------------------------------------------------- validation
+FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced
+
+
+def _verify_args(**kw):
+    from block_speculative_decoding_amd import _lib
+    a = _lib.VerifyArgs()
+    a.dtype, a.B, a.V = 0, 4, 4096
+    a.target_logits, a.t_batch_stride, a.t_row_stride = FAKE, 8 * 4096, 4096
+    a.draft_logits, a.d_batch_stride, a.d_row_stride = FAKE, 7 * 4096, 4096
+    a.draft_tokens = a.temperature = a.out_tokens = a.out_len = a.near_ties = FAKE
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _attn_args(**kw):
+    from block_speculative_decoding_amd import _lib
+    a = _lib.AttnArgs()
+    a.dtype, a.B = 0, 2
+    a.q = a.k_blk = a.v_blk = a.gq = a.gk = a.k_cache = a.v_cache = FAKE
+    a.block_table = a.ctx_len = a.out = FAKE
+    a.eps, a.rope_theta = 1e-6, 1e6
+    a.num_pages, a.max_pages = 10, 5
+    a.page_size, a.block_len, a.window, a.split_tokens = 16, 8, 0, 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _fuse_args(**kw):
+    from block_speculative_decoding_amd import _lib
+    a = _lib.FuseArgs()
+    a.dtype, a.num_layers, a.M = 0, 2, 64
+    for i in range(5):
+        a.hs[i] = FAKE
+        a.k_cache[i] = a.v_cache[i] = FAKE
+    a.hs_stride = 2560
+    a.wc = a.gc = a.wkv = a.gk = a.pos = a.slot = FAKE
+    a.eps, a.rope_theta, a.num_pages = 1e-6, 1e6, 16
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _ws(lib, kind, a):
+    n = ctypes.c_size_t()
+    rc = getattr(lib, f"dflash_{kind}_workspace_size")(ctypes.byref(a), ctypes.byref(n))
+    return rc, n.value
+
+
+def _call(lib, fn, a, ws=None, nbytes=0):
+    return getattr(lib, fn)(ctypes.byref(a), ws, nbytes, None)
+
+
+def test_verify_validation(lib):
+    rc, n = _ws(lib, "verify", _verify_args())
+    assert rc == 0 and n > 0
+    assert _ws(lib, "verify", _verify_args(V=4100))[0] == -1          # not a multiple of 8
+    assert _ws(lib, "verify", _verify_args(dtype=7))[0] == -2
+    assert _ws(lib, "verify", _verify_args(B=0))[0] == -1
+    assert _call(lib, "dflash_spec_verify", _verify_args(target_logits=None), FAKE, n) == -1
+    assert _call(lib, "dflash_spec_verify", _verify_args(draft_tokens=FAKE + 4), FAKE, n) == -1  # misaligned
+    assert _call(lib, "dflash_spec_verify", _verify_args(t_row_stride=4000), FAKE, n) == -1
+    assert _call(lib, "dflash_spec_verify", _verify_args(d_batch_stride=7 * 4096 + 4), FAKE, n) == -1
+    assert _call(lib, "dflash_spec_verify", _verify_args(), None, 0) == -4
+    assert _call(lib, "dflash_spec_verify", _verify_args(), FAKE, n - 1) == -4
+    assert b"workspace" in lib.dflash_last_error()
+    # workspace grows with B and V
+    assert _ws(lib, "verify", _verify_args(B=8))[1] > n
+    assert _ws(lib, "verify", _verify_args(V=262144))[1] > n
+
+
+def test_attn_validation(lib):
+    assert _ws(lib, "attn", _attn_args())[0] == 0
+    assert _ws(lib, "attn", _attn_args(block_len=7))[0] == -1
+    assert _ws(lib, "attn", _attn_args(page_size=32))[0] == -1
+    assert _ws(lib, "attn", _attn_args(split_tokens=100))[0] == -1
+    assert _ws(lib, "attn", _attn_args(window=-1))[0] == -1
+    assert _ws(lib, "attn", _attn_args(B=0))[0] == -1
+    assert _ws(lib, "attn", _attn_args(dtype=3))[0] == -2
+    assert _call(lib, "dflash_block_attn", _attn_args(q=None)) == -1
+    assert _call(lib, "dflash_block_attn", _attn_args(eps=0.0)) == -1
+    assert _call(lib, "dflash_block_attn", _attn_args(block_len=16)) == -1
+    assert b"block_len" in lib.dflash_last_error()
+    # A split count above one needs a workspace; a single split does not.
+    rc, n = _ws(lib, "attn", _attn_args(max_pages=1000, split_tokens=128))
+    assert rc == 0 and n > 0
+    assert _call(lib, "dflash_block_attn", _attn_args(max_pages=1000, split_tokens=128)) == -4
+    rc, n1 = _ws(lib, "attn", _attn_args(max_pages=8, split_tokens=1024))
+    assert rc == 0 and n1 == 0
+    # workspace is monotone in the context capacity
+    sizes = [_ws(lib, "attn", _attn_args(max_pages=p, split_tokens=128))[1] for p in (8, 64, 512)]
+    assert sizes == sorted(sizes)
+    # fp32 path needs no workspace
+    assert _ws(lib, "attn", _attn_args(dtype=1, max_pages=1000))[1] == 0
+
+
+def test_fuse_validation(lib):
+    rc, n = _ws(lib, "fuse", _fuse_args())
+    assert rc == 0 and n > 0
+    assert _ws(lib, "fuse", _fuse_args(M=0))[1] == 0
+    assert _call(lib, "dflash_ctx_fuse", _fuse_args(M=0)) == 0   # valid no-op
+    assert _ws(lib, "fuse", _fuse_args(num_layers=0))[0] == -1
+    assert _ws(lib, "fuse", _fuse_args(num_layers=6))[0] == -1
+    assert _ws(lib, "fuse", _fuse_args(M=-1))[0] == -1
+    assert _call(lib, "dflash_ctx_fuse", _fuse_args(hs_stride=2500), FAKE, n) == -1
+    assert _call(lib, "dflash_ctx_fuse", _fuse_args(wc=None), FAKE, n) == -1
+    a = _fuse_args()
+    a.k_cache[1] = None
+    assert _call(lib, "dflash_ctx_fuse", a, FAKE, n) == -1
+    a = _fuse_args(num_layers=1)
+    a.k_cache[1] = None  # ignored beyond num_layers
+    assert _call(lib, "dflash_ctx_fuse", a, None, 0) == -4
+    assert _call(lib, "dflash_ctx_fuse", _fuse_args(num_pages=0), FAKE, n) == -1
+    assert _ws(lib, "fuse", _fuse_args(M=4096))[1] > n
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+    import block_speculative_decoding_amd as dfl
+    z = torch.zeros((2, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(dfl.DFlashError):
+        dfl.spec_verify(z, z[:, :7], torch.zeros((2, 7), dtype=torch.int32), torch.zeros(2))

@@ -1,0 +1,114 @@
+"""GPU parity of dflash_ctx_fuse against the oracle: the fused context H_t
+and the K/V written at each slot (max abs error 2e-2 bf16, 1e-4 fp32)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_speculative_decoding_amd import synth
+from tests.gpu_util import BF16, F32, TOL, dev, exact, note
+from tests.layout import k_offsets, v_offsets, read_slots
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(M, L, dtype, seed, npages, slots, pos, rows=None, sentinel=-7.0):
+    import block_speculative_decoding_amd as dfl
+    hs_np = synth.capture_states(seed, M)
+    w = synth.fuse_weights(seed, L)
+    hs = [dev(h, dtype) for h in hs_np]
+    del hs_np
+    wc, gc, wkv, gk = (dev(w[k], dtype) for k in ("wc", "gc", "wkv", "gk"))
+    kcs = [torch.full((npages, 8, 2048), sentinel, dtype=dtype, device="cuda") for _ in range(L)]
+    vcs = [torch.full((npages, 8, 2048), sentinel, dtype=dtype, device="cuda") for _ in range(L)]
+    ht = torch.empty((M, 2560), dtype=dtype, device="cuda")
+    dfl.ctx_fuse(hs, wc, gc, wkv, gk, dev(pos, torch.int32), dev(slots, torch.int64), kcs, vcs, ht_out=ht)
+    torch.cuda.synchronize()
+    rows = np.arange(M) if rows is None else np.asarray(rows)
+    rsel = torch.from_numpy(rows).cuda()
+    ht_ref, _, K, V = oracle.ctx_fuse_ref([exact(h.index_select(0, rsel)) for h in hs], exact(wc), exact(gc),
+                                          exact(wkv), exact(gk), pos[rows], ht_bf16=(dtype == BF16))
+    ht_err = np.max(np.abs(exact(ht.index_select(0, rsel)) - ht_ref))
+    kv_err = 0.0
+    for l in range(L):
+        kg = read_slots(exact(kcs[l]), slots[rows], k_offsets())
+        vg = read_slots(exact(vcs[l]), slots[rows], v_offsets())
+        kv_err = max(kv_err, np.max(np.abs(kg - K[l])), np.max(np.abs(vg - V[l])))
+    return ht_err, kv_err, kcs, vcs
+
+
+def test_fuse_bf16_small_scattered():
+    M, L, npages = 40, 2, 8
+    rng = np.random.default_rng(0)
+    slots = rng.permutation(npages * 16)[:M].astype(np.int64)
+    pos = rng.integers(0, 131072, M).astype(np.int32)
+    ht_err, kv_err, kcs, _ = _run(M, L, BF16, 1, npages, slots, pos)
+    note(f"fuse bf16 M=40 L=2: H_t err {ht_err:.3e}, K/V err {kv_err:.3e}")
+    assert ht_err <= TOL[BF16] and kv_err <= TOL[BF16]
+    # Slots not named keep their contents.
+    untouched = np.setdiff1d(np.arange(npages * 16), slots)
+    kk = read_slots(exact(kcs[0]), untouched, k_offsets())
+    assert np.all(kk == -7.0)
+
+
+def test_fuse_fp32_config1_tiny():
+    """M=128 context rows, one draft layer, fp32, positions 0..127."""
+    M, L, npages = 128, 1, 8
+    slots = np.arange(M, dtype=np.int64)
+    pos = np.arange(M, dtype=np.int32)
+    ht_err, kv_err, _, _ = _run(M, L, F32, 0, npages, slots, pos)
+    note(f"fuse fp32 M=128: H_t err {ht_err:.3e}, K/V err {kv_err:.3e}")
+    assert ht_err <= TOL[F32] and kv_err <= TOL[F32]
+
+
+def test_fuse_skips_out_of_range_slots():
+    M, L, npages = 16, 1, 2
+    pos = np.arange(M, dtype=np.int32)
+    # Every slot is negative or past the cache: nothing may be written.
+    import block_speculative_decoding_amd as dfl
+    hs = [dev(h, BF16) for h in synth.capture_states(2, M)]
+    w = synth.fuse_weights(2, L)
+    wc, gc, wkv, gk = (dev(w[k], BF16) for k in ("wc", "gc", "wkv", "gk"))
+    kc = torch.full((npages, 8, 2048), -7.0, dtype=BF16, device="cuda")
+    vc = torch.full((npages, 8, 2048), -7.0, dtype=BF16, device="cuda")
+    bad = np.array([-1, -5, npages * 16, npages * 16 + 100] * 4, dtype=np.int64)
+    dfl.ctx_fuse(hs, wc, gc, wkv, gk, dev(pos, torch.int32), dev(bad, torch.int64), [kc], [vc])
+    torch.cuda.synchronize()
+    assert torch.all(kc == -7.0) and torch.all(vc == -7.0)
+
+
+def test_fuse_serving_new_rows():
+    """Serving shape: 64 sequences x 1..8 newly verified rows (M = sum),
+    five layers, appended at ctx_len .. ctx_len + n - 1 of shuffled pages."""
+    B = 64
+    n = synth.new_rows(2, B)
+    M = int(n.sum())
+    ctx = np.full(B, 8192, dtype=np.int32)
+    table, npages = synth.page_table(2, ctx + 8)
+    slots, pos = [], []
+    for b in range(B):
+        for r in range(n[b]):
+            t = ctx[b] + r
+            slots.append(table[b, t // 16] * 16 + t % 16)
+            pos.append(t)
+    slots = np.array(slots, dtype=np.int64)
+    pos = np.array(pos, dtype=np.int32)
+    ht_err, kv_err, _, _ = _run(M, 5, BF16, 2, npages, slots, pos)
+    note(f"fuse serving M={M} L=5: H_t err {ht_err:.3e}, K/V err {kv_err:.3e}")
+    assert ht_err <= TOL[BF16] and kv_err <= TOL[BF16]
+
+
+def test_fuse_prefill_full_size_sampled_rows():
+    """Prefill shape: M=32768 rows, five layers, positions 0..32767; sampled
+    rows checked one by one (fusion is row-independent)."""
+    M, L = 32768, 5
+    npages = M // 16
+    slots = np.arange(M, dtype=np.int64)
+    pos = np.arange(M, dtype=np.int32)
+    rows = np.random.default_rng(5).choice(M, 48, replace=False)
+    rows.sort()
+    rows[-1] = M - 1
+    ht_err, kv_err, _, _ = _run(M, L, BF16, 4, npages, slots, pos, rows=rows)
+    note(f"fuse prefill M=32768 L=5 sampled: H_t err {ht_err:.3e}, K/V err {kv_err:.3e}")
+    assert ht_err <= TOL[BF16] and kv_err <= TOL[BF16]

@@ -1,0 +1,145 @@
+"""GPU parity of dflash_spec_verify against the oracle: bit-exact tokens and
+lengths on shared Philox streams (near-ties counted and excluded)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_speculative_decoding_amd import synth
+from tests.gpu_util import BF16, F32, dev, exact, compare_verify, note
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(zt, zd, d, temp, seed, offset, dtype, B_check=None):
+    import block_speculative_decoding_amd as dfl
+    zt_d, zd_d = dev(zt, dtype), dev(zd, dtype)
+    toks, lens, nt = dfl.spec_verify(zt_d, zd_d, dev(d, torch.int32), dev(temp, F32), seed=seed, offset=offset)
+    torch.cuda.synchronize()
+    sel = np.arange(zt.shape[0]) if B_check is None else np.asarray(B_check)
+    tr = oracle.spec_verify_ref(exact(zt_d)[sel], exact(zd_d)[sel], d[sel], temp[sel], seed, offset)
+    return toks.cpu().numpy()[sel], lens.cpu().numpy()[sel], int(nt.item()), tr, sel
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_verify_mixed_ragged_vocab(dtype):
+    """B=24, V=50000 (ragged against both chunk sizes), temperatures mixed."""
+    B, V, seed = 24, 50000, 11
+    note(f"verify mixed B={B} V={V} {dtype}")
+    zt, zd = synth.logits(seed, B, V, 3.0, 1.0)
+    temp = np.array([0.0, 0.7, 1.0, 1.7] * (B // 4), dtype=np.float32)
+    d = synth.sample_drafts(seed, exact(dev(zd, dtype)), temp)
+    toks, lens, nt, tr, _ = _run(zt, zd, d, temp, 5, 17, dtype)
+    excl = compare_verify(toks, lens, tr)
+    assert excl <= 2
+    assert nt == tr.near_ties
+    assert np.all((lens >= 1) & (lens <= 8))
+
+
+def test_verify_config1_fp32_tiny():
+    """B=1, V=4096, fp32, logits N(0, 3^2): independent draft rows, rows with
+    draft = target + N(0,1), and planted matches; greedy and T=1."""
+    V = 4096
+    for variant in ("independent", "noisy", "planted"):
+        rng = np.random.default_rng(0)
+        zt = (rng.standard_normal((1, 8, V)) * 3).astype(np.float32)
+        if variant == "independent":
+            zd = (rng.standard_normal((1, 7, V)) * 3).astype(np.float32)
+        else:
+            zd = zt[:, :7] + rng.standard_normal((1, 7, V)).astype(np.float32)
+        for T in (0.0, 1.0):
+            temp = np.array([T], dtype=np.float32)
+            if variant == "planted":
+                d = np.argmax(zt[:, :7], -1).astype(np.int32)
+            else:
+                d = synth.sample_drafts(0, zd, temp)
+            note(f"verify config1 {variant} T={T}")
+            toks, lens, nt, tr, _ = _run(zt, zd, d, temp, 0, 0, F32)
+            compare_verify(toks, lens, tr)
+            if variant == "planted" and T == 0.0:
+                assert lens[0] == 8
+
+
+def test_verify_planted_rejections_and_all_accept():
+    B, V = 16, 1024
+    rng = np.random.default_rng(3)
+    zt = rng.standard_normal((B, 8, V)).astype(np.float32)
+    zd = zt[:, :7].copy()
+    d = rng.integers(0, V, (B, 7)).astype(np.int32)
+    # sequences 0..6: sampled rejection forced at k = b + 1; 7..13 greedy mismatch at k = b - 6
+    for b in range(7):
+        k = b + 1
+        zt[b, k - 1, d[b, k - 1]] = -60.0
+        zd[b, k - 1, d[b, k - 1]] = 60.0
+    am = np.argmax(zt, -1)
+    for b in range(7, 14):
+        k = b - 6
+        d[b] = am[b, :7]
+        d[b, k - 1] = (am[b, k - 1] + 1) % V
+    d[14] = am[14, :7]            # greedy, all accepted
+    temp = np.ones(B, dtype=np.float32)
+    temp[7:15] = 0.0              # 15: sampled with q == p -> all accepted, bonus draw
+    toks, lens, nt, tr, _ = _run(zt, zd, d, temp, 9, 2, F32)
+    compare_verify(toks, lens, tr)
+    assert list(lens[:7]) == [1, 2, 3, 4, 5, 6, 7]
+    assert list(lens[7:14]) == [1, 2, 3, 4, 5, 6, 7]
+    assert lens[14] == 8 and lens[15] == 8
+
+
+def test_verify_planted_near_tie_is_counted():
+    """p(d)/q(d) placed 5e-7 above the acceptance uniform: both sides count it."""
+    V = 8
+    u = oracle.uniforms(4, 6, 0, 0, 1, 0)  # U(stream 0, b=0, k=1, i=0)
+    target = float(u) + 5e-7
+    zd = np.zeros((1, 7, V), dtype=np.float32)   # q uniform: q(x) = 1/8
+    zt = np.zeros((1, 8, V), dtype=np.float32)
+    # p(d) = e^a / (e^a + 7) = target / 8  ->  e^a = 7 target / (8 - target)
+    zt[0, 0, 3] = np.float32(np.log(7 * target / (8 - target)))
+    d = np.full((1, 7), 3, dtype=np.int32)
+    temp = np.ones(1, dtype=np.float32)
+    toks, lens, nt, tr, _ = _run(zt, zd, d, temp, 4, 6, F32)
+    assert tr.near_ties == 1 and tr.near_tie_k[0] == 1
+    assert nt == 1
+
+
+def test_verify_strided_draft_view_and_determinism():
+    """Draft rows given as rows 1..7 of a [B, 8, V] tensor (the drafter's
+    output shifted by one row); two runs give identical results."""
+    import block_speculative_decoding_amd as dfl
+    B, V, seed = 6, 8192, 21
+    zt, zd7 = synth.logits(seed, B, V, 4.0, 1.0)
+    full = np.concatenate([np.zeros((B, 1, V), np.float32), zd7], axis=1)
+    temp = np.array([0.0, 0.7, 1.0, 0.0, 0.7, 1.0], dtype=np.float32)
+    zt_d, full_d = dev(zt, BF16), dev(full, BF16)
+    zd_view = full_d[:, 1:]
+    d = synth.sample_drafts(seed, exact(zd_view), temp)
+    outs = [dfl.spec_verify(zt_d, zd_view, dev(d, torch.int32), dev(temp, F32), seed=1, offset=2) for _ in range(2)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    tr = oracle.spec_verify_ref(exact(zt_d), exact(zd_view), d, temp, 1, 2)
+    compare_verify(outs[0][0].cpu().numpy(), outs[0][1].cpu().numpy(), tr)
+
+
+def test_verify_serving_batch_full_size():
+    """Serving-batch shape: [64, 8, 262144] bf16, N(0, 4^2), draft = target +
+    N(0, 1); first half greedy, second half T = 0.7."""
+    B, V, seed = 64, 262144, 2
+    note("verify serving batch B=64 V=262144")
+    zt, zd = synth.logits(seed, B, V, 4.0, 1.0)
+    temp = np.where(np.arange(B) < 32, 0.0, 0.7).astype(np.float32)
+    zt_d, zd_d = dev(zt, BF16), dev(zd, BF16)
+    del zt, zd
+    d = synth.sample_drafts(seed, exact(zd_d), temp)
+    import block_speculative_decoding_amd as dfl
+    toks, lens, nt = dfl.spec_verify(zt_d, zd_d, dev(d, torch.int32), dev(temp, F32), seed=2, offset=5)
+    torch.cuda.synchronize()
+    toks, lens = toks.cpu().numpy(), lens.cpu().numpy()
+    excl = 0
+    for b0 in range(0, B, 8):
+        sl = slice(b0, b0 + 8)
+        tr = oracle.spec_verify_ref(exact(zt_d[sl]), exact(zd_d[sl]), d[sl], temp[sl], 2, 5,
+                                    batch_offset=b0)
+        excl += compare_verify(toks[sl], lens[sl], tr)
+    note(f"  mean out_len {lens.mean():.2f}, excluded {excl}, near-ties {nt}")
+    assert excl <= 3

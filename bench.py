@@ -1,0 +1,303 @@
+"""Draft-verify cycle benchmark on one MI355X.
+
+One step = one DFlash draft-verify cycle's hot path on the serving batch:
+  ctx_fuse  of the newly verified rows (1..8 per sequence) into 5 layer caches
+  5 x block_attn (one per draft layer, over ctx_len + new rows)
+  spec_verify over [64, 8, 262144] target and [64, 7, 262144] draft logits
+Inputs are synthetic and already resident in HBM when timing starts.  Prints
+one JSON line (rank 0) with cycles/s, the attention roofline and an oracle
+CPU baseline on a bounded sample.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+B, S_CTX, V, LAYERS = 64, 8192, 262144, 5
+SEED = 2
+ATTN_SRC = os.path.join(ROOT, "block_speculative_decoding_amd", "csrc", "attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_attn_serving_b64_s8192_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Workload:
+    """Serving-batch inputs on the device."""
+
+    def __init__(self, torch, dfl, synth):
+        self.torch = torch
+        dev = torch.device("cuda:0")
+        bf = torch.bfloat16
+        t0 = time.time()
+
+        def d(x, dt=bf):
+            return torch.from_numpy(np.ascontiguousarray(x)).to(dt).to(dev)
+
+        # Paged caches: ctx 8192 + up to 8 new rows per sequence, shuffled pages.
+        self.n_new = synth.new_rows(SEED, B)
+        self.ctx = np.full(B, S_CTX, dtype=np.int32)
+        self.lens = (self.ctx + self.n_new).astype(np.int32)
+        table, npages = synth.page_table(SEED, self.ctx + 8)
+        self.table_np = table
+        self.block_table = d(table, torch.int32)
+        self.ctx_len = d(self.lens, torch.int32)
+        gen = torch.Generator(device=dev).manual_seed(SEED)
+        self.kc, self.vc = [], []
+        for _ in range(LAYERS):
+            self.kc.append(torch.randn((npages, 8, 2048), generator=gen, device=dev, dtype=torch.float32).to(bf))
+            self.vc.append(torch.randn((npages, 8, 2048), generator=gen, device=dev, dtype=torch.float32).to(bf))
+        # New rows: slots and positions right after each context.
+        slots, pos = [], []
+        for b in range(B):
+            for r in range(self.n_new[b]):
+                t = self.ctx[b] + r
+                slots.append(table[b, t // 16] * 16 + t % 16)
+                pos.append(t)
+        self.M = len(slots)
+        self.hs_np = synth.capture_states(SEED, self.M)
+        self.w_np = synth.fuse_weights(SEED, LAYERS)
+        self.hs = [d(h) for h in self.hs_np]
+        w = {k: d(v) for k, v in self.w_np.items()}
+        self.pos_np = np.array(pos, dtype=np.int32)
+        self.fuse = dfl.prepare_ctx_fuse(self.hs, w["wc"], w["gc"], w["wkv"], w["gk"], d(self.pos_np, torch.int32),
+                                         d(np.array(slots, dtype=np.int64), torch.int64), self.kc, self.vc)
+        # Per-layer block inputs.
+        self.blk_np = [synth.attn_block(SEED, B, layer=l) for l in range(LAYERS)]
+        self.attn = []
+        ws = None
+        for l in range(LAYERS):
+            bl = {k: d(v) for k, v in self.blk_np[l].items()}
+            p = dfl.prepare_block_attn(bl["q"], bl["k_blk"], bl["v_blk"], bl["gq"], bl["gk"], self.kc[l],
+                                       self.vc[l], self.block_table, self.ctx_len, workspace=ws)
+            ws = p.workspace  # one workspace shared by the five layers (same stream)
+            self.attn.append(p)
+        # Logits: N(0, 4^2) target, draft = target + N(0, 1); half greedy, half T = 0.7.
+        zt, zd = synth.logits(SEED, B, V, 4.0, 1.0)
+        self.temp_np = np.where(np.arange(B) < B // 2, 0.0, 0.7).astype(np.float32)
+        self.zt, self.zd = d(zt), d(zd)
+        del zt, zd
+        self.d_np = synth.sample_drafts(SEED, self.zd.float().cpu().numpy(), self.temp_np)
+        self.verify = dfl.prepare_spec_verify(self.zt, self.zd, d(self.d_np, torch.int32),
+                                              d(self.temp_np, torch.float32), seed=SEED, offset=0)
+        torch.cuda.synchronize()
+        log(f"[bench] inputs ready in {time.time() - t0:.1f}s: M={self.M} new rows, "
+            f"{npages} pages/layer, cache {LAYERS * 2 * self.kc[0].numel() * 2 / 1e9:.2f} GB")
+
+    def step(self, offset, ev=None):
+        self.verify.args.offset = offset
+        if ev is None:
+            self.fuse()
+            for a in self.attn:
+                a()
+            self.verify()
+            return
+        ev["fuse"][0].record()
+        self.fuse()
+        ev["fuse"][1].record()
+        for a in self.attn:
+            e0, e1 = ev["attn"].pop()
+            e0.record()
+            a()
+            e1.record()
+            ev["attn_done"].append((e0, e1))
+        ev["verify"][0].record()
+        self.verify()
+        ev["verify"][1].record()
+
+
+def attn_bytes(lens):
+    """Algorithmic bytes of one block_attn launch: K and V of every cached
+    token (8 heads x 128 x bf16 x 2) plus q, block K/V and out per sequence."""
+    per_seq = 32 * 8 * 128 * 2 * 2 + 2 * 8 * 8 * 128 * 2
+    return int(np.sum(lens.astype(np.int64) * 4096) + len(lens) * per_seq)
+
+
+def verify_bytes(temp):
+    rows = np.where(temp > 0, 15, 8)
+    return int(rows.sum() * V * 2)
+
+
+def fuse_flops_bytes(M):
+    flops = 2 * M * (12800 * 2560 + LAYERS * 2048 * 2560)
+    bytes_ = (12800 * 2560 + LAYERS * 2048 * 2560) * 2 + M * (5 * 2560 * 2 + LAYERS * 2048 * 2)
+    return flops, bytes_
+
+
+def src_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_per_launch():
+    """HBM bytes per block_attn launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("attn_src_sha256_16") != src_hash(ATTN_SRC):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(wl):
+    """The oracle as it stands, on a bounded sample of the same workload,
+    scaled to one full cycle: the fusion of all new rows, block attention of
+    4 sequences x 5 layers (x 16 for 64 sequences) and verification of 8
+    sequences (4 greedy + 4 sampled; x 8)."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    torch = wl.torch
+    t0 = time.perf_counter()
+    oracle.ctx_fuse_ref([h.astype(np.float64) for h in wl.hs_np], wl.w_np["wc"], wl.w_np["gc"], wl.w_np["wkv"],
+                        wl.w_np["gk"], wl.pos_np)
+    t_fuse = time.perf_counter() - t0
+    sample_b = [0, 21, 42, 63]
+    from tests.layout import k_offsets, v_offsets, unpack
+    t_attn = 0.0
+    for l in range(LAYERS):
+        for b in sample_b:
+            pages = torch.from_numpy(wl.table_np[b][wl.table_np[b] >= 0].astype(np.int64)).cuda()
+            kb = wl.kc[l].index_select(0, pages).float().cpu().numpy()
+            vb = wl.vc[l].index_select(0, pages).float().cpu().numpy()
+            loc = np.arange(len(pages))
+            kctx = unpack(kb, loc, int(wl.lens[b]), k_offsets()).astype(np.float64)
+            vctx = unpack(vb, loc, int(wl.lens[b]), v_offsets()).astype(np.float64)
+            blk = wl.blk_np[l]
+            t1 = time.perf_counter()
+            oracle.block_attn_ref(blk["q"][b:b + 1], blk["k_blk"][b:b + 1], blk["v_blk"][b:b + 1], blk["gq"],
+                                  blk["gk"], [kctx], [vctx], wl.lens[b:b + 1])
+            t_attn += time.perf_counter() - t1
+    vb_sel = [0, 1, 2, 3, 32, 33, 34, 35]
+    zt = wl.zt[vb_sel].float().cpu().numpy()
+    zd = wl.zd[vb_sel].float().cpu().numpy()
+    t1 = time.perf_counter()
+    for i, b in enumerate(vb_sel):
+        oracle.spec_verify_ref(zt[i:i + 1], zd[i:i + 1], wl.d_np[b:b + 1], wl.temp_np[b:b + 1], SEED, 0,
+                               batch_offset=b)
+    t_ver = time.perf_counter() - t1
+    cycle = t_fuse + t_attn * (B / len(sample_b)) + t_ver * (B / len(vb_sel))
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {
+        "value": round(1.0 / cycle, 6), "unit": "cycles/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"float64 numpy oracle: fusion of all {wl.M} new rows ({t_fuse:.2f}s), block attention of "
+                   f"4 of 64 sequences x 5 layers ({t_attn:.2f}s, scaled x16), verification of 8 of 64 "
+                   f"sequences, 4 greedy + 4 sampled ({t_ver:.2f}s, scaled x8); "
+                   f"{t_fuse + t_attn + t_ver:.1f}s measured, {cycle:.1f}s per scaled cycle"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "requested_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import block_speculative_decoding_amd as dfl
+    from block_speculative_decoding_amd import synth
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    dfl.load()
+    wl = Workload(torch, dfl, synth)
+
+    for i in range(args.warmup):
+        wl.step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+
+    K = args.steps
+    ev = {"fuse": None, "verify": None, "attn": [], "attn_done": []}
+    fuse_ms, attn_ms, ver_ms = [], [], []
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per_step = []
+    for i in range(K):
+        per_step.append({"fuse": (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)),
+                         "verify": (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)),
+                         "attn": [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                                  for _ in range(LAYERS)],
+                         "attn_done": []})
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        wl.step(args.warmup + i, per_step[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    for e in per_step:
+        fuse_ms.append(e["fuse"][0].elapsed_time(e["fuse"][1]))
+        ver_ms.append(e["verify"][0].elapsed_time(e["verify"][1]))
+        attn_ms.extend(a.elapsed_time(b) for a, b in e["attn_done"])
+    ms_step = total_ms / K
+    log(f"[bench] {K} steps: {ms_step:.3f} ms/step")
+
+    a_bytes = attn_bytes(wl.lens)
+    a_ms = float(np.mean(attn_ms))
+    a_gbs = a_bytes / (a_ms * 1e-3) / 1e9
+    v_bytes = verify_bytes(wl.temp_np)
+    v_ms = float(np.mean(ver_ms))
+    f_flops, f_bytes = fuse_flops_bytes(wl.M)
+    f_ms = float(np.mean(fuse_ms))
+    traffic = traffic_per_launch()
+    out_len = wl.verify.outputs[1].float().mean().item()
+
+    res = {
+        "metric": "draft-verify cycles/s @B=64,S=8192; attn/verify HBM GB/s; fuse GEMM MFMA %",
+        "value": round(1000.0 / ms_step, 3),
+        "unit": "cycles/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "serving batch: B=64, cached context 8192 + 1..8 newly verified rows per "
+                               "sequence (shuffled 16-token pages), 5 draft layers, ctx-fuse of the new rows, "
+                               "block attention per layer, spec-verify over V=262144 (32 greedy, 32 at T=0.7)",
+                   "B": B, "S": S_CTX, "new_rows": int(wl.M), "layers": LAYERS, "V": V, "parallelism": "none"},
+        "roofline": {"kernel": "block_attn (attn_bf16_kernel + attn_merge_kernel)", "bound": "hbm",
+                     "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(a_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic / (a_ms * 1e-3) / 1e9, 1),
+                     "algorithmic_bytes_per_launch": a_bytes, "avg_launch_ms": round(a_ms, 4)},
+        "kernels": {
+            "block_attn": {"ms": round(a_ms, 4), "GB/s": round(a_gbs, 1), "hbm_frac": round(a_gbs / HBM_PEAK_GBS, 4)},
+            "spec_verify": {"ms": round(v_ms, 4), "GB/s": round(v_bytes / (v_ms * 1e-3) / 1e9, 1),
+                            "hbm_frac": round(v_bytes / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "algorithmic_bytes": v_bytes, "mean_out_len": round(out_len, 3)},
+            "ctx_fuse": {"ms": round(f_ms, 4), "M": int(wl.M), "TFLOP/s": round(f_flops / (f_ms * 1e-3) / 1e12, 1),
+                         "mfma_frac": round(f_flops / (f_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "GB/s": round(f_bytes / (f_ms * 1e-3) / 1e9, 1)},
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -148,8 +148,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnParams p) {
                 kbs[jj * kQStride + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[e]);
                 kbs[jj * kQStride + 64 + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[8 + e]);
             }
-        } else if (tid < 128) {
-            const int t2 = tid - 64;  // 64 threads x 16 B = 2 KiB of v_blk
+        } else if (tid < 192) {
+            const int t2 = tid - 64;  // 128 threads x 16 B = the 2 KiB of v_blk (8 x 128 bf16)
             const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.vb) +
                                                               (((int64_t)b * 8 + g) * 8 * 128));
             reinterpret_cast<uint4*>(vbs)[t2] = src[t2];

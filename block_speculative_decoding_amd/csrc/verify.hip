@@ -72,7 +72,11 @@ __device__ __forceinline__ Scale make_scale(float T) {
     r.lo = (float)(s - (double)r.hi);
     return r;
 }
-__device__ __forceinline__ float scaled(float dz, Scale s) { return fmaf(dz, s.hi, dz * s.lo); }
+// -inf (an empty running max) maps to -inf; the split product alone would give
+// -inf + inf = NaN whenever lo < 0.
+__device__ __forceinline__ float scaled(float dz, Scale s) {
+    return dz == -INFINITY ? -INFINITY : fmaf(dz, s.hi, dz * s.lo);
+}
 
 __device__ __forceinline__ bool is_greedy(float T) { return !(T > 0.f); }
 

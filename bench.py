@@ -28,7 +28,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 B, S_CTX, V, LAYERS = 64, 8192, 262144, 5
 SEED = 2
 ATTN_SRC = os.path.join(ROOT, "block_speculative_decoding_amd", "csrc", "attn.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_attn_serving_b64_s8192_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_attn_serving_b64_s8192_traffic.md")
 
 
 def parse():
@@ -152,30 +152,35 @@ def src_hash(path):
 
 def traffic_per_launch():
     """HBM bytes per block_attn launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
+    summary (lines "key: value"), if it was taken on the current kernel
+    source; else None."""
     try:
-        t = json.load(open(TRAFFIC_FILE))
-    except (OSError, ValueError):
+        kv = dict(l.split(":", 1) for l in open(TRAFFIC_FILE).read().splitlines() if ":" in l)
+    except OSError:
         return None
-    if t.get("attn_src_sha256_16") != src_hash(ATTN_SRC):
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("attn_src_sha256_16") != src_hash(ATTN_SRC):
         return None
-    return t.get("bytes_per_launch")
+    try:
+        return float(kv["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(wl):
-    """The oracle as it stands, on a bounded sample of the same workload,
-    scaled to one full cycle: the fusion of all new rows, block attention of
-    4 sequences x 5 layers (x 16 for 64 sequences) and verification of 8
-    sequences (4 greedy + 4 sampled; x 8)."""
+    """The oracle as it stands, timed on the host cores on a bounded sample of
+    the same workload and scaled to one full cycle: the fusion of all new rows,
+    block attention of 16 of the 64 sequences in each of the 5 layers (x4) and
+    verification of 32 of the 64 sequences, 16 greedy + 16 sampled (x2)."""
     import oracle
     from threadpoolctl import threadpool_info
+    from tests.layout import k_offsets, v_offsets, unpack
     torch = wl.torch
     t0 = time.perf_counter()
     oracle.ctx_fuse_ref([h.astype(np.float64) for h in wl.hs_np], wl.w_np["wc"], wl.w_np["gc"], wl.w_np["wkv"],
                         wl.w_np["gk"], wl.pos_np)
     t_fuse = time.perf_counter() - t0
-    sample_b = [0, 21, 42, 63]
-    from tests.layout import k_offsets, v_offsets, unpack
+    sample_b = list(range(0, B, 4))
     t_attn = 0.0
     for l in range(LAYERS):
         for b in sample_b:
@@ -190,21 +195,21 @@ def cpu_baseline(wl):
             oracle.block_attn_ref(blk["q"][b:b + 1], blk["k_blk"][b:b + 1], blk["v_blk"][b:b + 1], blk["gq"],
                                   blk["gk"], [kctx], [vctx], wl.lens[b:b + 1])
             t_attn += time.perf_counter() - t1
-    vb_sel = [0, 1, 2, 3, 32, 33, 34, 35]
-    zt = wl.zt[vb_sel].float().cpu().numpy()
-    zd = wl.zd[vb_sel].float().cpu().numpy()
-    t1 = time.perf_counter()
-    for i, b in enumerate(vb_sel):
-        oracle.spec_verify_ref(zt[i:i + 1], zd[i:i + 1], wl.d_np[b:b + 1], wl.temp_np[b:b + 1], SEED, 0,
-                               batch_offset=b)
-    t_ver = time.perf_counter() - t1
+    vb_sel = list(range(0, 16)) + list(range(32, 48))
+    t_ver = 0.0
+    for b in vb_sel:
+        zt = wl.zt[b:b + 1].float().cpu().numpy()
+        zd = wl.zd[b:b + 1].float().cpu().numpy()
+        t1 = time.perf_counter()
+        oracle.spec_verify_ref(zt, zd, wl.d_np[b:b + 1], wl.temp_np[b:b + 1], SEED, 0, batch_offset=b)
+        t_ver += time.perf_counter() - t1
     cycle = t_fuse + t_attn * (B / len(sample_b)) + t_ver * (B / len(vb_sel))
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {
         "value": round(1.0 / cycle, 6), "unit": "cycles/s", "cores": int(threads), "kind": "oracle",
         "sample": (f"float64 numpy oracle: fusion of all {wl.M} new rows ({t_fuse:.2f}s), block attention of "
-                   f"4 of 64 sequences x 5 layers ({t_attn:.2f}s, scaled x16), verification of 8 of 64 "
-                   f"sequences, 4 greedy + 4 sampled ({t_ver:.2f}s, scaled x8); "
+                   f"16 of 64 sequences x 5 layers ({t_attn:.2f}s, scaled x4), verification of 32 of 64 "
+                   f"sequences, 16 greedy + 16 sampled ({t_ver:.2f}s, scaled x2); "
                    f"{t_fuse + t_attn + t_ver:.1f}s measured, {cycle:.1f}s per scaled cycle"),
     }
 

@@ -33,13 +33,10 @@ def pack(logical, table_row, cache, offsets):
 
 def unpack(cache, table_row, S, offsets):
     """Read logical [S, 8, 128] tokens of one sequence from cache [P, 8, 2048]."""
-    out = np.empty((S, HKV, HEAD_DIM), dtype=cache.dtype)
-    for t0 in range(0, S, PAGE):
-        page = table_row[t0 // PAGE]
-        n = min(PAGE, S - t0)
-        for h in range(HKV):
-            out[t0:t0 + n, h] = cache[page, h][offsets[:n]]
-    return out
+    t = np.arange(S)
+    pages = np.asarray(table_row)[t // PAGE]
+    idx = offsets[t % PAGE]  # [S, 128]
+    return cache[pages[:, None, None], np.arange(HKV)[None, :, None], idx[:, None, :]]
 
 
 def read_slots(cache, slots, offsets):

@@ -19,6 +19,8 @@
 // round-robin; the block's own 8 keys are one extra (masked) tile of the
 // last split.  Waves merge through LDS; splits merge with a log-sum-exp
 // kernel.
+#include <cmath>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -31,6 +33,7 @@ constexpr int kTile = 32;
 constexpr int kQStride = 136;    // bf16 per LDS row of q^ / k^blk (padded)
 constexpr int kAccStride = 132;  // floats per LDS row in the wave merge
 constexpr int kPartFloats = 64 + 32 * 128;  // m[32], l[32], acc[32][128]
+constexpr int kMaxSplit = 32768;            // tokens per split (page ids of a split live in LDS)
 
 struct AttnParams {
     const void* q; const void* kb; const void* vb; const void* gq; const void* gk;
@@ -41,6 +44,7 @@ struct AttnParams {
     int window; int split; int nsplit;
     void* out; float* lse;
     float* part;
+    double inv_freq[64];  // theta^(-i/64), computed on the host in fp64
 };
 
 struct SeqRange { int S, t0, a0, nspl; };
@@ -58,10 +62,9 @@ __device__ __forceinline__ SeqRange seq_range(const AttnParams& p, int b) {
     return r;
 }
 
-// cos/sin of pos * theta^(-i/64): angle and range reduction in fp64, then fp32.
-__device__ __forceinline__ void rope_cs(int pos, int i, double log2_theta, float& c, float& s) {
-    const double inv_freq = exp2(-(double)i * (1.0 / 64.0) * log2_theta);
-    double ang = (double)pos * inv_freq;
+// cos/sin of pos * inv_freq[i]: angle and range reduction in fp64, then fp32.
+__device__ __forceinline__ void rope_cs(int pos, int i, const double* inv_freq, float& c, float& s) {
+    double ang = (double)pos * inv_freq[i];
     const double two_pi = 6.283185307179586;
     ang -= rint(ang * (1.0 / two_pi)) * two_pi;
     sincosf((float)ang, &s, &c);
@@ -70,7 +73,7 @@ __device__ __forceinline__ void rope_cs(int pos, int i, double log2_theta, float
 // Normalise + rotate one 128-wide row spread over 8 consecutive lanes; lane
 // part p holds dims [8p, 8p+8) in x[0..7] and [64+8p, 64+8p+8) in x[8..15].
 __device__ __forceinline__ void norm_rope_16(float* x, const float* g, int part, int pos,
-                                             float eps, double log2_theta) {
+                                             float eps, const double* inv_freq) {
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) ss += x[e] * x[e];
@@ -83,7 +86,7 @@ __device__ __forceinline__ void norm_rope_16(float* x, const float* g, int part,
         const float a = x[e] * rinv * g[e];
         const float bb = x[8 + e] * rinv * g[8 + e];
         float c, s;
-        rope_cs(pos, 8 * part + e, log2_theta, c, s);
+        rope_cs(pos, 8 * part + e, inv_freq, c, s);
         x[e] = a * c - bb * s;
         x[8 + e] = bb * c + a * s;
     }
@@ -101,7 +104,16 @@ __device__ __forceinline__ void load_row16(const T* row, int part, float* x) {
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
 
 // ---------------------------------------------------------------- bf16 MFMA kernel
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnParams p) {
+#ifndef ATTN_PREFETCH
+#define ATTN_PREFETCH 1
+#endif
+#ifndef ATTN_Q_REGS
+#define ATTN_Q_REGS 1
+#endif
+#ifndef ATTN_WAVES_PER_EU
+#define ATTN_WAVES_PER_EU 1
+#endif
+__global__ __launch_bounds__(kThreads, ATTN_WAVES_PER_EU) void attn_bf16_kernel(AttnParams p) {
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const SeqRange sr = seq_range(p, b);
     if (c >= sr.nspl) return;
@@ -109,7 +121,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnParams p) {
     const int te = min(sr.S, tb + p.split);
     const bool last = c == sr.nspl - 1;
     const int ntiles = te > tb ? (te - tb + kTile - 1) / kTile : 0;
-    const int nwork = ntiles + (last ? 1 : 0);
 
     __shared__ __attribute__((aligned(16))) float smem[kWaves * (64 + 32 * kAccStride)];
     uint16_t* qs = reinterpret_cast<uint16_t*>(smem);          // [32][kQStride]
@@ -118,7 +129,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const double log2_theta = log2((double)p.theta);
     const uint16_t* gq = static_cast<const uint16_t*>(p.gq);
     const uint16_t* gk = static_cast<const uint16_t*>(p.gk);
 
@@ -131,7 +141,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnParams p) {
         float x[16], gw[16];
         load_row16(qrow, part, x);
         load_row16(gq, part, gw);
-        norm_rope_16(x, gw, part, sr.S + j, p.eps, log2_theta);
+        norm_rope_16(x, gw, part, sr.S + j, p.eps, p.inv_freq);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             qs[n * kQStride + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[e]);
@@ -142,7 +152,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnParams p) {
             const uint16_t* krow = static_cast<const uint16_t*>(p.kb) + ((((int64_t)b * 8 + g) * 8 + jj) * 128);
             load_row16(krow, part, x);
             load_row16(gk, part, gw);
-            norm_rope_16(x, gw, part, sr.S + jj, p.eps, log2_theta);
+            norm_rope_16(x, gw, part, sr.S + jj, p.eps, p.inv_freq);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 kbs[jj * kQStride + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[e]);
@@ -155,105 +165,103 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnParams p) {
             reinterpret_cast<uint4*>(vbs)[t2] = src[t2];
         }
     }
+    // Physical page ids of this split, staged once in LDS (-1 past the sequence
+    // or out of range) so a tile's K/V addresses need no dependent global read.
+    int* pages = reinterpret_cast<int*>(vbs + 8 * 128);  // [split/16 + 2]
+    const int pg_first = tb >> 4;
+    const int npg = ((te > tb ? te - 1 : tb) >> 4) - pg_first + 2;
+    {
+        const int32_t* bt = p.bt + (int64_t)b * p.max_pages;
+        for (int i = tid; i < npg; i += kThreads) {
+            const int pg = pg_first + i;
+            int ph = -1;
+            if (pg * 16 < te) {
+                ph = bt[pg];
+                if (ph < 0 || (int64_t)ph >= p.num_pages) ph = -1;
+            }
+            pages[i] = ph;
+        }
+    }
     __syncthreads();
 
     const int m32 = lane & 31, hl = lane >> 5;
-    bf16x8 qop[8];
+    const uint16_t* qlds = qs + m32 * kQStride + 64 * hl;  // this lane's Q^T operand row
+#if ATTN_Q_REGS
+    bf16x8 qreg[8];
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-        qop[kb] = *reinterpret_cast<const bf16x8*>(qs + m32 * kQStride + 64 * hl + 8 * kb);
-
-    const float sl2 = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
+    for (int kb = 0; kb < 8; ++kb) qreg[kb] = *reinterpret_cast<const bf16x8*>(qlds + 8 * kb);
+#endif
+    const float sl2 = kLog2e * 0.08838834764831845f;      // log2(e) / sqrt(128)
     const uint16_t* kc = static_cast<const uint16_t*>(p.kc);
     const uint16_t* vc = static_cast<const uint16_t*>(p.vc);
-    const int32_t* bt = p.bt + (int64_t)b * p.max_pages;
 
     f32x16 acc[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[db] = (f32x16){};
     float m_run = -INFINITY, l_run = 0.f;
+    const uint4 z4 = make_uint4(0, 0, 0, 0);
 
-    for (int it = wave; it < nwork; it += kWaves) {
-        bf16x8 kop[8], vop[2][4];
-        const bool blk = it >= ntiles;  // the block's own keys
+    // Issue the loads of context tile `it` into kr / vr.  Loads are
+    // unconditional (a missing page reads page 0 and is zeroed in process)
+    // so the compiler can wait for one tile while the next is in flight.
+    auto load = [&](int it, uint4 (&kr)[8], uint4 (&vr)[2][4]) {
         const int T0 = tb + it * kTile;
-        if (!blk) {
-            int phys[2];
+        const int li = (T0 >> 4) - pg_first;
+        const int ph0 = max(pages[li], 0), ph1 = max(pages[li + 1], 0);
+        const int myk = (m32 >> 4) ? ph1 : ph0;
+        const uint4* kp = reinterpret_cast<const uint4*>(kc + ((int64_t)myk * 8 + g) * 2048 + 8 * ((m32 & 15) + 16 * hl));
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const int pg = (T0 >> 4) + h2;
-                int ph = -1;
-                if (pg * 16 < te) ph = bt[pg];
-                phys[h2] = (ph >= 0 && (int64_t)ph < p.num_pages) ? ph : -1;
-            }
-            const int myk = phys[m32 >> 4];
-            if (myk >= 0) {
-                const uint4* kp = reinterpret_cast<const uint4*>(
-                    kc + ((int64_t)myk * 8 + g) * 2048 + 8 * ((m32 & 15) + 16 * hl));
+        for (int kb = 0; kb < 8; ++kb) kr[kb] = kp[32 * kb];
 #pragma unroll
-                for (int kb = 0; kb < 8; ++kb) kop[kb] = as_bf16x8(kp[32 * kb]);
-            } else {
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            const int ph = kb2 ? ph1 : ph0;
+            const uint4* vp = reinterpret_cast<const uint4*>(vc + ((int64_t)ph * 8 + g) * 2048 + 256 * hl + 8 * m32);
 #pragma unroll
-                for (int kb = 0; kb < 8; ++kb) kop[kb] = as_bf16x8(make_uint4(0, 0, 0, 0));
+            for (int db = 0; db < 4; ++db) vr[kb2][db] = vp[64 * db];
+        }
+    };
+
+    // Scores, online softmax and P.V for one loaded tile.  `blk` marks the
+    // block's own 8 keys (rows 0..7 valid).
+    auto process = [&](int it, bool blk, uint4 (&kr)[8], uint4 (&vr)[2][4]) {
+        const int T0 = tb + it * kTile;
+        if (!blk && T0 + kTile > te) {
+            // Tokens at or past the split end: their pages may be missing or
+            // their slots unwritten, so zero keys and values.
+            const int li = (T0 >> 4) - pg_first;
+            const bool kmiss = pages[li + (m32 >> 4)] < 0 || T0 + m32 >= te;
+            if (kmiss) {
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) kr[kb] = z4;
             }
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2) {
-                const int ph = phys[kb2];
-                if (ph >= 0) {
-                    const uint4* vp = reinterpret_cast<const uint4*>(
-                        vc + ((int64_t)ph * 8 + g) * 2048 + 256 * hl + 8 * m32);
-                    uint4 w[4];
+                const int tbase = T0 + 16 * kb2 + 4 * hl;  // tokens tbase+{0..3}, tbase+8+{0..3}
 #pragma unroll
-                    for (int db = 0; db < 4; ++db) w[db] = vp[64 * db];
-                    // Slots at or past the sequence end may hold garbage: zero them.
-                    const int tbase = T0 + 16 * kb2 + 4 * hl;  // tokens tbase+{0,1,2,3}, tbase+8+{0..3}
-                    if (tbase + 11 >= te) {
-#pragma unroll
-                        for (int db = 0; db < 4; ++db) {
-                            if (tbase + 0 >= te) w[db].x &= 0xFFFF0000u;
-                            if (tbase + 1 >= te) w[db].x &= 0x0000FFFFu;
-                            if (tbase + 2 >= te) w[db].y &= 0xFFFF0000u;
-                            if (tbase + 3 >= te) w[db].y &= 0x0000FFFFu;
-                            if (tbase + 8 >= te) w[db].z &= 0xFFFF0000u;
-                            if (tbase + 9 >= te) w[db].z &= 0x0000FFFFu;
-                            if (tbase + 10 >= te) w[db].w &= 0xFFFF0000u;
-                            if (tbase + 11 >= te) w[db].w &= 0x0000FFFFu;
-                        }
-                    }
-#pragma unroll
-                    for (int db = 0; db < 4; ++db) vop[kb2][db] = as_bf16x8(w[db]);
-                } else {
-#pragma unroll
-                    for (int db = 0; db < 4; ++db) vop[kb2][db] = as_bf16x8(make_uint4(0, 0, 0, 0));
+                for (int db = 0; db < 4; ++db) {
+                    uint4& w = vr[kb2][db];
+                    if (tbase + 0 >= te) w.x &= 0xFFFF0000u;
+                    if (tbase + 1 >= te) w.x &= 0x0000FFFFu;
+                    if (tbase + 2 >= te) w.y &= 0xFFFF0000u;
+                    if (tbase + 3 >= te) w.y &= 0x0000FFFFu;
+                    if (tbase + 8 >= te) w.z &= 0xFFFF0000u;
+                    if (tbase + 9 >= te) w.z &= 0x0000FFFFu;
+                    if (tbase + 10 >= te) w.w &= 0xFFFF0000u;
+                    if (tbase + 11 >= te) w.w &= 0x0000FFFFu;
                 }
             }
-        } else {
-            if (m32 < 8) {
-#pragma unroll
-                for (int kb = 0; kb < 8; ++kb)
-                    kop[kb] = *reinterpret_cast<const bf16x8*>(kbs + m32 * kQStride + 64 * hl + 8 * kb);
-            } else {
-#pragma unroll
-                for (int kb = 0; kb < 8; ++kb) kop[kb] = as_bf16x8(make_uint4(0, 0, 0, 0));
-            }
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                const int d = 32 * db + m32;
-                uint4 w;
-                w.x = (uint32_t)vbs[(4 * hl + 0) * 128 + d] | ((uint32_t)vbs[(4 * hl + 1) * 128 + d] << 16);
-                w.y = (uint32_t)vbs[(4 * hl + 2) * 128 + d] | ((uint32_t)vbs[(4 * hl + 3) * 128 + d] << 16);
-                w.z = 0;
-                w.w = 0;
-                vop[0][db] = as_bf16x8(w);
-                vop[1][db] = as_bf16x8(make_uint4(0, 0, 0, 0));
-            }
         }
-
         // S^T = K . Q^T  (rows: tokens of the tile, columns: the 32 query rows)
         f32x16 s = {};
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kb], qop[kb], s, 0, 0, 0);
-
+        for (int kb = 0; kb < 8; ++kb) {
+#if ATTN_Q_REGS
+            const bf16x8 qop = qreg[kb];
+#else
+            const bf16x8 qop = *reinterpret_cast<const bf16x8*>(qlds + 8 * kb);
+#endif
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[kb]), qop, s, 0, 0, 0);
+        }
         // Lane holds query row m32 and tokens 8*jj + 4*hl + r  (register 4*jj + r).
         float pv[16];
         float tmax = -INFINITY;
@@ -261,8 +269,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnParams p) {
         for (int r = 0; r < 16; ++r) {
             const int tok = 8 * (r >> 2) + 4 * hl + (r & 3);
             bool valid;
-            if (blk) valid = tok < 8;
-            else {
+            if (blk) {
+                valid = tok < 8;
+            } else {
                 const int t = T0 + tok;
                 valid = t >= sr.t0 && t < te;
             }
@@ -291,8 +300,58 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnParams p) {
         const bf16x8 pb1 = as_bf16x8(make_uint4(pk[4], pk[5], pk[6], pk[7]));
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[0][db], pb0, acc[db], 0, 0, 0);
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[1][db], pb1, acc[db], 0, 0, 0);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr[0][db]), pb0, acc[db], 0, 0, 0);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr[1][db]), pb1, acc[db], 0, 0, 0);
+        }
+    };
+
+    {
+        uint4 ka[8], va[2][4];
+#if ATTN_PREFETCH
+        // Two register sets: a wave's next tile is in flight while the current
+        // one is computed.  The last prefetch re-reads the current tile (an L2
+        // hit) so every iteration issues the same loads.
+        uint4 kx[8], vx[2][4];
+        int it = wave;
+        if (it < ntiles) load(it, ka, va);
+        while (it < ntiles) {
+            load(it + kWaves < ntiles ? it + kWaves : it, kx, vx);
+            process(it, false, ka, va);
+            it += kWaves;
+            if (it >= ntiles) break;
+            load(it + kWaves < ntiles ? it + kWaves : it, ka, va);
+            process(it, false, kx, vx);
+            it += kWaves;
+        }
+#else
+        for (int it = wave; it < ntiles; it += kWaves) {
+            load(it, ka, va);
+            process(it, false, ka, va);
+        }
+#endif
+        // The block's own 8 keys / values: one masked tile for the wave next
+        // in the round-robin order, in the last split of the sequence.
+        if (last && wave == (ntiles & (kWaves - 1))) {
+            if (m32 < 8) {
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb)
+                    ka[kb] = *reinterpret_cast<const uint4*>(kbs + m32 * kQStride + 64 * hl + 8 * kb);
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) ka[kb] = z4;
+            }
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const int d = 32 * db + m32;
+                uint4 w;
+                w.x = (uint32_t)vbs[(4 * hl + 0) * 128 + d] | ((uint32_t)vbs[(4 * hl + 1) * 128 + d] << 16);
+                w.y = (uint32_t)vbs[(4 * hl + 2) * 128 + d] | ((uint32_t)vbs[(4 * hl + 3) * 128 + d] << 16);
+                w.z = 0;
+                w.w = 0;
+                va[0][db] = w;
+                va[1][db] = z4;
+            }
+            process(ntiles, true, ka, va);
         }
     }
 
@@ -394,7 +453,6 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnParams p) {
     const SeqRange sr = seq_range(p, b);
     const int tid = threadIdx.x;
     const int n = tid >> 3, part = tid & 7, hh = n >> 3, j = n & 7;
-    const double log2_theta = log2((double)p.theta);
     __shared__ float kbs[8][128];
 
     const float* gq = static_cast<const float*>(p.gq);
@@ -405,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnParams p) {
         const float* krow = static_cast<const float*>(p.kb) + ((((int64_t)b * 8 + g) * 8 + jj) * 128);
         load_row16(krow, part, x);
         load_row16(gk, part, gw);
-        norm_rope_16(x, gw, part, sr.S + jj, p.eps, log2_theta);
+        norm_rope_16(x, gw, part, sr.S + jj, p.eps, p.inv_freq);
 #pragma unroll
         for (int e = 0; e < 8; ++e) { kbs[jj][8 * part + e] = x[e]; kbs[jj][64 + 8 * part + e] = x[8 + e]; }
     }
@@ -413,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnParams p) {
     float q[16];
     load_row16(qrow, part, q);
     load_row16(gq, part, gw);
-    norm_rope_16(q, gw, part, sr.S + j, p.eps, log2_theta);
+    norm_rope_16(q, gw, part, sr.S + j, p.eps, p.inv_freq);
     __syncthreads();
 
     const float* kc = static_cast<const float*>(p.kc);
@@ -489,14 +547,15 @@ AttnPlan attn_plan(const dflash_attn_args& a) {
     if (a.split_tokens > 0) {
         split = a.split_tokens;
     } else {
-        // Aim for ~2048 workgroups (8 per CU on 256 CUs) over B x 8 heads.
+        // One residency round: 256 CUs x 2 workgroups.  Fewer, longer splits
+        // stream better and leave less to merge.
         const int64_t pairs = (int64_t)a.B * 8;
-        int64_t want = (2048 + pairs - 1) / pairs;
+        int64_t want = (512 + pairs - 1) / pairs;
         if (want < 1) want = 1;
         int64_t s = (cap + want - 1) / want;
         s = (s + 127) / 128 * 128;
         if (s < 128) s = 128;
-        if (s > (1 << 30)) s = 1 << 30;
+        if (s > kMaxSplit) s = kMaxSplit;
         split = (int)s;
     }
     pl.split_tokens = split;
@@ -515,6 +574,7 @@ hipError_t launch_attn(const dflash_attn_args& a, const AttnPlan& pl, void* ws, 
     p.window = a.window; p.split = pl.split_tokens > 0 ? pl.split_tokens : (1 << 30); p.nsplit = pl.nsplit;
     p.out = a.out; p.lse = a.lse_out;
     p.part = static_cast<float*>(ws);
+    for (int i = 0; i < 64; ++i) p.inv_freq[i] = std::pow((double)a.rope_theta, -(double)i / 64.0);
     if (a.dtype == DFLASH_F32) {
         attn_f32_kernel<<<dim3(8, a.B), kThreads, 0, s>>>(p);
         return hipGetLastError();

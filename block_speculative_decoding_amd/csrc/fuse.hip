@@ -19,6 +19,8 @@
 // instruction, LDS double-buffered with an XOR swizzle, tiles ordered in
 // 8-row groups and laid out contiguously per XCD so neighbouring tiles that
 // share an operand panel run on the same L2.
+#include <cmath>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -63,46 +65,65 @@ __device__ __forceinline__ TileId tile_id(const GemmParams& p, int tiles_m, int 
     return t;
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+// ---- bf16 GEMM: 128x128 tile, BK = 32, four-stage LDS ring filled by the
+// gfx950 direct global->LDS load (global_load_lds_dwordx4: lane l's 16 bytes
+// land at the wave's LDS base + 16 l).  A stage holds A and B as [128 rows][4
+// chunks of 8 bf16]; chunk c of row r sits at position 4r + (c ^ swz(r)), an
+// XOR pattern that keeps the 16-byte operand reads of 8 or 16 consecutive
+// rows on distinct banks.  The swizzle is applied to the global address each
+// lane fetches, because the LDS position is fixed by the lane index.
+constexpr int BKD = 32;                      // k per stage
+constexpr int kStages = 4;
+constexpr int kStageChunks = 2 * BM * 4;     // A then B, 16-byte chunks
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+__device__ __forceinline__ void dma16(const void* g, uint4* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = p.N / BN;
     const TileId t = tile_id(p, tiles_m, tiles_n);
     if (!t.valid) return;
-    const int nk = p.K / BK;
+    const int nk = p.K / BKD;
     const int kt0 = t.ks * p.kt_per_split;
     const int kt1 = min(nk, kt0 + p.kt_per_split);
     if (kt0 >= kt1) return;
+    const int nloc = kt1 - kt0;
 
-    __shared__ __attribute__((aligned(16))) uint4 lds[2][2][BM * 8];  // [buf][A/B][row*8+chunk]
+    __shared__ __attribute__((aligned(16))) uint4 lds[kStages * kStageChunks];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m0 = t.tm * BM, n0 = t.tn * BN;
     const uint16_t* bmat = static_cast<const uint16_t*>(p.b);
 
-    uint4 ra[4], rb[4];
-    auto gload = [&](int kt) {
-        const int kg = kt * BK;
+    // Each thread issues 4 DMA chunks per stage at positions P = (j & 1) * 256 +
+    // tid of the A half (j = 0, 1) or the B half (j = 2, 3).  Rows past M
+    // read row M-1 (valid memory); their results are never stored.
+    int src_r[4], src_c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int P = (j & 1) * 256 + tid;
+        src_r[j] = P >> 2;
+        src_c[j] = (P & 3) ^ swz(P >> 2);
+    }
+    auto issue = [&](int kt, int slot) {
+        const int kg = kt * BKD;
         const int seg = kg / p.seg_w;
         const int kc = kg - seg * p.seg_w;
         const uint16_t* a = static_cast<const uint16_t*>(p.aseg[seg]);
+        uint4* sbase = lds + slot * kStageChunks;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int id = tid + kThreads * j;
-            const int row = id >> 3, ch = id & 7;
-            const int gm = m0 + row;
-            ra[j] = gm < p.M ? *reinterpret_cast<const uint4*>(a + (int64_t)gm * p.a_stride + kc + 8 * ch)
-                             : make_uint4(0, 0, 0, 0);
-            rb[j] = *reinterpret_cast<const uint4*>(bmat + (int64_t)(n0 + row) * p.K + kg + 8 * ch);
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int id = tid + kThreads * j;
-            const int row = id >> 3, ch = id & 7;
-            lds[buf][0][swz(row, ch)] = ra[j];
-            lds[buf][1][swz(row, ch)] = rb[j];
+            const uint16_t* g = j < 2 ? a + (int64_t)min(m0 + src_r[j], p.M - 1) * p.a_stride + kc + 8 * src_c[j]
+                                      : bmat + (int64_t)(n0 + src_r[j]) * p.K + kg + 8 * src_c[j];
+            // wave-uniform LDS base of this instruction
+            dma16(g, sbase + (j >> 1) * (BM * 4) + (j & 1) * 256 + wave * 64);
         }
     };
 
@@ -115,30 +136,39 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
     const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;
     const int lr = lane & 31, lh = lane >> 5;
 
-    gload(kt0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = kt0; kt < kt1; ++kt) {
-        const int cur = (kt - kt0) & 1;
-        if (kt + 1 < kt1) gload(kt + 1);
+    // Prologue: stages 0..kStages-2 (clamped re-reads past the end are harmless).
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int ch = 2 * s + lh;
-            bf16x8 af[2], bfr[2];
+    for (int s0 = 0; s0 < kStages - 1; ++s0) issue(kt0 + min(s0, nloc - 1), s0);
+
+    for (int i = 0; i < nloc; ++i) {
+        wait_vm<4 * (kStages - 2)>();  // stage i landed; the two newer ones may be in flight
+        // Plain s_barrier: __syncthreads() would also drain every outstanding
+        // load.  A wave's reads of stage i-1 completed before its MFMAs ran.
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(kt0 + min(i + kStages - 1, nloc - 1), (i + kStages - 1) % kStages);
+        const uint4* sa = lds + (i % kStages) * kStageChunks;
+        const uint4* sb = sa + BM * 4;
+        bf16x8 af[2][2], bfr[2][2];  // [k-step][block]: all operand reads first
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                af[i] = __builtin_bit_cast(bf16x8, lds[cur][0][swz(wr + 32 * i + lr, ch)]);
-                bfr[i] = __builtin_bit_cast(bf16x8, lds[cur][1][swz(wc + 32 * i + lr, ch)]);
+        for (int ks = 0; ks < 2; ++ks) {
+            const int ch = 2 * ks + lh;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int ra = wr + 32 * q + lr, rb = wc + 32 * q + lr;
+                af[ks][q] = __builtin_bit_cast(bf16x8, sa[4 * ra + (ch ^ swz(ra))]);
+                bfr[ks][q] = __builtin_bit_cast(bf16x8, sb[4 * rb + (ch ^ swz(rb))]);
             }
+        }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < kt1) lstore(cur ^ 1);
-        __syncthreads();
+                    acc[q][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][q], bfr[ks][j], acc[q][j], 0, 0, 0);
     }
+    wait_vm<0>();  // the clamped trailing loads must land before the workgroup exits
 
     // Lane holds column lr of each 32x32 block, rows 8*jj + 4*lh + r.
     float* out = p.part + (int64_t)t.ks * p.M * p.N;
@@ -189,22 +219,29 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
     }
 }
 
-// Sum split-K partials of one row, RMSNorm with g_c, store H_t.
+// Sum split-K partials of one row, RMSNorm with g_c, store H_t.  The split
+// loop is unrolled to kMaxKs so all partial loads of a row are in flight at once.
+constexpr int kMaxKs = 16;
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void fuse_norm_kernel(const float* part, int ks, int M, const T* gc,
                                                             float eps, T* ht, T* ht_out) {
     constexpr int D = DFLASH_D, PER = D / kThreads;
     const int m = blockIdx.x, tid = threadIdx.x;
     float y[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) y[e] = 0.f;
+#pragma unroll
+    for (int s = 0; s < kMaxKs; ++s) {
+        if (s < ks) {
+            const float* row = part + ((int64_t)s * M + m) * D + tid;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) y[e] += row[kThreads * e];
+        }
+    }
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-        const int c = tid + kThreads * e;
-        float v = 0.f;
-        for (int s = 0; s < ks; ++s) v += part[((int64_t)s * M + m) * D + c];
-        y[e] = v;
-        ss += v * v;
-    }
+    for (int e = 0; e < PER; ++e) ss += y[e] * y[e];
     ss = wave_sum(ss);
     __shared__ float red[kThreads / 64];
     if ((tid & 63) == 0) red[tid >> 6] = ss;
@@ -222,9 +259,10 @@ __global__ __launch_bounds__(kThreads) void fuse_norm_kernel(const float* part, 
 
 struct KvParams {
     const float* part; int ks; int M; int N;
-    const void* gk; float eps; float theta;
+    const void* gk; float eps;
     const int32_t* pos; const int64_t* slot;
     void* kc[5]; void* vc[5]; int64_t num_pages;
+    double inv_freq[64];  // theta^(-i/64), computed on the host in fp64
 };
 
 // One wave per (row, 128-wide head of the [K_0 | V_0 | K_1 | ...] output).
@@ -240,10 +278,13 @@ __global__ __launch_bounds__(kThreads) void fuse_kv_kernel(KvParams p) {
     const int t = (int)(slot & 15);
     const int n0 = hidx * 128;
     float x0 = 0.f, x1 = 0.f;
-    for (int s = 0; s < p.ks; ++s) {
-        const float* row = p.part + ((int64_t)s * p.M + m) * p.N + n0;
-        x0 += row[lane];
-        x1 += row[lane + 64];
+#pragma unroll
+    for (int s = 0; s < kMaxKs; ++s) {
+        if (s < p.ks) {
+            const float* row = p.part + ((int64_t)s * p.M + m) * p.N + n0;
+            x0 += row[lane];
+            x1 += row[lane + 64];
+        }
     }
     const int d0 = lane, d1 = lane + 64;
     if (kv == 0) {
@@ -252,8 +293,7 @@ __global__ __launch_bounds__(kThreads) void fuse_kv_kernel(KvParams p) {
         const T* gk = static_cast<const T*>(p.gk) + l * 128;
         const float a = Elem<T>::load(gk, d0) * (x0 * rinv);
         const float b = Elem<T>::load(gk, d1) * (x1 * rinv);
-        const double inv_freq = exp2(-(double)lane * (1.0 / 64.0) * log2((double)p.theta));
-        double ang = (double)p.pos[m] * inv_freq;
+        double ang = (double)p.pos[m] * p.inv_freq[lane];
         const double two_pi = 6.283185307179586;
         ang -= rint(ang * (1.0 / two_pi)) * two_pi;
         float sn, cs;
@@ -275,9 +315,10 @@ __global__ __launch_bounds__(kThreads) void fuse_kv_kernel(KvParams p) {
 
 int pick_ks(int M, int N, int K) {
     const int tiles = ((M + BM - 1) / BM) * (N / BN);
-    const int nk = K / BK;
-    int ks = (512 + tiles - 1) / tiles;  // aim for ~2 workgroups per CU
-    if (ks > nk / 4) ks = nk / 4;        // keep >= 4 k-tiles per split
+    const int nk = K / BKD;
+    int ks = 512 / tiles;                 // 2 workgroups per CU on 256 CUs, one round
+    if (ks > nk / 8) ks = nk / 8;         // keep >= 8 k-tiles per split
+    if (ks > kMaxKs) ks = kMaxKs;
     if (ks < 1) ks = 1;
     // Every split must own at least one k-tile: recount after rounding.
     const int per = (nk + ks - 1) / ks;
@@ -327,7 +368,7 @@ hipError_t launch_fuse(const dflash_fuse_args& a, const FusePlan& pl, void* ws, 
     for (int i = 0; i < 5; ++i) g1.aseg[i] = a.hs[i];
     g1.a_stride = a.hs_stride; g1.seg_w = DFLASH_D;
     g1.b = a.wc; g1.M = M; g1.N = DFLASH_D; g1.K = DFLASH_NCAPTURE * DFLASH_D;
-    g1.ks = pl.ks1; g1.kt_per_split = (g1.K / BK + pl.ks1 - 1) / pl.ks1;
+    g1.ks = pl.ks1; g1.kt_per_split = (g1.K / (a.dtype == DFLASH_BF16 ? BKD : BK) + pl.ks1 - 1) / pl.ks1;
     g1.part = part1;
     hipError_t e = launch_gemm(g1, a.dtype, s);
     if (e != hipSuccess) return e;
@@ -343,14 +384,15 @@ hipError_t launch_fuse(const dflash_fuse_args& a, const FusePlan& pl, void* ws, 
     GemmParams g2 = {};
     g2.aseg[0] = ht; g2.a_stride = DFLASH_D; g2.seg_w = DFLASH_D;
     g2.b = a.wkv; g2.M = M; g2.N = N2; g2.K = DFLASH_D;
-    g2.ks = pl.ks2; g2.kt_per_split = (g2.K / BK + pl.ks2 - 1) / pl.ks2;
+    g2.ks = pl.ks2; g2.kt_per_split = (g2.K / (a.dtype == DFLASH_BF16 ? BKD : BK) + pl.ks2 - 1) / pl.ks2;
     g2.part = part2;
     e = launch_gemm(g2, a.dtype, s);
     if (e != hipSuccess) return e;
 
     KvParams kp;
     kp.part = part2; kp.ks = pl.ks2; kp.M = M; kp.N = N2;
-    kp.gk = a.gk; kp.eps = a.eps; kp.theta = a.rope_theta;
+    kp.gk = a.gk; kp.eps = a.eps;
+    for (int i = 0; i < 64; ++i) kp.inv_freq[i] = std::pow((double)a.rope_theta, -(double)i / 64.0);
     kp.pos = a.pos; kp.slot = a.slot; kp.num_pages = a.num_pages;
     for (int i = 0; i < 5; ++i) { kp.kc[i] = a.k_cache[i]; kp.vc[i] = a.v_cache[i]; }
     const dim3 gkv(M, a.num_layers * 4);

@@ -177,113 +177,107 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------- decide
-// Merged row statistics: raw max M, sum S (double) of 2^((z - M) * scale), argmax.
-struct RowStat { float m; double s; int idx; };
-
-__device__ RowStat merge_row(const Params& p, int b, int r, double scale_d, bool greedy, int lane) {
-    const StatPart* sp = p.stats + ((int64_t)b * kRows + r) * p.nch1;
-    float m = -INFINITY;
-    int am = 0x7FFFFFFF;
-    for (int c = lane; c < p.nch1; c += 64) {
-        float v = sp[c].m;
-        if (greedy) combine_arg(m, am, v, sp[c].idx);
-        else m = fmaxf(m, v);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        float m2 = __shfl_xor(m, o);
-        int a2 = __shfl_xor(am, o);
-        if (greedy) combine_arg(m, am, m2, a2);
-        else m = fmaxf(m, m2);
-    }
-    double s = 0.0;
-    if (!greedy) {
-        for (int c = lane; c < p.nch1; c += 64) {
-            float mc = sp[c].m;
-            if (mc != -INFINITY) s += (double)sp[c].s * exp2((double)(mc - m) * scale_d);
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-    }
-    RowStat rs;
-    rs.m = m; rs.s = s; rs.idx = am;
-    return rs;
-}
-
+// One 256-thread block per sequence.  16 lanes merge the chunk partials of
+// each row; lanes k-1 (k = 1..7) evaluate decision k in parallel (ratio in
+// fp64 from the merged statistics, Philox uniform); thread 0 takes the
+// longest accepted prefix.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void decide_kernel(Params p) {
-    const int lane = threadIdx.x & 63;
-    const int b = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-    if (b >= p.B) return;
+    const int b = blockIdx.x, tid = threadIdx.x;
     const float Tb = p.temp[b];
     const bool greedy = is_greedy(Tb);
     const double scale_d = greedy ? 1.0 : 1.4426950408889634 / (double)Tb;
+    const int nrows = greedy ? 8 : kRows;
+
+    __shared__ float s_m[16];
+    __shared__ double s_s[16];
+    __shared__ int s_i[16];
+    __shared__ double s_rho[8];
+    __shared__ float s_u[8];
+    __shared__ int s_acc[8];
+
+    {
+        const int r = tid >> 4, c0 = tid & 15;
+        float m = -INFINITY;
+        int am = 0x7FFFFFFF;
+        const StatPart* sp = p.stats + ((int64_t)b * kRows + min(r, kRows - 1)) * p.nch1;
+        if (r < nrows)
+            for (int c = c0; c < p.nch1; c += 16) {
+                if (greedy) combine_arg(m, am, sp[c].m, sp[c].idx);
+                else m = fmaxf(m, sp[c].m);
+            }
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {
+            const float m2 = __shfl_xor(m, o);
+            const int a2 = __shfl_xor(am, o);
+            if (greedy) combine_arg(m, am, m2, a2);
+            else m = fmaxf(m, m2);
+        }
+        double sum = 0.0;
+        if (!greedy && r < nrows)
+            for (int c = c0; c < p.nch1; c += 16) {
+                const float mc = sp[c].m;
+                if (mc != -INFINITY) sum += (double)sp[c].s * exp2((double)(mc - m) * scale_d);
+            }
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+        if (c0 == 0) { s_m[r] = m; s_s[r] = sum; s_i[r] = am; }
+    }
+    __syncthreads();
+
     const int32_t* d = p.dtok + (int64_t)b * 7;
-    int32_t* out = p.out_tokens + (int64_t)b * 8;
-
-    if (greedy) {
-        int amax[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) amax[r] = merge_row(p, b, r, 1.0, true, lane).idx;
-        if (lane == 0) {
-            int n = 0;
-            while (n < 7 && d[n] == amax[n]) { out[n] = d[n]; ++n; }
-            out[n] = amax[n];
-            for (int j = n + 1; j < 8; ++j) out[j] = -1;
-            p.out_len[b] = n + 1;
-            Desc ds = {};
-            ds.mode = MODE_DONE; ds.nacc = n;
-            p.desc[b] = ds;
-        }
-        return;
-    }
-
-    RowStat st[8], sq[7];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) st[r] = merge_row(p, b, r, scale_d, false, lane);
-#pragma unroll
-    for (int r = 0; r < 7; ++r) sq[r] = merge_row(p, b, 8 + r, scale_d, false, lane);
-    if (lane != 0) return;
-
-    const T* tgt = reinterpret_cast<const T*>(p.target) + b * p.tbs;
-    const T* drf = reinterpret_cast<const T*>(p.draft) + b * p.dbs;
-    int n = 0;
-    int mode = MODE_BONUS;
-    for (int k = 1; k <= 7; ++k) {
+    if (tid < 7) {
+        const int k = tid + 1;
         const int x = d[k - 1];
-        double rho = 0.0;
-        if (x >= 0 && (int64_t)x < p.V) {
-            float zt = Elem<T>::load(tgt + (k - 1) * p.trs, x);
-            float zd = Elem<T>::load(drf + (k - 1) * p.drs, x);
-            // ln2-free ratio in the log2 domain: p(x)/q(x) = 2^(dt - dq) * Sq / St
-            double e = ((double)(zt - st[k - 1].m) - (double)(zd - sq[k - 1].m)) * scale_d;
-            rho = exp2(e) * (sq[k - 1].s / st[k - 1].s);
-        }
-        U64x4 ctr = {0ull, 8ull * (uint64_t)b + (uint64_t)k, 0ull, p.offset};
-        const float u = word_to_uniform(philox4x64_10(ctr, p.seed, 0ull).x0);
-        if (fabs((double)u - rho) < 1e-6) atomicAdd(p.near_ties, 1ull);
-        if ((double)u < rho) {
-            out[n] = x;
-            ++n;
+        if (greedy) {
+            s_acc[tid] = x == s_i[k - 1];
         } else {
-            mode = MODE_RESIDUAL;
-            break;
+            double rho = 0.0;
+            if (x >= 0 && (int64_t)x < p.V) {
+                const T* tgt = reinterpret_cast<const T*>(p.target) + b * p.tbs + (k - 1) * p.trs;
+                const T* drf = reinterpret_cast<const T*>(p.draft) + b * p.dbs + (k - 1) * p.drs;
+                const float zt = Elem<T>::load(tgt, x), zd = Elem<T>::load(drf, x);
+                // p(x)/q(x) = 2^((zt - Mt) - (zd - Mq)) * scale * Sq / St
+                const double e = ((double)(zt - s_m[k - 1]) - (double)(zd - s_m[8 + k - 1])) * scale_d;
+                rho = exp2(e) * (s_s[8 + k - 1] / s_s[k - 1]);
+            }
+            U64x4 ctr = {0ull, 8ull * (uint64_t)b + (uint64_t)k, 0ull, p.offset};
+            const float u = word_to_uniform(philox4x64_10(ctr, p.seed, 0ull).x0);
+            s_rho[tid] = rho;
+            s_u[tid] = u;
+            s_acc[tid] = (double)u < rho;
         }
     }
+    __syncthreads();
+    if (tid != 0) return;
+
+    int32_t* out = p.out_tokens + (int64_t)b * 8;
+    int n = 0;
+    while (n < 7 && s_acc[n]) { out[n] = d[n]; ++n; }
     for (int j = n + 1; j < 8; ++j) out[j] = -1;
     p.out_len[b] = n + 1;
-    Desc ds;
-    ds.mode = mode;
+    Desc ds = {};
     ds.nacc = n;
-    ds.pad = 0;
-    if (mode == MODE_RESIDUAL) {
+    if (greedy) {
+        out[n] = s_i[n];  // correction (row n) or bonus (row 7): the target argmax
+        ds.mode = MODE_DONE;
+        p.desc[b] = ds;
+        return;
+    }
+    // Near-ties among the decisions actually taken (k = 1 .. min(n + 1, 7)).
+    unsigned long long nt = 0;
+    for (int k = 1; k <= min(n + 1, 7); ++k)
+        if (fabs((double)s_u[k - 1] - s_rho[k - 1]) < 1e-6) ++nt;
+    if (nt) atomicAdd(p.near_ties, nt);
+    if (n < 7) {
+        ds.mode = MODE_RESIDUAL;
         ds.k = n + 1;
-        ds.mt = st[n].m; ds.inv_st = (float)(1.0 / st[n].s);
-        ds.mq = sq[n].m; ds.inv_sq = (float)(1.0 / sq[n].s);
+        ds.mt = s_m[n]; ds.inv_st = (float)(1.0 / s_s[n]);
+        ds.mq = s_m[8 + n]; ds.inv_sq = (float)(1.0 / s_s[8 + n]);
     } else {
+        ds.mode = MODE_BONUS;
         ds.k = 8;
-        ds.mt = st[7].m; ds.inv_st = (float)(1.0 / st[7].s);
-        ds.mq = 0.f; ds.inv_sq = 0.f;
+        ds.mt = s_m[7]; ds.inv_st = (float)(1.0 / s_s[7]);
     }
     p.desc[b] = ds;
 }
@@ -294,6 +288,16 @@ __device__ __forceinline__ float gumbel_from_word(uint64_t w) {
     return -logf(-logf(u));
 }
 
+// Gumbel noise of the 23-bit uniforms lies in [kGmin, kGmax] (u in
+// [2^-24, 1 - 2^-24]); the bounds are widened a little for fp32 rounding.
+constexpr float kGmax = 16.75f;   // -ln(-ln(1 - 2^-24)) = 16.636
+constexpr float kGmin = -2.85f;   // -ln(-ln(2^-24))     = -2.812
+
+// Gumbel-max over one chunk of the row a sampled sequence still needs.  Pass 1
+// (no random numbers) finds the chunk's largest log-weight L; the chunk's
+// winner then has key >= L + kGmin, so an entry whose log-weight plus kGmax
+// falls below that can never win and its Philox block is skipped.  The
+// result is exactly the Gumbel-max argmax; only the work depends on the data.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void sample_kernel(Params p) {
     const int b = blockIdx.x / p.nch2;
@@ -307,38 +311,77 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(Params p) {
     const T* dr = reinterpret_cast<const T*>(p.draft) + b * p.dbs + (k - 1) * p.drs;
     const bool resid = ds.mode == MODE_RESIDUAL;
     constexpr int N = Vec<T>::N;
+    constexpr int IT = kSampleChunk / (kThreads * N);  // vectors per thread
     const int64_t c0 = (int64_t)chunk * kSampleChunk;
-    const int64_t c1 = min(p.V, c0 + kSampleChunk);
     const uint64_t ctr1 = 8ull * (uint64_t)b + (uint64_t)k;
+    const int tid = threadIdx.x;
 
-    float best = -INFINITY, bestp = -INFINITY;
-    int bi = 0x7FFFFFFF, bip = 0x7FFFFFFF;
-    for (int64_t i0 = c0 + (int64_t)threadIdx.x * N; i0 < c1; i0 += (int64_t)kThreads * N) {
+    // Pass 1: log-weights.  w = ln r (residual; -inf where r <= 0), the fallback
+    // wp = ln p up to a constant, or z / T for the bonus draw.
+    float w[IT][N], wp[IT][N];
+    float lmax = -INFINITY, lpmax = -INFINITY;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int64_t i0 = c0 + ((int64_t)it * kThreads + tid) * N;
+        if (i0 >= p.V) {
+#pragma unroll
+            for (int e = 0; e < N; ++e) { w[it][e] = -INFINITY; wp[it][e] = -INFINITY; }
+            continue;
+        }
         float zt[N], zq[N];
         Vec<T>::load(tr + i0, zt);
         if (resid) Vec<T>::load(dr + i0, zq);
-        float g[N];
-#pragma unroll
-        for (int q4 = 0; q4 < N / 4; ++q4) {
-            U64x4 c = {(uint64_t)(i0 / 4 + q4), ctr1, 1ull, p.offset};
-            U64x4 w = philox4x64_10(c, p.seed, 0ull);
-            g[4 * q4 + 0] = gumbel_from_word(w.x0);
-            g[4 * q4 + 1] = gumbel_from_word(w.x1);
-            g[4 * q4 + 2] = gumbel_from_word(w.x2);
-            g[4 * q4 + 3] = gumbel_from_word(w.x3);
-        }
 #pragma unroll
         for (int e = 0; e < N; ++e) {
-            const int idx = (int)(i0 + e);
             if (resid) {
                 const float xt = scaled(zt[e] - ds.mt, sc);
                 const float pv = __builtin_amdgcn_exp2f(xt) * ds.inv_st;
                 const float qv = __builtin_amdgcn_exp2f(scaled(zq[e] - ds.mq, sc)) * ds.inv_sq;
                 const float rr = pv - qv;
-                if (rr > 0.f) combine_arg(best, bi, logf(rr) + g[e], idx);
-                combine_arg(bestp, bip, xt * kLn2 + g[e], idx);
+                w[it][e] = rr > 0.f ? logf(rr) : -INFINITY;
+                wp[it][e] = xt * kLn2;
             } else {
-                combine_arg(best, bi, zt[e] / Tb + g[e], idx);
+                w[it][e] = zt[e] / Tb;
+                wp[it][e] = -INFINITY;
+            }
+            lmax = fmaxf(lmax, w[it][e]);
+            lpmax = fmaxf(lpmax, wp[it][e]);
+        }
+    }
+    __shared__ float red[2][kThreads / 64];
+    lmax = wave_max(lmax);
+    lpmax = wave_max(lpmax);
+    if ((tid & 63) == 0) { red[0][tid >> 6] = lmax; red[1][tid >> 6] = lpmax; }
+    __syncthreads();
+    lmax = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    lpmax = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    // A chunk with a positive residual never needs the fallback keys (the
+    // row then has one); a chunk without one only needs them.
+    const bool use_resid = lmax > -INFINITY;
+    const float thr = (use_resid ? lmax : lpmax) + kGmin - kGmax;
+
+    float best = -INFINITY, bestp = -INFINITY;
+    int bi = 0x7FFFFFFF, bip = 0x7FFFFFFF;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int64_t i0 = c0 + ((int64_t)it * kThreads + tid) * N;
+#pragma unroll
+        for (int q4 = 0; q4 < N / 4; ++q4) {
+            bool need = false;
+#pragma unroll
+            for (int e = 4 * q4; e < 4 * q4 + 4; ++e) need |= (use_resid ? w[it][e] : wp[it][e]) >= thr;
+            if (!need) continue;
+            U64x4 c = {(uint64_t)(i0 / 4 + q4), ctr1, 1ull, p.offset};
+            const U64x4 r = philox4x64_10(c, p.seed, 0ull);
+            const uint64_t words[4] = {r.x0, r.x1, r.x2, r.x3};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ee = 4 * q4 + e;
+                const float wv = use_resid ? w[it][ee] : wp[it][ee];
+                if (wv == -INFINITY) continue;
+                const float key = wv + gumbel_from_word(words[e]);
+                if (use_resid) combine_arg(best, bi, key, (int)(i0 + ee));
+                else combine_arg(bestp, bip, key, (int)(i0 + ee));
             }
         }
     }
@@ -348,10 +391,10 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(Params p) {
         combine_arg(bestp, bip, __shfl_xor(bestp, o), __shfl_xor(bip, o));
     }
     __shared__ SamplePart sw[kThreads / 64];
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) { sw[w].key = best; sw[w].idx = bi; sw[w].keyp = bestp; sw[w].idxp = bip; }
+    const int wv = tid >> 6;
+    if ((tid & 63) == 0) { sw[wv].key = best; sw[wv].idx = bi; sw[wv].keyp = bestp; sw[wv].idxp = bip; }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
         for (int i = 1; i < kThreads / 64; ++i) {
             combine_arg(best, bi, sw[i].key, sw[i].idx);
             combine_arg(bestp, bip, sw[i].keyp, sw[i].idxp);
@@ -419,11 +462,11 @@ hipError_t launch_verify(const dflash_verify_args& a, void* ws, hipStream_t s) {
     const dim3 g1(p.nch1 * a.B * kRows), g2(p.nch2 * a.B), gw((a.B + 3) / 4);
     if (a.dtype == DFLASH_BF16) {
         stats_kernel<uint16_t><<<g1, kThreads, 0, s>>>(p);
-        decide_kernel<uint16_t><<<gw, kThreads, 0, s>>>(p);
+        decide_kernel<uint16_t><<<a.B, kThreads, 0, s>>>(p);
         sample_kernel<uint16_t><<<g2, kThreads, 0, s>>>(p);
     } else {
         stats_kernel<float><<<g1, kThreads, 0, s>>>(p);
-        decide_kernel<float><<<gw, kThreads, 0, s>>>(p);
+        decide_kernel<float><<<a.B, kThreads, 0, s>>>(p);
         sample_kernel<float><<<g2, kThreads, 0, s>>>(p);
     }
     finalize_kernel<<<gw, kThreads, 0, s>>>(p);

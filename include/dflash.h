@@ -153,7 +153,7 @@ typedef struct dflash_attn_args {
     int32_t page_size;        /* must be 16 */
     int32_t block_len;        /* must be 8 */
     int32_t window;           /* 0 = full context; > 0 = latest `window` tokens */
-    int32_t split_tokens;     /* 0 = automatic; else tokens per split-K chunk, multiple of 128 */
+    int32_t split_tokens;     /* 0 = automatic; else tokens per split-K chunk, multiple of 128, <= 32768 */
     void* out;                /* device [B][32][8][128] (dtype) */
     float* lse_out;           /* optional device [B][32][8] natural-log LSE; NULL = not written */
 } dflash_attn_args;

@@ -37,7 +37,23 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (5 times), the known-size "
+                         "reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     return ap.parse_args()
+
+
+def copy_probe():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "repeats": 5}))
 
 
 def log(msg):
@@ -216,6 +232,9 @@ def cpu_baseline(wl):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "requested_gpus": args.gpus}))
@@ -283,7 +302,9 @@ def main():
                                "sequence (shuffled 16-token pages), 5 draft layers, ctx-fuse of the new rows, "
                                "block attention per layer, spec-verify over V=262144 (32 greedy, 32 at T=0.7)",
                    "B": B, "S": S_CTX, "new_rows": int(wl.M), "layers": LAYERS, "V": V, "parallelism": "none"},
-        "roofline": {"kernel": "block_attn (attn_bf16_kernel + attn_merge_kernel)", "bound": "hbm",
+        "roofline": {"kernel": "block_attn (attn_bf16_kernel" + (" + attn_merge_kernel)" if wl.attn[0].ws_bytes else
+                                                                  ", one split per sequence: no merge launch)"),
+                     "bound": "hbm",
                      "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(a_gbs / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic / (a_ms * 1e-3) / 1e9, 1),

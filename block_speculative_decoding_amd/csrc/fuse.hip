@@ -184,6 +184,192 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
             }
 }
 
+// ---- bf16 GEMM for large M: 256x256 tile, eight waves (two per SIMD, so one
+// wave's MFMAs cover the other's LDS waits and barrier) of 64x128 each (2x4
+// blocks of the 32x32x16 instruction, 128 fp32 accumulators per lane), BK =
+// 32, the same four-stage direct-to-LDS ring (128 KiB).  No split-K.  With
+// KV = true the epilogue is the K/V injection: each wave's 128 columns are
+// exactly one head, so k_norm (row sums over the head), RoPE (pairs d, d+64
+// sit in the same lane) and the paged-cache store happen in registers and
+// the fp32 product never reaches memory.
+constexpr int BMB = 256, BNB = 256;
+constexpr int kBigThreads = 512;
+constexpr int kBigStageChunks = 2 * BMB * 4;  // A then B, 16-byte chunks (32 KiB)
+
+struct KvEpilogue {
+    const float2* cs;      // [M][64] (cos, sin) of pos[row] * inv_freq[i]
+    const void* gk;        // [L][128]
+    float eps;
+    const int64_t* slot;
+    int64_t num_pages;
+    void* kc[5];
+    void* vc[5];
+};
+
+template <bool KV>
+__global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParams p, KvEpilogue ep) {
+    const int tiles_m = (p.M + BMB - 1) / BMB, tiles_n = p.N / BNB;
+    const TileId t = tile_id(p, tiles_m, tiles_n);
+    if (!t.valid) return;
+    const int nk = p.K / BKD;
+
+    __shared__ __attribute__((aligned(16))) uint4 lds[kStages * kBigStageChunks];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m0 = t.tm * BMB, n0 = t.tn * BNB;
+    const uint16_t* bmat = static_cast<const uint16_t*>(p.b);
+
+    // 4 DMA chunks per thread per stage: j = 0,1 -> A rows, j = 2,3 -> B rows,
+    // position P = (j & 1) * 512 + tid inside the half.
+    int src_r[2], src_c[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int P = j * kBigThreads + tid;
+        src_r[j] = P >> 2;
+        src_c[j] = (P & 3) ^ swz(P >> 2);
+    }
+    auto issue = [&](int kt, int slot) {
+        const int kg = kt * BKD;
+        const int seg = kg / p.seg_w;
+        const int kc = kg - seg * p.seg_w;
+        const uint16_t* a = static_cast<const uint16_t*>(p.aseg[seg]);
+        uint4* sbase = lds + slot * kBigStageChunks;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int jj = j & 1;
+            const uint16_t* g = j < 2 ? a + (int64_t)min(m0 + src_r[jj], p.M - 1) * p.a_stride + kc + 8 * src_c[jj]
+                                      : bmat + (int64_t)(n0 + src_r[jj]) * p.K + kg + 8 * src_c[jj];
+            dma16(g, sbase + (j >> 1) * (BMB * 4) + jj * kBigThreads + wave * 64);
+        }
+    };
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
+
+    const int wr = (wave >> 1) * 64, wc = (wave & 1) * 128;
+    const int lr = lane & 31, lh = lane >> 5;
+
+#pragma unroll
+    for (int s0 = 0; s0 < kStages - 1; ++s0) issue(min(s0, nk - 1), s0);
+
+    for (int i = 0; i < nk; ++i) {
+        wait_vm<4 * (kStages - 2)>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(min(i + kStages - 1, nk - 1), (i + kStages - 1) % kStages);
+        const uint4* sa = lds + (i % kStages) * kBigStageChunks;
+        const uint4* sb = sa + BMB * 4;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int ch = 2 * ks + lh;
+            bf16x8 af[2], bfr[4];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int ra = wr + 32 * q + lr;
+                af[q] = __builtin_bit_cast(bf16x8, sa[4 * ra + (ch ^ swz(ra))]);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int rb = wc + 32 * q + lr;
+                bfr[q] = __builtin_bit_cast(bf16x8, sb[4 * rb + (ch ^ swz(rb))]);
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[q][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q], bfr[j], acc[q][j], 0, 0, 0);
+        }
+    }
+    wait_vm<0>();
+
+    // Lane holds column lr of each 32x32 block, rows 8*jj + 4*lh + r.
+    if (!KV) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int gm = m0 + wr + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    const int gn = n0 + wc + 32 * j + lr;
+                    if (gm < p.M) p.part[(int64_t)gm * p.N + gn] = acc[i][j][r];
+                }
+        return;
+    }
+
+    const int hidx = (n0 + wc) >> 7;  // [layer][K/V][head] of this wave's 128 columns
+    const int l = hidx >> 4, isv = (hidx >> 3) & 1, head = hidx & 7;
+    if (!isv) {
+        // k_norm: row sums of squares over the head = the wave's 4 column blocks x 32 lanes.
+        const uint16_t* gk = static_cast<const uint16_t*>(ep.gk) + l * 128;
+        float g[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) g[j] = bf16_bits_to_f32(gk[32 * j + lr]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float ss = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ss += acc[i][j][r] * acc[i][j][r];
+#pragma unroll
+                for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o);
+                const float rinv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + ep.eps);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j][r] *= rinv * g[j];
+            }
+    }
+    uint16_t* cache = static_cast<uint16_t*>(isv ? ep.vc[l] : ep.kc[l]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int gm = m0 + wr + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+            if (gm >= p.M) continue;
+            const int64_t slot = ep.slot[gm];
+            if (slot < 0 || slot >= ep.num_pages * 16) continue;
+            uint16_t* blk = cache + ((slot >> 4) * 8 + head) * 2048;
+            const int tt = (int)(slot & 15);
+            if (!isv) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int d0 = 32 * j + lr, d1 = d0 + 64;
+                    const float2 cs = ep.cs[(int64_t)gm * 64 + d0];
+                    const float a = acc[i][j][r], b = acc[i][j + 2][r];
+                    blk[256 * ((d0 & 63) >> 3) + 8 * (tt + 16 * (d0 >> 6)) + (d0 & 7)] =
+                        (uint16_t)f32_to_bf16_bits(a * cs.x - b * cs.y);
+                    blk[256 * ((d1 & 63) >> 3) + 8 * (tt + 16 * (d1 >> 6)) + (d1 & 7)] =
+                        (uint16_t)f32_to_bf16_bits(b * cs.x + a * cs.y);
+                }
+            } else {
+                const int te = ((tt >> 3) << 2) | (tt & 3), th = (tt >> 2) & 1;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int d = 32 * j + lr;
+                    blk[512 * (d >> 5) + 256 * th + 8 * (d & 31) + te] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
+                }
+            }
+        }
+}
+
+// (cos, sin) of pos[m] * inv_freq[i] for every fused row: fp64 angle and
+// range reduction, fp32 sincos.
+struct RopeTabParams { const int32_t* pos; float2* cs; int M; double inv_freq[64]; };
+__global__ __launch_bounds__(256) void rope_table_kernel(RopeTabParams p) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= p.M * 64) return;
+    const int m = idx >> 6, i = idx & 63;
+    double ang = (double)p.pos[m] * p.inv_freq[i];
+    const double two_pi = 6.283185307179586;
+    ang -= rint(ang * (1.0 / two_pi)) * two_pi;
+    float sn, cs;
+    sincosf((float)ang, &sn, &cs);
+    p.cs[idx] = make_float2(cs, sn);
+}
+
 // Plain fp32 GEMM for the fp32 path: 64x64 tile, 4x4 outputs per thread.
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
     const int tm = blockIdx.x, tn = blockIdx.y;
@@ -340,18 +526,25 @@ hipError_t launch_gemm(const GemmParams& g, int dtype, hipStream_t s) {
 
 }  // namespace
 
+// Large fused row counts use the 256x256 kernel (no split-K, fused K/V
+// epilogue); small ones the 128x128 split-K kernel.
+constexpr int kBigM = 8192;
+
 FusePlan fuse_plan(const dflash_fuse_args& a) {
     FusePlan pl;
     const int M = (int)a.M;
     const int N2 = a.num_layers * 2048;
     const bool bf = a.dtype == DFLASH_BF16;
-    pl.ks1 = bf ? pick_ks(M, DFLASH_D, DFLASH_NCAPTURE * DFLASH_D) : 1;
-    pl.ks2 = bf ? pick_ks(M, N2, DFLASH_D) : 1;
+    pl.big = bf && M >= kBigM;
+    pl.ks1 = bf && !pl.big ? pick_ks(M, DFLASH_D, DFLASH_NCAPTURE * DFLASH_D) : 1;
+    pl.ks2 = bf && !pl.big ? pick_ks(M, N2, DFLASH_D) : 1;
     const size_t es = bf ? 2 : 4;
     pl.off_part1 = 0;
     pl.off_ht = align256((size_t)pl.ks1 * M * DFLASH_D * 4);
     pl.off_part2 = pl.off_ht + align256((size_t)M * DFLASH_D * es);
-    pl.ws_bytes = pl.off_part2 + align256((size_t)pl.ks2 * M * N2 * 4);
+    // The big path needs no second partial buffer, only the RoPE table.
+    pl.ws_bytes = pl.off_part2 + (pl.big ? align256((size_t)M * 64 * sizeof(float2))
+                                         : align256((size_t)pl.ks2 * M * N2 * 4));
     return pl;
 }
 
@@ -363,17 +556,26 @@ hipError_t launch_fuse(const dflash_fuse_args& a, const FusePlan& pl, void* ws, 
     void* ht = w + pl.off_ht;
     float* part2 = reinterpret_cast<float*>(w + pl.off_part2);
     const int N2 = a.num_layers * 2048;
+    const bool bf = a.dtype == DFLASH_BF16;
+    double inv_freq[64];
+    for (int i = 0; i < 64; ++i) inv_freq[i] = std::pow((double)a.rope_theta, -(double)i / 64.0);
 
     GemmParams g1 = {};
     for (int i = 0; i < 5; ++i) g1.aseg[i] = a.hs[i];
     g1.a_stride = a.hs_stride; g1.seg_w = DFLASH_D;
     g1.b = a.wc; g1.M = M; g1.N = DFLASH_D; g1.K = DFLASH_NCAPTURE * DFLASH_D;
-    g1.ks = pl.ks1; g1.kt_per_split = (g1.K / (a.dtype == DFLASH_BF16 ? BKD : BK) + pl.ks1 - 1) / pl.ks1;
+    g1.ks = pl.ks1; g1.kt_per_split = (g1.K / (bf ? BKD : BK) + pl.ks1 - 1) / pl.ks1;
     g1.part = part1;
-    hipError_t e = launch_gemm(g1, a.dtype, s);
-    if (e != hipSuccess) return e;
+    KvEpilogue ep = {};
+    if (pl.big) {
+        const int tiles = ((M + BMB - 1) / BMB) * (DFLASH_D / BNB);
+        gemm_bf16_big_kernel<false><<<(tiles + kXcds - 1) / kXcds * kXcds, kBigThreads, 0, s>>>(g1, ep);
+    } else {
+        hipError_t e = launch_gemm(g1, a.dtype, s);
+        if (e != hipSuccess) return e;
+    }
 
-    if (a.dtype == DFLASH_BF16)
+    if (bf)
         fuse_norm_kernel<uint16_t><<<M, kThreads, 0, s>>>(part1, pl.ks1, M, static_cast<const uint16_t*>(a.gc),
                                                           a.eps, static_cast<uint16_t*>(ht),
                                                           static_cast<uint16_t*>(a.ht_out));
@@ -384,19 +586,31 @@ hipError_t launch_fuse(const dflash_fuse_args& a, const FusePlan& pl, void* ws, 
     GemmParams g2 = {};
     g2.aseg[0] = ht; g2.a_stride = DFLASH_D; g2.seg_w = DFLASH_D;
     g2.b = a.wkv; g2.M = M; g2.N = N2; g2.K = DFLASH_D;
-    g2.ks = pl.ks2; g2.kt_per_split = (g2.K / (a.dtype == DFLASH_BF16 ? BKD : BK) + pl.ks2 - 1) / pl.ks2;
+    g2.ks = pl.ks2; g2.kt_per_split = (g2.K / (bf ? BKD : BK) + pl.ks2 - 1) / pl.ks2;
     g2.part = part2;
-    e = launch_gemm(g2, a.dtype, s);
+    if (pl.big) {
+        RopeTabParams rp;
+        rp.pos = a.pos; rp.cs = reinterpret_cast<float2*>(part2); rp.M = M;
+        for (int i = 0; i < 64; ++i) rp.inv_freq[i] = inv_freq[i];
+        rope_table_kernel<<<(M * 64 + 255) / 256, 256, 0, s>>>(rp);
+        ep.cs = reinterpret_cast<const float2*>(part2);
+        ep.gk = a.gk; ep.eps = a.eps; ep.slot = a.slot; ep.num_pages = a.num_pages;
+        for (int i = 0; i < 5; ++i) { ep.kc[i] = a.k_cache[i]; ep.vc[i] = a.v_cache[i]; }
+        const int tiles = ((M + BMB - 1) / BMB) * (N2 / BNB);
+        gemm_bf16_big_kernel<true><<<(tiles + kXcds - 1) / kXcds * kXcds, kBigThreads, 0, s>>>(g2, ep);
+        return hipGetLastError();
+    }
+    hipError_t e = launch_gemm(g2, a.dtype, s);
     if (e != hipSuccess) return e;
 
     KvParams kp;
     kp.part = part2; kp.ks = pl.ks2; kp.M = M; kp.N = N2;
     kp.gk = a.gk; kp.eps = a.eps;
-    for (int i = 0; i < 64; ++i) kp.inv_freq[i] = std::pow((double)a.rope_theta, -(double)i / 64.0);
+    for (int i = 0; i < 64; ++i) kp.inv_freq[i] = inv_freq[i];
     kp.pos = a.pos; kp.slot = a.slot; kp.num_pages = a.num_pages;
     for (int i = 0; i < 5; ++i) { kp.kc[i] = a.k_cache[i]; kp.vc[i] = a.v_cache[i]; }
     const dim3 gkv(M, a.num_layers * 4);
-    if (a.dtype == DFLASH_BF16) fuse_kv_kernel<uint16_t><<<gkv, kThreads, 0, s>>>(kp);
+    if (bf) fuse_kv_kernel<uint16_t><<<gkv, kThreads, 0, s>>>(kp);
     else fuse_kv_kernel<float><<<gkv, kThreads, 0, s>>>(kp);
     return hipGetLastError();
 }

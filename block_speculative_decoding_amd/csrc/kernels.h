@@ -25,6 +25,7 @@ hipError_t launch_attn(const dflash_attn_args& a, const AttnPlan& plan, void* ws
 // ---- ctx_fuse ----
 struct FusePlan {
     int ks1, ks2;          // split-K factors of the two GEMMs
+    bool big;              // 256x256 kernels with the fused K/V epilogue
     size_t off_part1, off_ht, off_part2, ws_bytes;
 };
 FusePlan fuse_plan(const dflash_fuse_args& a);

@@ -112,3 +112,18 @@ def test_fuse_prefill_full_size_sampled_rows():
     ht_err, kv_err, _, _ = _run(M, L, BF16, 4, npages, slots, pos, rows=rows)
     note(f"fuse prefill M=32768 L=5 sampled: H_t err {ht_err:.3e}, K/V err {kv_err:.3e}")
     assert ht_err <= TOL[BF16] and kv_err <= TOL[BF16]
+
+
+def test_fuse_large_ragged_rows_scattered_slots():
+    """M = 8292 (large-M kernel path, not a multiple of its 256-row tile), two
+    layers, shuffled slots and positions; sampled rows checked."""
+    M, L = 8292, 2
+    npages = (M + 15) // 16 + 7
+    rng = np.random.default_rng(9)
+    slots = rng.permutation(npages * 16)[:M].astype(np.int64)
+    pos = rng.integers(0, 131072, M).astype(np.int32)
+    rows = np.sort(rng.choice(M, 40, replace=False))
+    rows[-1] = M - 1
+    ht_err, kv_err, _, _ = _run(M, L, BF16, 6, npages, slots, pos, rows=rows)
+    note(f"fuse large ragged M={M} L={L}: H_t err {ht_err:.3e}, K/V err {kv_err:.3e}")
+    assert ht_err <= TOL[BF16] and kv_err <= TOL[BF16]

@@ -51,13 +51,28 @@ template <> struct Elem<uint16_t> {  // bf16 bits
 // ---- Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11) ----
 struct U64x4 { uint64_t x0, x1, x2, x3; };
 
+// Full 64x64 -> 128-bit product from four 32x32+64 multiply-adds
+// (v_mad_u64_u32): x*M = (p3 + hi32(p2))*2^64 + lo32(p2)*2^32 + lo32(p0), the
+// partial sums chained so that none overflows 64 bits.
+__device__ __forceinline__ void mulhilo64(uint64_t m, uint64_t x, uint64_t& hi, uint64_t& lo) {
+    const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32);
+    const uint32_t xl = (uint32_t)x, xh = (uint32_t)(x >> 32);
+    const uint64_t p0 = (uint64_t)xl * ml;
+    const uint64_t p1 = (uint64_t)xh * ml + (p0 >> 32);
+    const uint64_t p2 = (uint64_t)xl * mh + (uint32_t)p1;
+    const uint64_t p3 = (uint64_t)xh * mh + (p1 >> 32);
+    hi = p3 + (p2 >> 32);
+    lo = (p2 << 32) | (uint32_t)p0;
+}
+
 __device__ __forceinline__ U64x4 philox4x64_10(U64x4 c, uint64_t k0, uint64_t k1) {
     const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
     const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
-        uint64_t hi0 = __umul64hi(M0, c.x0), lo0 = M0 * c.x0;
-        uint64_t hi1 = __umul64hi(M1, c.x2), lo1 = M1 * c.x2;
+        uint64_t hi0, lo0, hi1, lo1;
+        mulhilo64(M0, c.x0, hi0, lo0);
+        mulhilo64(M1, c.x2, hi1, lo1);
         U64x4 n;
         n.x0 = hi1 ^ c.x1 ^ k0;
         n.x1 = lo1;

@@ -99,6 +99,64 @@ __device__ __forceinline__ void combine_arg(float& v, int& i, float v2, int i2) 
 }
 
 // ---------------------------------------------------------------- stats
+// One chunk of one row.  Greedy rows keep (max, lowest argmax); sampled rows
+// keep (max, sum of 2^((z - m) * scale)) and no argmax.  In the sampled
+// loop the exponent is fma(z, hi, c_hi) + c_lo with (c_hi, c_lo) = -M * hi
+// split exactly (M * hi has at most 48 significant bits), so the only
+// systematic error is hi's own rounding (2^-25 relative, times the exponent).
+template <typename T, bool GREEDY>
+__device__ __forceinline__ void stats_chunk(const T* src, int64_t c0, int64_t c1, Scale sc, float& m, float& s,
+                                            int& am) {
+    constexpr int N = Vec<T>::N;
+    constexpr int U = 4;  // 16-byte loads in flight per thread per step
+    const int tid = threadIdx.x;
+    for (int64_t base = c0; base < c1; base += (int64_t)kThreads * N * U) {
+        float f[U][N];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int64_t i = base + ((int64_t)j * kThreads + tid) * N;
+            if (i < c1) {
+                Vec<T>::load(src + i, f[j]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < N; ++e) f[j][e] = -INFINITY;
+            }
+        }
+        if (GREEDY) {
+            float lm = -INFINITY;
+            int li = 0x7FFFFFFF;
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                const int i = (int)(base + ((int64_t)j * kThreads + tid) * N);
+#pragma unroll
+                for (int e = 0; e < N; ++e)
+                    if (f[j][e] > lm) { lm = f[j][e]; li = i + e; }
+            }
+            combine_arg(m, am, lm, li);
+        } else {
+            float lm = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < U; ++j)
+#pragma unroll
+                for (int e = 0; e < N; ++e) lm = fmaxf(lm, f[j][e]);
+            const float M = fmaxf(m, lm);
+            if (M == -INFINITY) continue;
+            const double cm = -(double)M * (double)sc.hi;
+            const float c_hi = (float)cm, c_lo = (float)(cm - (double)c_hi);
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < U; ++j)
+#pragma unroll
+                for (int e = 0; e < N; ++e) acc += __builtin_amdgcn_exp2f(fmaf(f[j][e], sc.hi, c_hi) + c_lo);
+            s = s * __builtin_amdgcn_exp2f(scaled(m - M, sc)) + acc;
+            m = M;
+        }
+    }
+}
+
+// Rows a sequence needs: greedy, target rows 0..7 (argmax); sampled, target
+// rows 0..6 and draft rows 0..6 (the bonus draw at row 7 is a Gumbel-max over
+// unnormalised logits and needs no statistics).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void stats_kernel(Params p) {
     const int row = blockIdx.x / p.nch1;
@@ -106,57 +164,21 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Params p) {
     const int b = row / kRows, r = row % kRows;
     const float Tb = p.temp[b];
     const bool greedy = is_greedy(Tb);
-    if (greedy && r >= 8) return;  // greedy sequences never read draft rows
+    if (greedy ? r >= 8 : r == 7) return;
     const T* src = row_ptr<T>(p, b, r);
     const Scale sc = make_scale(greedy ? 1.f : Tb);
-    constexpr int N = Vec<T>::N;
-    constexpr int U = 4;  // 16-byte loads in flight per thread per step
     const int64_t c0 = (int64_t)chunk * kStatsChunk;
     const int64_t c1 = min(p.V, c0 + kStatsChunk);
     const int tid = threadIdx.x;
 
     float m = -INFINITY, s = 0.f;
     int am = 0x7FFFFFFF;
-    for (int64_t base = c0; base < c1; base += (int64_t)kThreads * N * U) {
-        float f[U][N];
-        bool ok[U];
-#pragma unroll
-        for (int j = 0; j < U; ++j) {
-            int64_t i = base + ((int64_t)j * kThreads + tid) * N;
-            ok[j] = i < c1;
-            if (ok[j]) Vec<T>::load(src + i, f[j]);
-        }
-        float lm = -INFINITY;
-        int li = 0x7FFFFFFF;
-#pragma unroll
-        for (int j = 0; j < U; ++j) {
-            if (!ok[j]) continue;
-            int64_t i = base + ((int64_t)j * kThreads + tid) * N;
-#pragma unroll
-            for (int e = 0; e < N; ++e)
-                if (f[j][e] > lm) { lm = f[j][e]; li = (int)(i + e); }
-        }
-        if (greedy) {
-            combine_arg(m, am, lm, li);
-        } else {
-            float M = fmaxf(m, lm);
-            if (M == -INFINITY) continue;
-            float acc = 0.f;
-#pragma unroll
-            for (int j = 0; j < U; ++j) {
-                if (!ok[j]) continue;
-#pragma unroll
-                for (int e = 0; e < N; ++e) acc += __builtin_amdgcn_exp2f(scaled(f[j][e] - M, sc));
-            }
-            s = s * __builtin_amdgcn_exp2f(scaled(m - M, sc)) + acc;
-            m = M;
-        }
-    }
-    // wave reduction
+    if (greedy) stats_chunk<T, true>(src, c0, c1, sc, m, s, am);
+    else stats_chunk<T, false>(src, c0, c1, sc, m, s, am);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-        float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
-        int a2 = __shfl_xor(am, o);
+        const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+        const int a2 = __shfl_xor(am, o);
         if (greedy) combine_arg(m, am, m2, a2);
         else combine_ms(m, s, m2, s2, sc);
     }
@@ -201,7 +223,8 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(Params p) {
         float m = -INFINITY;
         int am = 0x7FFFFFFF;
         const StatPart* sp = p.stats + ((int64_t)b * kRows + min(r, kRows - 1)) * p.nch1;
-        if (r < nrows)
+        const bool used = r < nrows && (greedy || r != 7);
+        if (used)
             for (int c = c0; c < p.nch1; c += 16) {
                 if (greedy) combine_arg(m, am, sp[c].m, sp[c].idx);
                 else m = fmaxf(m, sp[c].m);
@@ -214,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(Params p) {
             else m = fmaxf(m, m2);
         }
         double sum = 0.0;
-        if (!greedy && r < nrows)
+        if (!greedy && used)
             for (int c = c0; c < p.nch1; c += 16) {
                 const float mc = sp[c].m;
                 if (mc != -INFINITY) sum += (double)sp[c].s * exp2((double)(mc - m) * scale_d);
@@ -275,9 +298,8 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(Params p) {
         ds.mt = s_m[n]; ds.inv_st = (float)(1.0 / s_s[n]);
         ds.mq = s_m[8 + n]; ds.inv_sq = (float)(1.0 / s_s[8 + n]);
     } else {
-        ds.mode = MODE_BONUS;
+        ds.mode = MODE_BONUS;  // row 7 has no statistics: the draw needs none
         ds.k = 8;
-        ds.mt = s_m[7]; ds.inv_st = (float)(1.0 / s_s[7]);
     }
     p.desc[b] = ds;
 }
@@ -310,6 +332,7 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(Params p) {
     const T* tr = reinterpret_cast<const T*>(p.target) + b * p.tbs + (k - 1) * p.trs;
     const T* dr = reinterpret_cast<const T*>(p.draft) + b * p.dbs + (k - 1) * p.drs;
     const bool resid = ds.mode == MODE_RESIDUAL;
+    const float invT = 1.0f / Tb;
     constexpr int N = Vec<T>::N;
     constexpr int IT = kSampleChunk / (kThreads * N);  // vectors per thread
     const int64_t c0 = (int64_t)chunk * kSampleChunk;
@@ -341,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(Params p) {
                 w[it][e] = rr > 0.f ? logf(rr) : -INFINITY;
                 wp[it][e] = xt * kLn2;
             } else {
-                w[it][e] = zt[e] / Tb;
+                w[it][e] = zt[e] * invT;
                 wp[it][e] = -INFINITY;
             }
             lmax = fmaxf(lmax, w[it][e]);

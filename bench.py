@@ -152,7 +152,10 @@ def attn_bytes(lens):
 
 
 def verify_bytes(temp):
-    rows = np.where(temp > 0, 15, 8)
+    # One pass over the rows the decisions need: 8 target rows of a greedy
+    # sequence; target rows 0..6 and draft rows 0..6 of a sampled one (its
+    # bonus draw at row 7 needs no normaliser).
+    rows = np.where(temp > 0, 14, 8)
     return int(rows.sum() * V * 2)
 
 

@@ -144,8 +144,10 @@ int dflash_ctx_fuse(const dflash_fuse_args* a, void* ws, size_t ws_bytes, void* 
     if (a->M == 0) return ok();
     for (int i = 0; i < DFLASH_NCAPTURE; ++i)
         if (!a->hs[i] || !aligned16(a->hs[i])) return fail(DFLASH_EINVAL, "%s: hs[%d] null or not 16-byte aligned", fn, i);
-    if (a->hs_stride < DFLASH_D || a->hs_stride % 8 != 0)
-        return fail(DFLASH_EINVAL, "%s: hs_stride %lld must be >= 2560 and a multiple of 8", fn, (long long)a->hs_stride);
+    // Row offsets inside a 256-row tile are 32-bit byte offsets: stride <= 2^22.
+    if (a->hs_stride < DFLASH_D || a->hs_stride % 8 != 0 || a->hs_stride > (1 << 22))
+        return fail(DFLASH_EINVAL, "%s: hs_stride %lld must be in [2560, 2^22] and a multiple of 8", fn,
+                    (long long)a->hs_stride);
     REQUIRE_PTR(a->wc);
     REQUIRE_PTR(a->gc);
     REQUIRE_PTR(a->wkv);

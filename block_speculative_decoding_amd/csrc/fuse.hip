@@ -184,17 +184,55 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
             }
 }
 
-// ---- bf16 GEMM for large M: 256x256 tile, eight waves (two per SIMD, so one
-// wave's MFMAs cover the other's LDS waits and barrier) of 64x128 each (2x4
-// blocks of the 32x32x16 instruction, 128 fp32 accumulators per lane), BK =
-// 32, the same four-stage direct-to-LDS ring (128 KiB).  No split-K.  With
-// KV = true the epilogue is the K/V injection: each wave's 128 columns are
-// exactly one head, so k_norm (row sums over the head), RoPE (pairs d, d+64
-// sit in the same lane) and the paged-cache store happen in registers and
-// the fp32 product never reaches memory.
+// ---- bf16 GEMM for large M: 256x256 tile, four waves of 128x128 (4x4 blocks
+// of the 32x32x16 instruction, 256 fp32 accumulators per lane), 64 k per stage
+// in a two-stage LDS ring (2 x 64 KiB), no split-K.
+//  * Operands reach LDS through buffer loads that write LDS directly (16 B per
+//    lane, lane l at the wave's LDS base + 16 l).  The descriptor's range stops
+//    at row M, so rows of the last A tile past M read as zero.
+//  * A stage row is 128 B = 8 chunks of 16 B; chunk c of row r sits at
+//    c ^ ((r >> 1) & 7), which keeps the 16-byte operand reads of 16
+//    consecutive rows on distinct banks.
+//  * The operand reads of k-substep s+1 are in flight while substep s
+//    multiplies (inline-asm ds_read_b128 with explicit lgkmcnt waits: the
+//    compiler's own wait placement would drain them), and the next stage's 16
+//    loads are issued one by one between the 16 MFMAs of the last substep.
+// With KV = true the epilogue is the K/V injection: a wave's 128 output
+// columns are exactly one head, so k_norm (row sums over the head), RoPE (pairs
+// d, d+64 sit in the same lane) and the paged-cache store happen from the
+// accumulators, and the fp32 product never reaches memory.
 constexpr int BMB = 256, BNB = 256;
-constexpr int kBigThreads = 512;
-constexpr int kBigStageChunks = 2 * BMB * 4;  // A then B, 16-byte chunks (32 KiB)
+constexpr int kBigThreads = 256;
+constexpr int BKB = 64;                        // k per stage
+constexpr int kBigPitch = BKB * 2;             // bytes per LDS row
+constexpr int kBigStageBytes = 2 * BMB * kBigPitch;
+constexpr int kBigParts = 2 * BKB / 8;         // buffer loads per thread per stage (A then B)
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) uint32_t* lds,
+                                                           int size, int voffset, int soffset, int offset,
+                                                           int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+// Raw buffer descriptor: 48-bit base, stride 0, range in bytes.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    i32x4 r;
+    r[0] = (int)(uint32_t)a;
+    r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);
+    r[2] = (int)bytes;
+    r[3] = 0x00020000;
+    return r;
+}
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
+    bf16x8 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
 
 struct KvEpilogue {
     const float2* cs;      // [M][64] (cos, sin) of pos[row] * inv_freq[i]
@@ -211,84 +249,120 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
     const int tiles_m = (p.M + BMB - 1) / BMB, tiles_n = p.N / BNB;
     const TileId t = tile_id(p, tiles_m, tiles_n);
     if (!t.valid) return;
-    const int nk = p.K / BKD;
+    const int nk = p.K / BKB;
 
-    __shared__ __attribute__((aligned(16))) uint4 lds[kStages * kBigStageChunks];
+    __shared__ __attribute__((aligned(16))) uint4 lds[2 * kBigStageBytes / 16];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m0 = t.tm * BMB, n0 = t.tn * BNB;
-    const uint16_t* bmat = static_cast<const uint16_t*>(p.b);
+    const uint16_t* bmat = static_cast<const uint16_t*>(p.b) + (int64_t)n0 * p.K;
+    const void *aseg0 = p.aseg[0], *aseg1 = p.aseg[1], *aseg2 = p.aseg[2], *aseg3 = p.aseg[3], *aseg4 = p.aseg[4];
+    const uint32_t arows = (uint32_t)min(p.M - m0, BMB);
 
-    // 4 DMA chunks per thread per stage: j = 0,1 -> A rows, j = 2,3 -> B rows,
-    // position P = (j & 1) * 512 + tid inside the half.
-    int src_r[2], src_c[2];
+    // Load j of a thread covers unit P = j * 256 + tid of the A (or B) half:
+    // row P >> 3, chunk (P & 7) ^ swz8(row).
+    uint32_t voa[8], vob[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int P = j * kBigThreads + tid;
-        src_r[j] = P >> 2;
-        src_c[j] = (P & 3) ^ swz(P >> 2);
+    for (int j = 0; j < 8; ++j) {
+        const int P = j * kBigThreads + tid, r = P >> 3, c = (P & 7) ^ swz8(r);
+        voa[j] = (uint32_t)(r * (int)p.a_stride + 8 * c) * 2u;
+        vob[j] = (uint32_t)(r * p.K + 8 * c) * 2u;
     }
-    auto issue = [&](int kt, int slot) {
-        const int kg = kt * BKD;
-        const int seg = kg / p.seg_w;
-        const int kc = kg - seg * p.seg_w;
-        const uint16_t* a = static_cast<const uint16_t*>(p.aseg[seg]);
-        uint4* sbase = lds + slot * kBigStageChunks;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int jj = j & 1;
-            const uint16_t* g = j < 2 ? a + (int64_t)min(m0 + src_r[jj], p.M - 1) * p.a_stride + kc + 8 * src_c[jj]
-                                      : bmat + (int64_t)(n0 + src_r[jj]) * p.K + kg + 8 * src_c[jj];
-            dma16(g, sbase + (j >> 1) * (BMB * 4) + jj * kBigThreads + wave * 64);
+    auto load_part = [&](int kt, int slot, int part) {
+        const int kg = kt * BKB;
+        uint4* sb = lds + slot * (kBigStageBytes / 16) + wave * 64;
+        if (part < 8) {
+            // The K/V projection's A operand (H_t) is one segment.
+            const int seg = KV ? 0 : kg / p.seg_w;
+            const int kc = kg - seg * p.seg_w;
+            const void* av = seg == 0 ? aseg0 : seg == 1 ? aseg1 : seg == 2 ? aseg2 : seg == 3 ? aseg3 : aseg4;
+            const uint16_t* a = static_cast<const uint16_t*>(av) + (int64_t)m0 * p.a_stride + kc;
+            const i32x4 rs = buffer_rsrc(a, arows * (uint32_t)p.a_stride * 2u - (uint32_t)kc * 2u);
+            llvm_amdgcn_raw_buffer_load_lds(rs, (__attribute__((address_space(3))) uint32_t*)(sb + part * kBigThreads), 16,
+                                            (int)voa[part], 0, 0, 0);
+        } else {
+            const i32x4 rs = buffer_rsrc(bmat + kg, (uint32_t)BNB * (uint32_t)p.K * 2u - (uint32_t)kg * 2u);
+            llvm_amdgcn_raw_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) uint32_t*)(sb + BMB * 8 + (part - 8) * kBigThreads), 16,
+                (int)vob[part - 8], 0, 0, 0);
         }
     };
 
-    f32x16 acc[2][4];
+    f32x16 acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
 
-    const int wr = (wave >> 1) * 64, wc = (wave & 1) * 128;
+    const int wr = (wave >> 1) * 128, wc = (wave & 1) * 128;
     const int lr = lane & 31, lh = lane >> 5;
-
+    // Byte address of this lane's 16-byte operand chunk for k-substep 0 of slot
+    // 0; substep s flips chunk bits 1-2 (address ^ 32 s), block q adds 32 rows.
+    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint4*)lds);
+    const uint32_t a_lane = lds0 + kBigPitch * (wr + lr) + 16 * (lh ^ swz8(lr));
+    const uint32_t b_lane = lds0 + BMB * kBigPitch + kBigPitch * (wc + lr) + 16 * (lh ^ swz8(lr));
+    auto rd = [&](int slot, int ks, bf16x8* a, bf16x8* b) {
+        const uint32_t so = (uint32_t)slot * kBigStageBytes, x = 32u * ks;
+        const uint32_t aa = (a_lane + so) ^ x, bb = (b_lane + so) ^ x;
+        a[0] = lds_read16<0>(aa);
+        a[1] = lds_read16<32 * kBigPitch>(aa);
+        a[2] = lds_read16<64 * kBigPitch>(aa);
+        a[3] = lds_read16<96 * kBigPitch>(aa);
+        b[0] = lds_read16<0>(bb);
+        b[1] = lds_read16<32 * kBigPitch>(bb);
+        b[2] = lds_read16<64 * kBigPitch>(bb);
+        b[3] = lds_read16<96 * kBigPitch>(bb);
+    };
+    auto mm = [&](const bf16x8* a, const bf16x8* b) {
 #pragma unroll
-    for (int s0 = 0; s0 < kStages - 1; ++s0) issue(min(s0, nk - 1), s0);
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    };
 
+    bf16x8 fa[2][4], fb[2][4];
+#pragma unroll
+    for (int s0 = 0; s0 < 2; ++s0)
+#pragma unroll
+        for (int t2 = 0; t2 < kBigParts; ++t2) load_part(min(s0, nk - 1), s0, t2);
+    wait_vm<kBigParts>();  // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    rd(0, 0, fa[0], fb[0]);
     for (int i = 0; i < nk; ++i) {
-        wait_vm<4 * (kStages - 2)>();
-        __builtin_amdgcn_s_barrier();
+        const int slot = i & 1;
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+            rd(slot, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+            wait_lgkm<8>();  // substep s's reads (issued before these 8) are back
+            __builtin_amdgcn_sched_barrier(0);
+            mm(fa[s & 1], fb[s & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_lgkm<0>();
+        wait_vm<0>();                  // stage i+1 landed
+        __builtin_amdgcn_s_barrier();  // and every wave is done reading stage i
         asm volatile("" ::: "memory");
-        issue(min(i + kStages - 1, nk - 1), (i + kStages - 1) % kStages);
-        const uint4* sa = lds + (i % kStages) * kBigStageChunks;
-        const uint4* sb = sa + BMB * 4;
+        rd(slot ^ 1, 0, fa[0], fb[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int kn = min(i + 2, nk - 1);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int ch = 2 * ks + lh;
-            bf16x8 af[2], bfr[4];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int ra = wr + 32 * q + lr;
-                af[q] = __builtin_bit_cast(bf16x8, sa[4 * ra + (ch ^ swz(ra))]);
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int rb = wc + 32 * q + lr;
-                bfr[q] = __builtin_bit_cast(bf16x8, sb[4 * rb + (ch ^ swz(rb))]);
-            }
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[q][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q], bfr[j], acc[q][j], 0, 0, 0);
+        for (int t2 = 0; t2 < 16; ++t2) {
+            acc[t2 >> 2][t2 & 3] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][t2 >> 2], fb[1][t2 & 3], acc[t2 >> 2][t2 & 3], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            load_part(kn, slot, t2);  // stage i+2 into the slot stage i used
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
-    wait_vm<0>();
+    wait_vm<0>();  // the clamped trailing loads must land before the workgroup exits
+    wait_lgkm<0>();
 
-    // Lane holds column lr of each 32x32 block, rows 8*jj + 4*lh + r.
+    // Lane holds column lr of each 32x32 block, rows 8*(r/4) + 4*lh + (r%4).
     if (!KV) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -302,57 +376,106 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
 
     const int hidx = (n0 + wc) >> 7;  // [layer][K/V][head] of this wave's 128 columns
     const int l = hidx >> 4, isv = (hidx >> 3) & 1, head = hidx & 7;
-    if (!isv) {
-        // k_norm: row sums of squares over the head = the wave's 4 column blocks x 32 lanes.
-        const uint16_t* gk = static_cast<const uint16_t*>(ep.gk) + l * 128;
-        float g[4];
+    uint16_t* cache = static_cast<uint16_t*>(isv ? ep.vc[l] : ep.kc[l]);
+    const int64_t nslots = ep.num_pages * 16;
+    const int rbase = m0 + wr;  // first row of this wave's 128
+
+    if (isv) {
+        // V granules hold one dim of 8 tokens (te = 4*(t/8) + t%4, half th =
+        // (t/4)%2).  When a 32-row block fills two pages in slot order, the 8
+        // values a lane keeps for rows 8*(r/4) + 4*lh + r%4, r = 0..7 (8..15),
+        // are exactly the granule of page 0 (page 1) for half lh: one 16-byte
+        // store each.  Otherwise every element is stored on its own.
 #pragma unroll
-        for (int j = 0; j < 4; ++j) g[j] = bf16_bits_to_f32(gk[32 * j + lr]);
+        for (int i = 0; i < 4; ++i) {
+            const int row0 = rbase + 32 * i;
+            const int myrow = row0 + lr;
+            const int64_t s0 = row0 < p.M ? ep.slot[row0] : -1;
+            const int64_t sm = myrow < p.M ? ep.slot[myrow] : -1;
+            const bool ok = (s0 & 15) == 0 && s0 >= 0 && s0 + 32 <= nslots && sm == s0 + lr;
+            if (__builtin_amdgcn_read_exec() == __ballot(ok) && __ballot(ok) == ~0ull) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+                for (int pg = 0; pg < 2; ++pg) {
+                    uint16_t* blk = cache + (((s0 >> 4) + pg) * 8 + head) * 2048;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const f32x16& v = acc[i][j];
+                        uint4 w;
+                        w.x = pack_bf16x2(v[8 * pg + 0], v[8 * pg + 1]);
+                        w.y = pack_bf16x2(v[8 * pg + 2], v[8 * pg + 3]);
+                        w.z = pack_bf16x2(v[8 * pg + 4], v[8 * pg + 5]);
+                        w.w = pack_bf16x2(v[8 * pg + 6], v[8 * pg + 7]);
+                        *reinterpret_cast<uint4*>(blk + 512 * j + 256 * lh + 8 * lr) = w;
+                    }
+                }
+                continue;
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float ss = 0.f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) ss += acc[i][j][r] * acc[i][j][r];
-#pragma unroll
-                for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o);
-                const float rinv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + ep.eps);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j][r] *= rinv * g[j];
-            }
-    }
-    uint16_t* cache = static_cast<uint16_t*>(isv ? ep.vc[l] : ep.kc[l]);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int gm = m0 + wr + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-            if (gm >= p.M) continue;
-            const int64_t slot = ep.slot[gm];
-            if (slot < 0 || slot >= ep.num_pages * 16) continue;
-            uint16_t* blk = cache + ((slot >> 4) * 8 + head) * 2048;
-            const int tt = (int)(slot & 15);
-            if (!isv) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int d0 = 32 * j + lr, d1 = d0 + 64;
-                    const float2 cs = ep.cs[(int64_t)gm * 64 + d0];
-                    const float a = acc[i][j][r], b = acc[i][j + 2][r];
-                    blk[256 * ((d0 & 63) >> 3) + 8 * (tt + 16 * (d0 >> 6)) + (d0 & 7)] =
-                        (uint16_t)f32_to_bf16_bits(a * cs.x - b * cs.y);
-                    blk[256 * ((d1 & 63) >> 3) + 8 * (tt + 16 * (d1 >> 6)) + (d1 & 7)] =
-                        (uint16_t)f32_to_bf16_bits(b * cs.x + a * cs.y);
-                }
-            } else {
+                const int gm = row0 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (gm >= p.M) continue;
+                const int64_t slot = ep.slot[gm];
+                if (slot < 0 || slot >= nslots) continue;
+                uint16_t* blk = cache + ((slot >> 4) * 8 + head) * 2048;
+                const int tt = (int)(slot & 15);
                 const int te = ((tt >> 3) << 2) | (tt & 3), th = (tt >> 2) & 1;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int d = 32 * j + lr;
-                    blk[512 * (d >> 5) + 256 * th + 8 * (d & 31) + te] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
-                }
+                for (int j = 0; j < 4; ++j)
+                    blk[512 * j + 256 * th + 8 * lr + te] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
             }
         }
+        return;
+    }
+
+    // K: k_norm over the head (row sums over 4 column blocks x 32 lanes), RoPE on
+    // the pair (d, d+64) held by one lane, rounded to bf16 and staged through
+    // this wave's 32 KiB of LDS as [row][128 dims] (16-byte chunk c of row r at
+    // c ^ (r % 16)); then each lane stores 16-byte chunks (8 dims of one token),
+    // which is the K granule of the cache.  16 lanes cover one chunk index of
+    // 16 rows: 256 contiguous bytes when those rows fill a page in slot order.
+    float g[4];
+    {
+        const uint16_t* gk = static_cast<const uint16_t*>(ep.gk) + l * 128;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) g[j] = bf16_bits_to_f32(gk[32 * j + lr]);
+    }
+    __syncthreads();  // every wave is done with the operand stages in LDS
+    uint16_t* st16 = reinterpret_cast<uint16_t*>(lds) + wave * 16384;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ss += acc[i][j][r] * acc[i][j][r];
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o);
+            const float rinv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + ep.eps);
+            const int row = 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+            const int gm = min(rbase + row, p.M - 1);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int d0 = 32 * j + lr, d1 = d0 + 64;
+                const float2 cs = ep.cs[(int64_t)gm * 64 + d0];
+                const float a = acc[i][j][r] * (rinv * g[j]), b = acc[i][j + 2][r] * (rinv * g[j + 2]);
+                st16[row * 128 + 8 * ((d0 >> 3) ^ (row & 15)) + (d0 & 7)] = (uint16_t)f32_to_bf16_bits(a * cs.x - b * cs.y);
+                st16[row * 128 + 8 * ((d1 >> 3) ^ (row & 15)) + (d1 & 7)] = (uint16_t)f32_to_bf16_bits(b * cs.x + a * cs.y);
+            }
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+        const int q = it * 64 + lane;
+        const int t = q & 15, c = (q >> 4) & 15, row = 16 * (q >> 8) + t;
+        const int gm = rbase + row;
+        if (gm >= p.M) continue;
+        const int64_t slot = ep.slot[gm];
+        if (slot < 0 || slot >= nslots) continue;
+        const uint4 w = *reinterpret_cast<const uint4*>(st16 + row * 128 + 8 * (c ^ (row & 15)));
+        uint16_t* blk = cache + ((slot >> 4) * 8 + head) * 2048;
+        *reinterpret_cast<uint4*>(blk + 256 * (c & 7) + 8 * ((int)(slot & 15) + 16 * (c >> 3))) = w;
+    }
 }
 
 // (cos, sin) of pos[m] * inv_freq[i] for every fused row: fp64 angle and

@@ -103,7 +103,7 @@ typedef struct dflash_fuse_args {
     int32_t num_layers;       /* 1..5 draft layers to write */
     int64_t M;                /* rows to fuse; 0 is a valid no-op */
     const void* hs[5];        /* device, each [M][hs_stride], first 2560 used; capture order */
-    int64_t hs_stride;        /* elements between rows, >= 2560, multiple of 8 */
+    int64_t hs_stride;        /* elements between rows, >= 2560, multiple of 8, <= 2^22 */
     const void* wc;           /* device [2560][12800] row-major (out, in) */
     const void* gc;           /* device [2560] fusion-norm weight */
     const void* wkv;          /* device [num_layers*2048][2560]; per layer 1024 K rows then 1024 V rows */

@@ -171,6 +171,7 @@ def test_fuse_validation(lib):
     assert _ws(lib, "fuse", _fuse_args(num_layers=6))[0] == -1
     assert _ws(lib, "fuse", _fuse_args(M=-1))[0] == -1
     assert _call(lib, "dflash_ctx_fuse", _fuse_args(hs_stride=2500), FAKE, n) == -1
+    assert _call(lib, "dflash_ctx_fuse", _fuse_args(hs_stride=(1 << 22) + 8), FAKE, n) == -1
     assert _call(lib, "dflash_ctx_fuse", _fuse_args(wc=None), FAKE, n) == -1
     a = _fuse_args()
     a.k_cache[1] = None

@@ -127,3 +127,24 @@ def test_fuse_large_ragged_rows_scattered_slots():
     ht_err, kv_err, _, _ = _run(M, L, BF16, 6, npages, slots, pos, rows=rows)
     note(f"fuse large ragged M={M} L={L}: H_t err {ht_err:.3e}, K/V err {kv_err:.3e}")
     assert ht_err <= TOL[BF16] and kv_err <= TOL[BF16]
+
+
+@pytest.mark.parametrize("shift", [16, 8])
+def test_fuse_large_contiguous_slots_page_offsets(shift):
+    """Large-M path with slots in order starting at `shift`: with 16 every full
+    32-row block fills two whole pages (the V granule store), with 8 none does
+    (element stores); M = 8200 leaves a partial last block either way.  Slots
+    outside the written range must keep their sentinel."""
+    M, L = 8200, 1
+    npages = (M + shift + 15) // 16 + 2
+    slots = shift + np.arange(M, dtype=np.int64)
+    pos = np.arange(M, dtype=np.int32) + 5
+    rows = np.sort(np.random.default_rng(11).choice(M, 40, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    ht_err, kv_err, kcs, vcs = _run(M, L, BF16, 7, npages, slots, pos, rows=rows)
+    note(f"fuse contiguous slots shift={shift} M={M}: H_t err {ht_err:.3e}, K/V err {kv_err:.3e}")
+    assert ht_err <= TOL[BF16] and kv_err <= TOL[BF16]
+    untouched = np.setdiff1d(np.arange(npages * 16), slots)
+    for cache, offs in ((kcs[0], k_offsets()), (vcs[0], v_offsets())):
+        vals = read_slots(exact(cache), untouched, offs)
+        assert np.all(vals == -7.0)

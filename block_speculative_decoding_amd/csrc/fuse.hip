@@ -7,7 +7,7 @@
 // per-head K RMSNorm before RoPE; unquantized K/V projections fused into one
 // matrix multiplication).
 //
-// Launch sequence on one stream:
+// Launch sequence on one stream (bf16, M below 8192 rows):
 //   gemm  (A = the five capture pointers, one K segment each; B = W_c)
 //         -> fp32 split-K partials [ks1][M][2560]
 //   norm  -> sums the partials, RMSNorm with g_c, stores H_t (dtype)
@@ -15,10 +15,13 @@
 //         -> fp32 split-K partials [ks2][M][N]
 //   kv    -> sums the partials; per 128-wide head: K gets k_norm and RoPE,
 //            V is copied; both are scattered into the paged cache layout.
-// The bf16 GEMM is a 128x128x64 tile on the 32x32x16 bf16 matrix
-// instruction, LDS double-buffered with an XOR swizzle, tiles ordered in
-// 8-row groups and laid out contiguously per XCD so neighbouring tiles that
-// share an operand panel run on the same L2.
+// From 8192 rows on, both GEMMs use 256x256 tiles without split-K and the
+// second one carries the K/V injection in its epilogue (no kv launch).
+// The bf16 GEMMs run on the 32x32x16 bf16 matrix instruction with operands
+// staged through LDS by loads that write LDS directly (global_load_lds for
+// the split-K kernel, buffer loads for the large-M one); tiles are laid out
+// contiguously per XCD in 8-row groups so that tiles sharing an operand panel
+// run on the same L2.
 #include <cmath>
 
 #include "device_common.h"

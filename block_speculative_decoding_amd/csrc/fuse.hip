@@ -535,34 +535,34 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
 // loop is unrolled to kMaxKs so all partial loads of a row are in flight at once.
 constexpr int kMaxKs = 16;
 
+// 640 threads x 4 consecutive columns = one 2560-wide row per workgroup.
+constexpr int kNormThreads = DFLASH_D / 4;
+
 template <typename T>
-__global__ __launch_bounds__(kThreads) void fuse_norm_kernel(const float* part, int ks, int M, const T* gc,
-                                                            float eps, T* ht, T* ht_out) {
-    constexpr int D = DFLASH_D, PER = D / kThreads;
+__global__ __launch_bounds__(kNormThreads) void fuse_norm_kernel(const float* part, int ks, int M, const T* gc,
+                                                                float eps, T* ht, T* ht_out) {
+    constexpr int D = DFLASH_D;
     const int m = blockIdx.x, tid = threadIdx.x;
-    float y[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) y[e] = 0.f;
+    float y[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < kMaxKs; ++s) {
         if (s < ks) {
-            const float* row = part + ((int64_t)s * M + m) * D + tid;
-#pragma unroll
-            for (int e = 0; e < PER; ++e) y[e] += row[kThreads * e];
+            const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)s * M + m) * D + 4 * tid);
+            y[0] += v.x; y[1] += v.y; y[2] += v.z; y[3] += v.w;
         }
     }
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) ss += y[e] * y[e];
+    float ss = y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
     ss = wave_sum(ss);
-    __shared__ float red[kThreads / 64];
+    __shared__ float red[kNormThreads / 64];
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
-    const float tot = red[0] + red[1] + red[2] + red[3];
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < kNormThreads / 64; ++i) tot += red[i];
     const float rinv = 1.0f / sqrtf(tot * (1.0f / D) + eps);
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-        const int c = tid + kThreads * e;
+    for (int e = 0; e < 4; ++e) {
+        const int c = 4 * tid + e;
         const float h = Elem<T>::load(gc, c) * (y[e] * rinv);
         Elem<T>::store(ht, (int64_t)m * D + c, h);
         if (ht_out) Elem<T>::store(ht_out, (int64_t)m * D + c, h);
@@ -702,11 +702,11 @@ hipError_t launch_fuse(const dflash_fuse_args& a, const FusePlan& pl, void* ws, 
     }
 
     if (bf)
-        fuse_norm_kernel<uint16_t><<<M, kThreads, 0, s>>>(part1, pl.ks1, M, static_cast<const uint16_t*>(a.gc),
+        fuse_norm_kernel<uint16_t><<<M, kNormThreads, 0, s>>>(part1, pl.ks1, M, static_cast<const uint16_t*>(a.gc),
                                                           a.eps, static_cast<uint16_t*>(ht),
                                                           static_cast<uint16_t*>(a.ht_out));
     else
-        fuse_norm_kernel<float><<<M, kThreads, 0, s>>>(part1, pl.ks1, M, static_cast<const float*>(a.gc), a.eps,
+        fuse_norm_kernel<float><<<M, kNormThreads, 0, s>>>(part1, pl.ks1, M, static_cast<const float*>(a.gc), a.eps,
                                                        static_cast<float*>(ht), static_cast<float*>(a.ht_out));
 
     GemmParams g2 = {};

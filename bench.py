@@ -8,7 +8,13 @@ Inputs are synthetic and already resident in HBM when timing starts.  Prints
 one JSON line (rank 0) with cycles/s, the attention roofline and an oracle
 CPU baseline on a bounded sample.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+After the timed cycles (outside the timed region) it also times the prefill
+workload's context fusion (one 32768-token prompt: the [32768,12800]x[12800,2560]
+fusion GEMM, the five layers' K/V projection with k_norm + RoPE + cache write)
+and its verify-only step over [256,8,262144] logits at T = 0.7, reported under
+"kernels" as the fusion's MFMA fraction and the verification's HBM fraction.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill]
 """
 
 import argparse
@@ -37,6 +43,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill fusion / B=256 verify timings")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (5 times), the known-size "
                          "reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
@@ -233,6 +240,59 @@ def cpu_baseline(wl):
     }
 
 
+def timed(torch, fn, warmup=2, reps=5):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def prefill_measurements(torch, dfl, synth):
+    """Prefill workload: ctx_fuse of a 32768-token prompt into 5 layer caches
+    (slots 0..32767 in order), then one verify-only step over B = 256."""
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev).manual_seed(SEED + 1)
+    M = 32768
+    hs = [torch.randn((M, 2560), generator=g, device=dev, dtype=torch.float32).to(bf) for _ in range(5)]
+    w = {k: torch.from_numpy(np.ascontiguousarray(v)).to(bf).to(dev) for k, v in synth.fuse_weights(SEED, LAYERS).items()}
+    npages = M // 16
+    kc = [torch.zeros((npages, 8, 2048), dtype=bf, device=dev) for _ in range(LAYERS)]
+    vc = [torch.zeros((npages, 8, 2048), dtype=bf, device=dev) for _ in range(LAYERS)]
+    pos = torch.arange(M, dtype=torch.int32, device=dev)
+    slot = torch.arange(M, dtype=torch.int64, device=dev)
+    fuse = dfl.prepare_ctx_fuse(hs, w["wc"], w["gc"], w["wkv"], w["gk"], pos, slot, kc, vc)
+    f_ms = timed(torch, fuse)
+    flops, _ = fuse_flops_bytes(M)
+    del hs, kc, vc, fuse
+    # Verify-only step: B = 256, N(0, 4^2) target, draft = target + N(0, 1), T = 0.7.
+    Bv = 256
+    zt = (4.0 * torch.randn((Bv, 8, V), generator=g, device=dev, dtype=torch.float32)).to(bf)
+    zd = (zt[:, :7].float() + torch.randn((Bv, 7, V), generator=g, device=dev, dtype=torch.float32)).to(bf)
+    temp = torch.full((Bv,), 0.7, dtype=torch.float32, device=dev)
+    u = torch.rand((Bv, 7, V), generator=g, device=dev).clamp_(1e-7, 1 - 1e-7)
+    d = (zd.float() / 0.7 - torch.log(-torch.log(u))).argmax(-1).to(torch.int32)
+    del u
+    ver = dfl.prepare_spec_verify(zt, zd, d, temp, seed=SEED, offset=0)
+    v_ms = timed(torch, ver)
+    v_bytes = verify_bytes(temp.cpu().numpy())
+    out = {"prefill_ctx_fuse_m32768": {"ms": round(f_ms, 4), "M": M,
+                                       "TFLOP/s": round(flops / (f_ms * 1e-3) / 1e12, 1),
+                                       "mfma_frac": round(flops / (f_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+           "prefill_verify_b256": {"ms": round(v_ms, 4), "GB/s": round(v_bytes / (v_ms * 1e-3) / 1e9, 1),
+                                   "hbm_frac": round(v_bytes / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                   "algorithmic_bytes": v_bytes}}
+    del zt, zd, ver
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -322,6 +382,9 @@ def main():
                          "GB/s": round(f_bytes / (f_ms * 1e-3) / 1e9, 1)},
         },
     }
+    if not args.no_prefill:
+        log("[bench] prefill workload: ctx_fuse M=32768, verify B=256")
+        res["kernels"].update(prefill_measurements(torch, dfl, synth))
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(wl)

@@ -85,9 +85,14 @@ __device__ __forceinline__ U64x4 philox4x64_10(U64x4 c, uint64_t k0, uint64_t k1
     return c;
 }
 
-// u = ((w >> 41) + 0.5) * 2^-23 : exact in fp32, strictly inside (0, 1).
+// u = (bits + 0.5) * 2^-23 of a word's top 23 bits (half 0: bits 41..63) or
+// of its low word's top 23 bits (half 1: bits 9..31): exact in fp32,
+// strictly inside (0, 1).
 __device__ __forceinline__ float word_to_uniform(uint64_t w) {
     return ((float)(uint32_t)(w >> 41) + 0.5f) * 1.1920928955078125e-07f;
+}
+__device__ __forceinline__ float word_to_uniform_lo(uint64_t w) {
+    return ((float)(((uint32_t)w >> 9) & 0x7FFFFFu) + 0.5f) * 1.1920928955078125e-07f;
 }
 
 // ---- wave64 reductions ----

@@ -305,10 +305,6 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------- sample
-__device__ __forceinline__ float gumbel_from_word(uint64_t w) {
-    const float u = word_to_uniform(w);
-    return -logf(-logf(u));
-}
 
 // Gumbel noise of the 23-bit uniforms lies in [kGmin, kGmax] (u in
 // [2^-24, 1 - 2^-24]); the bounds are widened a little for fp32 rounding.
@@ -385,27 +381,29 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(Params p) {
 
     float best = -INFINITY, bestp = -INFINITY;
     int bi = 0x7FFFFFFF, bip = 0x7FFFFFFF;
+    // One Philox block holds the uniforms of 8 consecutive entries: entry j of
+    // the group uses half j % 2 of word j / 2.  A bf16 vector is one group; an
+    // fp32 vector is half of one.
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int64_t i0 = c0 + ((int64_t)it * kThreads + tid) * N;
+        bool need = false;
 #pragma unroll
-        for (int q4 = 0; q4 < N / 4; ++q4) {
-            bool need = false;
+        for (int e = 0; e < N; ++e) need |= (use_resid ? w[it][e] : wp[it][e]) >= thr;
+        if (!need) continue;
+        U64x4 c = {(uint64_t)(i0 >> 3), ctr1, 1ull, p.offset};
+        const U64x4 r = philox4x64_10(c, p.seed, 0ull);
+        const uint64_t words[4] = {r.x0, r.x1, r.x2, r.x3};
 #pragma unroll
-            for (int e = 4 * q4; e < 4 * q4 + 4; ++e) need |= (use_resid ? w[it][e] : wp[it][e]) >= thr;
-            if (!need) continue;
-            U64x4 c = {(uint64_t)(i0 / 4 + q4), ctr1, 1ull, p.offset};
-            const U64x4 r = philox4x64_10(c, p.seed, 0ull);
-            const uint64_t words[4] = {r.x0, r.x1, r.x2, r.x3};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int ee = 4 * q4 + e;
-                const float wv = use_resid ? w[it][ee] : wp[it][ee];
-                if (wv == -INFINITY) continue;
-                const float key = wv + gumbel_from_word(words[e]);
-                if (use_resid) combine_arg(best, bi, key, (int)(i0 + ee));
-                else combine_arg(bestp, bip, key, (int)(i0 + ee));
-            }
+        for (int e = 0; e < N; ++e) {
+            const float wv = use_resid ? w[it][e] : wp[it][e];
+            if (wv == -INFINITY) continue;
+            const int j = (int)((i0 + e) & 7);
+            const uint64_t wd = words[j >> 1];
+            const float u = (j & 1) ? word_to_uniform_lo(wd) : word_to_uniform(wd);
+            const float key = wv - logf(-logf(u));
+            if (use_resid) combine_arg(best, bi, key, (int)(i0 + e));
+            else combine_arg(bestp, bip, key, (int)(i0 + e));
         }
     }
 #pragma unroll

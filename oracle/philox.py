@@ -10,12 +10,18 @@ definition (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
 64x64->128-bit products with the multipliers below, and a Weyl key schedule.
 This module is pinned against numpy's independent Philox implementation.
 
-Layout (a reading chosen for this build; the pages are silent):
+Layout (a reading chosen here; the pages are silent):
 
-    U(stream, b, k, i) = word (i mod 4) of Philox4x64-10 with
+    U(stream, b, k, i) = 23-bit half (i mod 2) of word ((i // 2) mod 4) of
+        Philox4x64-10 with
         key     = (seed, 0)
-        counter = (i // 4, 8*b + k, stream, offset)
-    u = ((w >> 41) + 0.5) * 2**-23        -- exact in fp32, inside (0, 1)
+        counter = (i // 8, 8*b + k, stream, offset)
+    half 0: bits 41..63 of the word, half 1: bits 9..31
+    u = (bits + 0.5) * 2**-23             -- exact in fp32, inside (0, 1)
+
+so one Philox block serves eight consecutive entries (the two halves of a
+uniformly random 64-bit word are independent uniform 32-bit values; each
+keeps its top 23 bits).
 
 stream 0: acceptance uniforms (i = 0, k = 1..7)
 stream 1: Gumbel noise of the correction / bonus sample (k = 1..8, i < V)
@@ -71,10 +77,14 @@ def philox4x64_10(counter, key):
         return np.stack([x0, x1, x2, x3], axis=-1)
 
 
-def words_to_uniform(w):
-    """u = ((w >> 41) + 0.5) * 2**-23, as float64 (exactly an fp32 value)."""
+def words_to_uniform(w, half=0):
+    """u = (bits + 0.5) * 2**-23 of a word's 23-bit half (0: bits 41..63,
+    1: bits 9..31), as float64 (exactly an fp32 value)."""
     w = np.asarray(w, dtype=np.uint64)
-    return ((w >> np.uint64(41)).astype(np.float64) + 0.5) * 2.0 ** -23
+    half = np.asarray(half, dtype=np.uint64)
+    shift = np.where(half == 0, np.uint64(41), np.uint64(9))
+    bits = (w >> shift) & np.uint64(0x7FFFFF)
+    return (bits.astype(np.float64) + 0.5) * 2.0 ** -23
 
 
 def uniforms(seed, offset, stream, b, k, i):
@@ -82,25 +92,28 @@ def uniforms(seed, offset, stream, b, k, i):
     b, k, i = np.broadcast_arrays(np.asarray(b, dtype=np.uint64),
                                   np.asarray(k, dtype=np.uint64),
                                   np.asarray(i, dtype=np.uint64))
-    ctr = np.stack([i >> np.uint64(2),
+    ctr = np.stack([i >> np.uint64(3),
                     np.uint64(8) * b + k,
                     np.full(i.shape, stream, dtype=np.uint64),
                     np.full(i.shape, offset, dtype=np.uint64)], axis=-1)
     w = philox4x64_10(ctr, (np.uint64(seed), np.uint64(0)))
-    word = np.take_along_axis(w, (i & np.uint64(3)).astype(np.int64)[..., None], axis=-1)[..., 0]
-    return words_to_uniform(word)
+    word_idx = ((i >> np.uint64(1)) & np.uint64(3)).astype(np.int64)
+    word = np.take_along_axis(w, word_idx[..., None], axis=-1)[..., 0]
+    return words_to_uniform(word, i & np.uint64(1))
 
 
 def uniform_row(seed, offset, stream, b, k, n):
-    """U(stream, b, k, i) for i = 0 .. n-1 (one Philox block per 4 entries)."""
-    nb = (n + 3) // 4
+    """U(stream, b, k, i) for i = 0 .. n-1 (one Philox block per 8 entries)."""
+    nb = (n + 7) // 8
     c0 = np.arange(nb, dtype=np.uint64)
     ctr = np.stack([c0,
                     np.full(nb, 8 * b + k, dtype=np.uint64),
                     np.full(nb, stream, dtype=np.uint64),
                     np.full(nb, offset, dtype=np.uint64)], axis=-1)
-    w = philox4x64_10(ctr, (np.uint64(seed), np.uint64(0)))
-    return words_to_uniform(w.reshape(-1)[:n])
+    w = philox4x64_10(ctr, (np.uint64(seed), np.uint64(0))).reshape(-1)   # words in order
+    hi = words_to_uniform(w, 0)
+    lo = words_to_uniform(w, 1)
+    return np.stack([hi, lo], axis=-1).reshape(-1)[:n]                   # entry 2j: half 0 of word j
 
 
 def gumbel(u):

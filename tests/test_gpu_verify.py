@@ -143,3 +143,32 @@ def test_verify_serving_batch_full_size():
         excl += compare_verify(toks[sl], lens[sl], tr)
     note(f"  mean out_len {lens.mean():.2f}, excluded {excl}, near-ties {nt}")
     assert excl <= 3
+
+
+def test_verify_only_step_b256_sampled_sequences():
+    """Prefill workload's verify-only step: [256, 8, 262144] bf16 at T = 0.7
+    (N(0, 4^2) target, draft = target + N(0, 1)); the GPU verifies all 256
+    sequences in one call, the oracle checks 32 of them (every 8th) with their
+    batch indices, since the decisions of a sequence depend only on its rows
+    and its own counters."""
+    B, V, seed = 256, 262144, 12
+    note("verify-only B=256 V=262144")
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    zt_d = (4.0 * torch.randn((B, 8, V), generator=g, device="cuda")).to(BF16)
+    zd_d = (zt_d[:, :7].float() + torch.randn((B, 7, V), generator=g, device="cuda")).to(BF16)
+    temp = np.full(B, 0.7, dtype=np.float32)
+    pick = np.arange(0, B, 8)
+    d = np.zeros((B, 7), dtype=np.int32)
+    d[pick] = synth.sample_drafts(seed, exact(zd_d[pick]), temp[pick])
+    import block_speculative_decoding_amd as dfl
+    toks, lens, nt = dfl.spec_verify(zt_d, zd_d, dev(d, torch.int32), dev(temp, F32), seed=seed, offset=3)
+    torch.cuda.synchronize()
+    toks, lens = toks.cpu().numpy(), lens.cpu().numpy()
+    assert np.all((lens >= 1) & (lens <= 8))
+    excl = 0
+    for b in pick:
+        tr = oracle.spec_verify_ref(exact(zt_d[b:b + 1]), exact(zd_d[b:b + 1]), d[b:b + 1], temp[b:b + 1], seed, 3,
+                                    batch_offset=int(b))
+        excl += compare_verify(toks[b:b + 1], lens[b:b + 1], tr)
+    note(f"  checked {len(pick)} sequences, excluded {excl}, near-ties {nt}")
+    assert excl <= 2

@@ -44,15 +44,17 @@ def test_vectorised_equals_scalar():
 
 
 def test_uniform_layout_word_selection():
-    # U(s, b, k, i) is word i % 4 of the block at counter (i // 4, 8b + k, s, offset).
+    # U(s, b, k, i) is 23-bit half i % 2 (0: bits 41..63, 1: bits 9..31) of
+    # word (i // 2) % 4 of the block at counter (i // 8, 8b + k, s, offset).
     seed, off, s, b, k = 11, 4, 1, 3, 5
     i = np.arange(37)
     u = uniforms(seed, off, s, b, k, i)
     for j in i:
-        blk = philox4x64_10(np.array([j // 4, 8 * b + k, s, off], dtype=np.uint64),
+        blk = philox4x64_10(np.array([j // 8, 8 * b + k, s, off], dtype=np.uint64),
                             (np.uint64(seed), np.uint64(0)))
-        w = int(blk[j % 4])
-        assert u[j] == ((w >> 41) + 0.5) * 2.0 ** -23
+        w = int(blk[(j // 2) % 4])
+        bits = (w >> 41) if j % 2 == 0 else ((w >> 9) & 0x7FFFFF)
+        assert u[j] == (bits + 0.5) * 2.0 ** -23
     np.testing.assert_array_equal(uniform_row(seed, off, s, b, k, 37), u)
 
 
@@ -61,9 +63,23 @@ def test_uniform_range_and_fp32_exact():
     u = words_to_uniform(w)
     assert u[0] == 0.5 * 2.0 ** -23 and u[-1] == 1.0 - 0.5 * 2.0 ** -23
     assert u[3] == 1.5 * 2.0 ** -23
+    # low half: bits 9..31 only
+    lo = words_to_uniform(np.array([0, 2 ** 9 - 1, 2 ** 9, 2 ** 32 - 1, 2 ** 64 - 1 - (2 ** 32 - 2 ** 9)],
+                                   dtype=np.uint64), 1)
+    assert lo[0] == lo[1] == 0.5 * 2.0 ** -23 and lo[2] == 1.5 * 2.0 ** -23
+    assert lo[3] == 1.0 - 0.5 * 2.0 ** -23 and lo[4] == 0.5 * 2.0 ** -23
     rowu = uniform_row(1, 2, 1, 0, 1, 1 << 16)
     assert np.all(rowu > 0) and np.all(rowu < 1)
     np.testing.assert_array_equal(rowu.astype(np.float32).astype(np.float64), rowu)
+
+
+def test_uniform_halves_are_independent():
+    # The two halves of the same words: no correlation beyond sampling noise.
+    n = 200_000
+    u = uniform_row(77, 0, 1, 2, 3, 2 * n)
+    hi, lo = u[0::2], u[1::2]
+    r = np.corrcoef(hi, lo)[0, 1]
+    assert abs(r) < 4 / np.sqrt(n)
 
 
 def test_uniform_and_gumbel_moments():

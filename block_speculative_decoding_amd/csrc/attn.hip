@@ -6,9 +6,12 @@
 // RoPE; the block attends bidirectionally over the cached context followed
 // by its own eight keys ("DFlash & DFlash2" 4.1: K = [K_ctx ; K_blk]).
 //
-// bf16 design.  One workgroup (4 waves) owns (sequence b, KV head g, split c).
-// The 4 query heads x 8 positions of KV head g form 32 query rows, so each
-// 32-token tile is two dense 32x32 products on the matrix cores:
+// bf16 design.  One workgroup (8 waves) owns (sequence b, KV heads 2h and
+// 2h+1, split c); four waves work on each head.  A head's (page, head) K and
+// V blocks are 4 KiB each and the two heads' blocks are neighbours, so the
+// workgroup reads 8-KiB runs of the shuffled pages.  The 4 query heads x 8
+// positions of KV head g form 32 query rows, so each 32-token tile is two
+// dense 32x32 products on the matrix cores:
 //     S^T[32 tok x 32 rows] = K[32 x 128] . Q^T        (8 x mfma 32x32x16)
 //     O^T[128 x 32 rows]   += V^T[128 x 32] . P^T      (8 x mfma 32x32x16)
 // The page layouts (see include/dflash.h) put each lane's operand bytes in
@@ -16,9 +19,9 @@
 // run, so K and V go from HBM straight into operand registers.  A lane of
 // S^T owns one query row and 16 of the 32 tokens, so the softmax row
 // reductions need a single cross-half exchange.  Waves take tiles
-// round-robin; the block's own 8 keys are one extra (masked) tile of the
-// last split.  Waves merge through LDS; splits merge with a log-sum-exp
-// kernel.
+// round-robin within their head; the block's own 8 keys are one extra
+// (masked) tile of the last split.  A head's four waves merge through LDS;
+// splits merge with a log-sum-exp kernel.
 #include <cmath>
 
 #include "device_common.h"
@@ -28,7 +31,9 @@ namespace dflash {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;    // waves per head, taking the head's tiles round-robin
+constexpr int kHpw = 2;      // KV heads per workgroup
+constexpr int kWgThreads = kThreads * kHpw;
 constexpr int kTile = 32;
 constexpr int kQStride = 136;    // bf16 per LDS row of q^ / k^blk (padded)
 constexpr int kAccStride = 132;  // floats per LDS row in the wave merge
@@ -104,17 +109,12 @@ __device__ __forceinline__ void load_row16(const T* row, int part, float* x) {
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
 
 // ---------------------------------------------------------------- bf16 MFMA kernel
-#ifndef ATTN_PREFETCH
-#define ATTN_PREFETCH 1
-#endif
-#ifndef ATTN_Q_REGS
-#define ATTN_Q_REGS 1
-#endif
-#ifndef ATTN_WAVES_PER_EU
-#define ATTN_WAVES_PER_EU 1
-#endif
-__global__ __launch_bounds__(kThreads, ATTN_WAVES_PER_EU) void attn_bf16_kernel(AttnParams p) {
-    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+__global__ __launch_bounds__(kWgThreads, 1) void attn_bf16_kernel(AttnParams p) {
+    const int c = blockIdx.x, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int hw = wave >> 2, wl = wave & 3;      // head within the workgroup, wave within the head
+    const int g = blockIdx.y * kHpw + hw;
     const SeqRange sr = seq_range(p, b);
     if (c >= sr.nspl) return;
     const int tb = sr.a0 + c * p.split;
@@ -122,57 +122,61 @@ __global__ __launch_bounds__(kThreads, ATTN_WAVES_PER_EU) void attn_bf16_kernel(
     const bool last = c == sr.nspl - 1;
     const int ntiles = te > tb ? (te - tb + kTile - 1) / kTile : 0;
 
-    __shared__ __attribute__((aligned(16))) float smem[kWaves * (64 + 32 * kAccStride)];
-    uint16_t* qs = reinterpret_cast<uint16_t*>(smem);          // [32][kQStride]
-    uint16_t* kbs = qs + 32 * kQStride;                         // [8][kQStride]
-    uint16_t* vbs = kbs + 8 * kQStride;                         // [8][128]
+    __shared__ __attribute__((aligned(16))) float smem[kHpw * kWaves * (64 + 32 * kAccStride)];
+    uint16_t* qs_all = reinterpret_cast<uint16_t*>(smem);        // [kHpw][32][kQStride]
+    uint16_t* kbs_all = qs_all + kHpw * 32 * kQStride;           // [kHpw][8][kQStride]
+    uint16_t* vbs_all = kbs_all + kHpw * 8 * kQStride;           // [kHpw][8][128]
+    uint16_t* qs = qs_all + hw * 32 * kQStride;
+    uint16_t* kbs = kbs_all + hw * 8 * kQStride;
+    uint16_t* vbs = vbs_all + hw * 8 * 128;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
     const uint16_t* gq = static_cast<const uint16_t*>(p.gq);
     const uint16_t* gk = static_cast<const uint16_t*>(p.gk);
 
-    // ---- prologue: q^ for 32 rows, k^blk / v_blk of head g into LDS
+    // ---- prologue: q^ for 32 rows, k^blk / v_blk of each head into LDS
     {
-        const int n = tid >> 3, part = tid & 7;  // row n = hh*8 + j
-        const int hh = n >> 3, j = n & 7;
+        const int n = tid >> 3, part = tid & 7;  // n = hw2*32 + hh*8 + j
+        const int hw2 = n >> 5, hh = (n >> 3) & 3, j = n & 7;
+        const int g2 = blockIdx.y * kHpw + hw2;
         const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-                               ((((int64_t)b * 32 + 4 * g + hh) * 8 + j) * 128);
+                               ((((int64_t)b * 32 + 4 * g2 + hh) * 8 + j) * 128);
         float x[16], gw[16];
         load_row16(qrow, part, x);
         load_row16(gq, part, gw);
         norm_rope_16(x, gw, part, sr.S + j, p.eps, p.inv_freq);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            qs[n * kQStride + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[e]);
-            qs[n * kQStride + 64 + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[8 + e]);
+            qs_all[n * kQStride + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[e]);
+            qs_all[n * kQStride + 64 + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[8 + e]);
         }
-        if (tid < 64) {
-            const int jj = tid >> 3;
-            const uint16_t* krow = static_cast<const uint16_t*>(p.kb) + ((((int64_t)b * 8 + g) * 8 + jj) * 128);
+        if (tid < 64 * kHpw) {
+            const int hk = tid >> 6, jj = (tid >> 3) & 7;
+            const int gk2 = blockIdx.y * kHpw + hk;
+            const uint16_t* krow = static_cast<const uint16_t*>(p.kb) + ((((int64_t)b * 8 + gk2) * 8 + jj) * 128);
             load_row16(krow, part, x);
             load_row16(gk, part, gw);
             norm_rope_16(x, gw, part, sr.S + jj, p.eps, p.inv_freq);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                kbs[jj * kQStride + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[e]);
-                kbs[jj * kQStride + 64 + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[8 + e]);
+                kbs_all[(hk * 8 + jj) * kQStride + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[e]);
+                kbs_all[(hk * 8 + jj) * kQStride + 64 + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[8 + e]);
             }
-        } else if (tid < 192) {
-            const int t2 = tid - 64;  // 128 threads x 16 B = the 2 KiB of v_blk (8 x 128 bf16)
+        } else if (tid < 64 * kHpw + 128 * kHpw) {
+            const int t2 = tid - 64 * kHpw;  // 128 threads x 16 B = the 2 KiB of v_blk (8 x 128 bf16) per head
+            const int hv = t2 >> 7;
             const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.vb) +
-                                                              (((int64_t)b * 8 + g) * 8 * 128));
-            reinterpret_cast<uint4*>(vbs)[t2] = src[t2];
+                                                              (((int64_t)b * 8 + blockIdx.y * kHpw + hv) * 8 * 128));
+            reinterpret_cast<uint4*>(vbs_all + hv * 8 * 128)[t2 & 127] = src[t2 & 127];
         }
     }
     // Physical page ids of this split, staged once in LDS (-1 past the sequence
     // or out of range) so a tile's K/V addresses need no dependent global read.
-    int* pages = reinterpret_cast<int*>(vbs + 8 * 128);  // [split/16 + 2]
+    int* pages = reinterpret_cast<int*>(vbs_all + kHpw * 8 * 128);  // [split/16 + 2]
     const int pg_first = tb >> 4;
     const int npg = ((te > tb ? te - 1 : tb) >> 4) - pg_first + 2;
     {
         const int32_t* bt = p.bt + (int64_t)b * p.max_pages;
-        for (int i = tid; i < npg; i += kThreads) {
+        for (int i = tid; i < npg; i += kWgThreads) {
             const int pg = pg_first + i;
             int ph = -1;
             if (pg * 16 < te) {
@@ -186,11 +190,9 @@ __global__ __launch_bounds__(kThreads, ATTN_WAVES_PER_EU) void attn_bf16_kernel(
 
     const int m32 = lane & 31, hl = lane >> 5;
     const uint16_t* qlds = qs + m32 * kQStride + 64 * hl;  // this lane's Q^T operand row
-#if ATTN_Q_REGS
     bf16x8 qreg[8];
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) qreg[kb] = *reinterpret_cast<const bf16x8*>(qlds + 8 * kb);
-#endif
     const float sl2 = kLog2e * 0.08838834764831845f;      // log2(e) / sqrt(128)
     const uint16_t* kc = static_cast<const uint16_t*>(p.kc);
     const uint16_t* vc = static_cast<const uint16_t*>(p.vc);
@@ -202,8 +204,7 @@ __global__ __launch_bounds__(kThreads, ATTN_WAVES_PER_EU) void attn_bf16_kernel(
     const uint4 z4 = make_uint4(0, 0, 0, 0);
 
     // Issue the loads of context tile `it` into kr / vr.  Loads are
-    // unconditional (a missing page reads page 0 and is zeroed in process)
-    // so the compiler can wait for one tile while the next is in flight.
+    // unconditional: a missing page reads page 0 and is zeroed in process.
     auto load = [&](int it, uint4 (&kr)[8], uint4 (&vr)[2][4]) {
         const int T0 = tb + it * kTile;
         const int li = (T0 >> 4) - pg_first;
@@ -255,11 +256,7 @@ __global__ __launch_bounds__(kThreads, ATTN_WAVES_PER_EU) void attn_bf16_kernel(
         f32x16 s = {};
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
-#if ATTN_Q_REGS
             const bf16x8 qop = qreg[kb];
-#else
-            const bf16x8 qop = *reinterpret_cast<const bf16x8*>(qlds + 8 * kb);
-#endif
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[kb]), qop, s, 0, 0, 0);
         }
         // Lane holds query row m32 and tokens 8*jj + 4*hl + r  (register 4*jj + r).
@@ -307,31 +304,13 @@ __global__ __launch_bounds__(kThreads, ATTN_WAVES_PER_EU) void attn_bf16_kernel(
 
     {
         uint4 ka[8], va[2][4];
-#if ATTN_PREFETCH
-        // Two register sets: a wave's next tile is in flight while the current
-        // one is computed.  The last prefetch re-reads the current tile (an L2
-        // hit) so every iteration issues the same loads.
-        uint4 kx[8], vx[2][4];
-        int it = wave;
-        if (it < ntiles) load(it, ka, va);
-        while (it < ntiles) {
-            load(it + kWaves < ntiles ? it + kWaves : it, kx, vx);
-            process(it, false, ka, va);
-            it += kWaves;
-            if (it >= ntiles) break;
-            load(it + kWaves < ntiles ? it + kWaves : it, ka, va);
-            process(it, false, kx, vx);
-            it += kWaves;
-        }
-#else
-        for (int it = wave; it < ntiles; it += kWaves) {
+        for (int it = wl; it < ntiles; it += kWaves) {
             load(it, ka, va);
             process(it, false, ka, va);
         }
-#endif
         // The block's own 8 keys / values: one masked tile for the wave next
         // in the round-robin order, in the last split of the sequence.
-        if (last && wave == (ntiles & (kWaves - 1))) {
+        if (last && wl == (ntiles & (kWaves - 1))) {
             if (m32 < 8) {
 #pragma unroll
                 for (int kb = 0; kb < 8; ++kb)
@@ -367,17 +346,20 @@ __global__ __launch_bounds__(kThreads, ATTN_WAVES_PER_EU) void attn_bf16_kernel(
             wacc[m32 * kAccStride + 32 * db + 8 * (r >> 2) + 4 * hl + (r & 3)] = acc[db][r];
     __syncthreads();
 
-    const int n = tid >> 3, d0 = 16 * (tid & 7);
+    // Threads [256 h, 256 h + 256) merge head h's four waves.
+    const int hm = tid >> 8, gm = blockIdx.y * kHpw + hm;
+    const int n = (tid & 255) >> 3, d0 = 16 * (tid & 7);
+    const float* wbase = smem + hm * kWaves * (64 + 32 * kAccStride);
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, smem[w * (64 + 32 * kAccStride) + n]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wbase[w * (64 + 32 * kAccStride) + n]);
     const float Mu = M == -INFINITY ? 0.f : M;
     float L = 0.f, o[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[e] = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-        const float* base = smem + w * (64 + 32 * kAccStride);
+        const float* base = wbase + w * (64 + 32 * kAccStride);
         const float f = __builtin_amdgcn_exp2f(base[n] - Mu);
         L += base[32 + n] * f;
         const float4* av = reinterpret_cast<const float4*>(base + 64 + n * kAccStride + d0);
@@ -390,7 +372,7 @@ __global__ __launch_bounds__(kThreads, ATTN_WAVES_PER_EU) void attn_bf16_kernel(
     }
     if (sr.nspl == 1) {
         const float inv = 1.0f / L;
-        uint16_t* orow = static_cast<uint16_t*>(p.out) + ((((int64_t)b * 32 + 4 * g + (n >> 3)) * 8 + (n & 7)) * 128) + d0;
+        uint16_t* orow = static_cast<uint16_t*>(p.out) + ((((int64_t)b * 32 + 4 * gm + (n >> 3)) * 8 + (n & 7)) * 128) + d0;
         uint4 w0, w1;
         w0.x = pack_bf16x2(o[0] * inv, o[1] * inv);   w0.y = pack_bf16x2(o[2] * inv, o[3] * inv);
         w0.z = pack_bf16x2(o[4] * inv, o[5] * inv);   w0.w = pack_bf16x2(o[6] * inv, o[7] * inv);
@@ -399,9 +381,9 @@ __global__ __launch_bounds__(kThreads, ATTN_WAVES_PER_EU) void attn_bf16_kernel(
         reinterpret_cast<uint4*>(orow)[0] = w0;
         reinterpret_cast<uint4*>(orow)[1] = w1;
         if (p.lse && (tid & 7) == 0)
-            p.lse[((int64_t)b * 32 + 4 * g + (n >> 3)) * 8 + (n & 7)] = (Mu + log2f(L)) * kLn2;
+            p.lse[((int64_t)b * 32 + 4 * gm + (n >> 3)) * 8 + (n & 7)] = (Mu + log2f(L)) * kLn2;
     } else {
-        float* pp = p.part + (((int64_t)b * 8 + g) * p.nsplit + c) * kPartFloats;
+        float* pp = p.part + (((int64_t)b * 8 + gm) * p.nsplit + c) * kPartFloats;
         if ((tid & 7) == 0) { pp[n] = M; pp[32 + n] = L; }
         float4* dst = reinterpret_cast<float4*>(pp + 64 + n * 128 + d0);
 #pragma unroll
@@ -547,10 +529,11 @@ AttnPlan attn_plan(const dflash_attn_args& a) {
     if (a.split_tokens > 0) {
         split = a.split_tokens;
     } else {
-        // One residency round: 256 CUs x 2 workgroups.  Fewer, longer splits
-        // stream better and leave less to merge.
-        const int64_t pairs = (int64_t)a.B * 8;
-        int64_t want = (512 + pairs - 1) / pairs;
+        // One residency round: one 8-wave workgroup per CU on 256 CUs.
+        // Fewer, longer splits stream better and leave less to merge.
+        const int64_t pairs = (int64_t)a.B * (8 / kHpw);
+        const int64_t target = 512 / kHpw;
+        int64_t want = (target + pairs - 1) / pairs;
         if (want < 1) want = 1;
         int64_t s = (cap + want - 1) / want;
         s = (s + 127) / 128 * 128;
@@ -579,7 +562,7 @@ hipError_t launch_attn(const dflash_attn_args& a, const AttnPlan& pl, void* ws, 
         attn_f32_kernel<<<dim3(8, a.B), kThreads, 0, s>>>(p);
         return hipGetLastError();
     }
-    attn_bf16_kernel<<<dim3(pl.nsplit, 8, a.B), kThreads, 0, s>>>(p);
+    attn_bf16_kernel<<<dim3(pl.nsplit, 8 / kHpw, a.B), kWgThreads, 0, s>>>(p);
     if (pl.nsplit > 1) attn_merge_kernel<uint16_t><<<dim3(8, a.B), kThreads, 0, s>>>(p);
     return hipGetLastError();
 }

@@ -535,8 +535,21 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
 // loop is unrolled to kMaxKs so all partial loads of a row are in flight at once.
 constexpr int kMaxKs = 16;
 
-// 640 threads x 4 consecutive columns = one 2560-wide row per workgroup.
+// Split-K path (ks partials): 640 threads x 4 consecutive columns = one
+// 2560-wide row per workgroup, all ks partial loads of a thread in flight.
 constexpr int kNormThreads = DFLASH_D / 4;
+
+template <typename T>
+__device__ __forceinline__ void norm_store(const float* y, float rinv, const T* gc, int64_t base, int c0, T* ht,
+                                           T* ht_out) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int c = c0 + e;
+        const float h = Elem<T>::load(gc, c) * (y[e] * rinv);
+        Elem<T>::store(ht, base + c, h);
+        if (ht_out) Elem<T>::store(ht_out, base + c, h);
+    }
+}
 
 template <typename T>
 __global__ __launch_bounds__(kNormThreads) void fuse_norm_kernel(const float* part, int ks, int M, const T* gc,
@@ -560,12 +573,30 @@ __global__ __launch_bounds__(kNormThreads) void fuse_norm_kernel(const float* pa
 #pragma unroll
     for (int i = 0; i < kNormThreads / 64; ++i) tot += red[i];
     const float rinv = 1.0f / sqrtf(tot * (1.0f / D) + eps);
+    norm_store(y, rinv, gc, (int64_t)m * D, 4 * tid, ht, ht_out);
+}
+
+// Single-partial path (large M): one wave per row, 4 rows per workgroup, ten
+// 16-byte loads per lane in flight, a wave-only reduction.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void fuse_norm_rows_kernel(const float* part, int M, const T* gc, float eps,
+                                                                 T* ht, T* ht_out) {
+    constexpr int D = DFLASH_D, PER = D / (64 * 4);  // 10 float4 per lane
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (m >= M) return;
+    const float4* row = reinterpret_cast<const float4*>(part + (int64_t)m * D);
+    float4 v[PER];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int c = 4 * tid + e;
-        const float h = Elem<T>::load(gc, c) * (y[e] * rinv);
-        Elem<T>::store(ht, (int64_t)m * D + c, h);
-        if (ht_out) Elem<T>::store(ht_out, (int64_t)m * D + c, h);
+    for (int i = 0; i < PER; ++i) v[i] = row[64 * i + lane];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    ss = wave_sum(ss);
+    const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const float y[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        norm_store(y, rinv, gc, (int64_t)m * D, 4 * (64 * i + lane), ht, ht_out);
     }
 }
 
@@ -701,13 +732,23 @@ hipError_t launch_fuse(const dflash_fuse_args& a, const FusePlan& pl, void* ws, 
         if (e != hipSuccess) return e;
     }
 
-    if (bf)
+    if (pl.ks1 == 1) {
+        const int nb = (M + 3) / 4;
+        if (bf)
+            fuse_norm_rows_kernel<uint16_t><<<nb, kThreads, 0, s>>>(part1, M, static_cast<const uint16_t*>(a.gc), a.eps,
+                                                                    static_cast<uint16_t*>(ht),
+                                                                    static_cast<uint16_t*>(a.ht_out));
+        else
+            fuse_norm_rows_kernel<float><<<nb, kThreads, 0, s>>>(part1, M, static_cast<const float*>(a.gc), a.eps,
+                                                                 static_cast<float*>(ht), static_cast<float*>(a.ht_out));
+    } else if (bf) {
         fuse_norm_kernel<uint16_t><<<M, kNormThreads, 0, s>>>(part1, pl.ks1, M, static_cast<const uint16_t*>(a.gc),
-                                                          a.eps, static_cast<uint16_t*>(ht),
-                                                          static_cast<uint16_t*>(a.ht_out));
-    else
+                                                              a.eps, static_cast<uint16_t*>(ht),
+                                                              static_cast<uint16_t*>(a.ht_out));
+    } else {
         fuse_norm_kernel<float><<<M, kNormThreads, 0, s>>>(part1, pl.ks1, M, static_cast<const float*>(a.gc), a.eps,
-                                                       static_cast<float*>(ht), static_cast<float*>(a.ht_out));
+                                                           static_cast<float*>(ht), static_cast<float*>(a.ht_out));
+    }
 
     GemmParams g2 = {};
     g2.aseg[0] = ht; g2.a_stride = DFLASH_D; g2.seg_w = DFLASH_D;

@@ -187,9 +187,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
             }
 }
 
-// ---- bf16 GEMM for large M: 256x256 tile, four waves of 128x128 (4x4 blocks
-// of the 32x32x16 instruction, 256 fp32 accumulators per lane), 64 k per stage
-// in a two-stage LDS ring (2 x 64 KiB), no split-K.
+// ---- bf16 GEMM for large M: 256x256 tile, eight waves (two per SIMD) of
+// 128x64 (4x2 blocks of the 32x32x16 instruction, 128 fp32 accumulators per
+// lane), 64 k per stage in a two-stage LDS ring (2 x 64 KiB), no split-K.
 //  * Operands reach LDS through buffer loads that write LDS directly (16 B per
 //    lane, lane l at the wave's LDS base + 16 l).  The descriptor's range stops
 //    at row M, so rows of the last A tile past M read as zero.
@@ -198,18 +198,22 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
 //    consecutive rows on distinct banks.
 //  * The operand reads of k-substep s+1 are in flight while substep s
 //    multiplies (inline-asm ds_read_b128 with explicit lgkmcnt waits: the
-//    compiler's own wait placement would drain them), and the next stage's 16
-//    loads are issued one by one between the 16 MFMAs of the last substep.
-// With KV = true the epilogue is the K/V injection: a wave's 128 output
-// columns are exactly one head, so k_norm (row sums over the head), RoPE (pairs
-// d, d+64 sit in the same lane) and the paged-cache store happen from the
-// accumulators, and the fp32 product never reaches memory.
+//    compiler's own wait placement would drain them), and the next stage's 8
+//    loads per thread are issued one by one between the 8 MFMAs of the last
+//    substep.
+// Column blocks: wave w owns rows 128 (w / 4) .. +128 and, within the 256
+// columns, blocks 64 (w % 4) + {0, 32} for the plain GEMM; for the K/V
+// projection (KV = true) blocks 128 (w % 4 / 2) + 32 (w % 2) + {0, 64}, so the
+// RoPE pair (d, d+64) of a head sits in one lane and a head's 128 columns are
+// two waves.  The K/V epilogue does k_norm (row sums over the head, the two
+// waves' halves added through LDS), RoPE and the paged-cache store from the
+// accumulators; the fp32 product never reaches memory.
 constexpr int BMB = 256, BNB = 256;
-constexpr int kBigThreads = 256;
+constexpr int kBigThreads = 512;
 constexpr int BKB = 64;                        // k per stage
 constexpr int kBigPitch = BKB * 2;             // bytes per LDS row
 constexpr int kBigStageBytes = 2 * BMB * kBigPitch;
-constexpr int kBigParts = 2 * BKB / 8;         // buffer loads per thread per stage (A then B)
+constexpr int kBigPartsA = BMB * 8 / kBigThreads;  // buffer loads per thread per stage and operand (4)
 __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -254,7 +258,9 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
     if (!t.valid) return;
     const int nk = p.K / BKB;
 
-    __shared__ __attribute__((aligned(16))) uint4 lds[2 * kBigStageBytes / 16];
+    // Two operand stages; the K epilogue reuses them as a [256][256] bf16
+    // staging tile plus 4 KiB of row sums after them.
+    __shared__ __attribute__((aligned(16))) uint4 lds[2 * kBigStageBytes / 16 + 256];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m0 = t.tm * BMB, n0 = t.tn * BNB;
@@ -262,11 +268,11 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
     const void *aseg0 = p.aseg[0], *aseg1 = p.aseg[1], *aseg2 = p.aseg[2], *aseg3 = p.aseg[3], *aseg4 = p.aseg[4];
     const uint32_t arows = (uint32_t)min(p.M - m0, BMB);
 
-    // Load j of a thread covers unit P = j * 256 + tid of the A (or B) half:
+    // Load j of a thread covers unit P = j * 512 + tid of the A (or B) half:
     // row P >> 3, chunk (P & 7) ^ swz8(row).
-    uint32_t voa[8], vob[8];
+    uint32_t voa[kBigPartsA], vob[kBigPartsA];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kBigPartsA; ++j) {
         const int P = j * kBigThreads + tid, r = P >> 3, c = (P & 7) ^ swz8(r);
         voa[j] = (uint32_t)(r * (int)p.a_stride + 8 * c) * 2u;
         vob[j] = (uint32_t)(r * p.K + 8 * c) * 2u;
@@ -274,7 +280,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
     auto load_part = [&](int kt, int slot, int part) {
         const int kg = kt * BKB;
         uint4* sb = lds + slot * (kBigStageBytes / 16) + wave * 64;
-        if (part < 8) {
+        if (part < kBigPartsA) {
             // The K/V projection's A operand (H_t) is one segment.
             const int seg = KV ? 0 : kg / p.seg_w;
             const int kc = kg - seg * p.seg_w;
@@ -284,20 +290,23 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
             llvm_amdgcn_raw_buffer_load_lds(rs, (__attribute__((address_space(3))) uint32_t*)(sb + part * kBigThreads), 16,
                                             (int)voa[part], 0, 0, 0);
         } else {
+            const int j = part - kBigPartsA;
             const i32x4 rs = buffer_rsrc(bmat + kg, (uint32_t)BNB * (uint32_t)p.K * 2u - (uint32_t)kg * 2u);
             llvm_amdgcn_raw_buffer_load_lds(
-                rs, (__attribute__((address_space(3))) uint32_t*)(sb + BMB * 8 + (part - 8) * kBigThreads), 16,
-                (int)vob[part - 8], 0, 0, 0);
+                rs, (__attribute__((address_space(3))) uint32_t*)(sb + BMB * 8 + j * kBigThreads), 16, (int)vob[j], 0, 0, 0);
         }
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
+        for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16){};
 
-    const int wr = (wave >> 1) * 128, wc = (wave & 1) * 128;
+    const int wq = wave & 3;
+    const int wr = (wave >> 2) * 128;
+    const int wc = KV ? 128 * (wq >> 1) + 32 * (wq & 1) : 64 * wq;  // column of block 0
+    constexpr int kBstep = KV ? 64 : 32;                           // columns from block 0 to block 1
     const int lr = lane & 31, lh = lane >> 5;
     // Byte address of this lane's 16-byte operand chunk for k-substep 0 of slot
     // 0; substep s flips chunk bits 1-2 (address ^ 32 s), block q adds 32 rows.
@@ -312,24 +321,22 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
         a[2] = lds_read16<64 * kBigPitch>(aa);
         a[3] = lds_read16<96 * kBigPitch>(aa);
         b[0] = lds_read16<0>(bb);
-        b[1] = lds_read16<32 * kBigPitch>(bb);
-        b[2] = lds_read16<64 * kBigPitch>(bb);
-        b[3] = lds_read16<96 * kBigPitch>(bb);
+        b[1] = lds_read16<kBstep * kBigPitch>(bb);
     };
     auto mm = [&](const bf16x8* a, const bf16x8* b) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     };
 
-    bf16x8 fa[2][4], fb[2][4];
+    bf16x8 fa[2][4], fb[2][2];
 #pragma unroll
     for (int s0 = 0; s0 < 2; ++s0)
 #pragma unroll
-        for (int t2 = 0; t2 < kBigParts; ++t2) load_part(min(s0, nk - 1), s0, t2);
-    wait_vm<kBigParts>();  // stage 0 landed
+        for (int t2 = 0; t2 < 2 * kBigPartsA; ++t2) load_part(min(s0, nk - 1), s0, t2);
+    wait_vm<2 * kBigPartsA>();  // stage 0 landed
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     rd(0, 0, fa[0], fb[0]);
@@ -338,7 +345,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
             rd(slot, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-            wait_lgkm<8>();  // substep s's reads (issued before these 8) are back
+            wait_lgkm<6>();  // substep s's reads (issued before these 6) are back
             __builtin_amdgcn_sched_barrier(0);
             mm(fa[s & 1], fb[s & 1]);
             __builtin_amdgcn_sched_barrier(0);
@@ -351,9 +358,9 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
         __builtin_amdgcn_sched_barrier(0);
         const int kn = min(i + 2, nk - 1);
 #pragma unroll
-        for (int t2 = 0; t2 < 16; ++t2) {
-            acc[t2 >> 2][t2 & 3] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][t2 >> 2], fb[1][t2 & 3], acc[t2 >> 2][t2 & 3], 0, 0, 0);
+        for (int t2 = 0; t2 < 8; ++t2) {
+            acc[t2 >> 1][t2 & 1] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][t2 >> 1], fb[1][t2 & 1], acc[t2 >> 1][t2 & 1], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             load_part(kn, slot, t2);  // stage i+2 into the slot stage i used
             __builtin_amdgcn_sched_barrier(0);
@@ -367,18 +374,21 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int gm = m0 + wr + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    const int gn = n0 + wc + 32 * j + lr;
+                    const int gn = n0 + wc + kBstep * j + lr;
                     if (gm < p.M) p.part[(int64_t)gm * p.N + gn] = acc[i][j][r];
                 }
         return;
     }
 
-    const int hidx = (n0 + wc) >> 7;  // [layer][K/V][head] of this wave's 128 columns
+    // Head of this wave's columns: [layer][K/V][head]; both halves of a head
+    // (waves w and w ^ 1) share it.  Dims d0 = 32 (w % 2) + lr and d0 + 64.
+    const int hidx = (n0 >> 7) + (wq >> 1);
     const int l = hidx >> 4, isv = (hidx >> 3) & 1, head = hidx & 7;
+    const int d0 = 32 * (wq & 1) + lr;
     uint16_t* cache = static_cast<uint16_t*>(isv ? ep.vc[l] : ep.kc[l]);
     const int64_t nslots = ep.num_pages * 16;
     const int rbase = m0 + wr;  // first row of this wave's 128
@@ -396,19 +406,20 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
             const int64_t s0 = row0 < p.M ? ep.slot[row0] : -1;
             const int64_t sm = myrow < p.M ? ep.slot[myrow] : -1;
             const bool ok = (s0 & 15) == 0 && s0 >= 0 && s0 + 32 <= nslots && sm == s0 + lr;
-            if (__builtin_amdgcn_read_exec() == __ballot(ok) && __ballot(ok) == ~0ull) {
+            if (__ballot(ok) == ~0ull) {
 #pragma unroll
                 for (int pg = 0; pg < 2; ++pg) {
                     uint16_t* blk = cache + (((s0 >> 4) + pg) * 8 + head) * 2048;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
+                    for (int j = 0; j < 2; ++j) {
                         const f32x16& v = acc[i][j];
+                        const int d = d0 + 64 * j;
                         uint4 w;
                         w.x = pack_bf16x2(v[8 * pg + 0], v[8 * pg + 1]);
                         w.y = pack_bf16x2(v[8 * pg + 2], v[8 * pg + 3]);
                         w.z = pack_bf16x2(v[8 * pg + 4], v[8 * pg + 5]);
                         w.w = pack_bf16x2(v[8 * pg + 6], v[8 * pg + 7]);
-                        *reinterpret_cast<uint4*>(blk + 512 * j + 256 * lh + 8 * lr) = w;
+                        *reinterpret_cast<uint4*>(blk + 512 * (d >> 5) + 256 * lh + 8 * (d & 31)) = w;
                     }
                 }
                 continue;
@@ -423,60 +434,80 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
                 const int tt = (int)(slot & 15);
                 const int te = ((tt >> 3) << 2) | (tt & 3), th = (tt >> 2) & 1;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    blk[512 * j + 256 * th + 8 * lr + te] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
+                for (int j = 0; j < 2; ++j) {
+                    const int d = d0 + 64 * j;
+                    blk[512 * (d >> 5) + 256 * th + 8 * (d & 31) + te] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
+                }
             }
         }
         return;
     }
 
-    // K: k_norm over the head (row sums over 4 column blocks x 32 lanes), RoPE on
-    // the pair (d, d+64) held by one lane, rounded to bf16 and staged through
-    // this wave's 32 KiB of LDS as [row][128 dims] (16-byte chunk c of row r at
-    // c ^ (r % 16)); then each lane stores 16-byte chunks (8 dims of one token),
-    // which is the K granule of the cache.  16 lanes cover one chunk index of
-    // 16 rows: 256 contiguous bytes when those rows fill a page in slot order.
-    float g[4];
+    // K: k_norm over the head, RoPE on the pair (d0, d0+64) held by one lane,
+    // rounded to bf16 and staged through LDS as [256 rows][256 columns] of
+    // this workgroup (16-byte chunk c of row r at c ^ (r % 16) within each
+    // 128-column head); then each thread stores 16-byte chunks (8 dims of one
+    // token), the K granule of the cache.  16 consecutive threads cover one
+    // chunk index of 16 rows: 256 contiguous bytes when those rows fill a page
+    // in slot order.
+    float g[2];
     {
         const uint16_t* gk = static_cast<const uint16_t*>(ep.gk) + l * 128;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) g[j] = bf16_bits_to_f32(gk[32 * j + lr]);
+        g[0] = bf16_bits_to_f32(gk[d0]);
+        g[1] = bf16_bits_to_f32(gk[d0 + 64]);
     }
+    // Per-row partial sums of squares of this wave's 64 columns.
+    float ssp[4][16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float ss = acc[i][0][r] * acc[i][0][r] + acc[i][1][r] * acc[i][1][r];
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o);
+            ssp[i][r] = ss;
+        }
     __syncthreads();  // every wave is done with the operand stages in LDS
-    uint16_t* st16 = reinterpret_cast<uint16_t*>(lds) + wave * 16384;
+    float* sums = reinterpret_cast<float*>(lds + 2 * kBigStageBytes / 16);  // [8 waves][128 rows]
+    if (lr == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sums[wave * 128 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3)] = ssp[i][r];
+    }
+    __syncthreads();
+    uint16_t* st16 = reinterpret_cast<uint16_t*>(lds);  // [256 rows][256 columns] bf16
+    const int cb = 128 * (wq >> 1);                      // this head's first column in the stage
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            float ss = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ss += acc[i][j][r] * acc[i][j][r];
-#pragma unroll
-            for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o);
+            const int rl = 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);  // row within the wave's 128
+            const float ss = ssp[i][r] + sums[(wave ^ 1) * 128 + rl];
             const float rinv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + ep.eps);
-            const int row = 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-            const int gm = min(rbase + row, p.M - 1);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int d0 = 32 * j + lr, d1 = d0 + 64;
-                const float2 cs = ep.cs[(int64_t)gm * 64 + d0];
-                const float a = acc[i][j][r] * (rinv * g[j]), b = acc[i][j + 2][r] * (rinv * g[j + 2]);
-                st16[row * 128 + 8 * ((d0 >> 3) ^ (row & 15)) + (d0 & 7)] = (uint16_t)f32_to_bf16_bits(a * cs.x - b * cs.y);
-                st16[row * 128 + 8 * ((d1 >> 3) ^ (row & 15)) + (d1 & 7)] = (uint16_t)f32_to_bf16_bits(b * cs.x + a * cs.y);
-            }
+            const int row = wr + rl;
+            const int gm = min(m0 + row, p.M - 1);
+            const float2 cs = ep.cs[(int64_t)gm * 64 + d0];
+            const float a = acc[i][0][r] * (rinv * g[0]), bb = acc[i][1][r] * (rinv * g[1]);
+            const int d1 = d0 + 64;
+            st16[row * 256 + cb + 8 * ((d0 >> 3) ^ (row & 15)) + (d0 & 7)] = (uint16_t)f32_to_bf16_bits(a * cs.x - bb * cs.y);
+            st16[row * 256 + cb + 8 * ((d1 >> 3) ^ (row & 15)) + (d1 & 7)] = (uint16_t)f32_to_bf16_bits(bb * cs.x + a * cs.y);
         }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    // 256 rows x 2 heads x 16 chunks = 8192 chunks, 16 per thread.
+    const int hs = tid >> 8;                       // head of the pair this thread stores
+    const int headst = ((n0 >> 7) + hs) & 7;
 #pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
-        const int q = it * 64 + lane;
-        const int t = q & 15, c = (q >> 4) & 15, row = 16 * (q >> 8) + t;
-        const int gm = rbase + row;
+    for (int it = 0; it < 16; ++it) {
+        const int q = it * 256 + (tid & 255);
+        const int tk = q & 15, c = (q >> 4) & 15, row = 16 * (q >> 8) + tk;
+        const int gm = m0 + row;
         if (gm >= p.M) continue;
         const int64_t slot = ep.slot[gm];
         if (slot < 0 || slot >= nslots) continue;
-        const uint4 w = *reinterpret_cast<const uint4*>(st16 + row * 128 + 8 * (c ^ (row & 15)));
-        uint16_t* blk = cache + ((slot >> 4) * 8 + head) * 2048;
+        const uint4 w = *reinterpret_cast<const uint4*>(st16 + row * 256 + 128 * hs + 8 * (c ^ (row & 15)));
+        uint16_t* blk = cache + ((slot >> 4) * 8 + headst) * 2048;
         *reinterpret_cast<uint4*>(blk + 256 * (c & 7) + 8 * ((int)(slot & 15) + 16 * (c >> 3))) = w;
     }
 }

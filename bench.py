@@ -4,9 +4,13 @@ One step = one DFlash draft-verify cycle's hot path on the serving batch:
   ctx_fuse  of the newly verified rows (1..8 per sequence) into 5 layer caches
   5 x block_attn (one per draft layer, over ctx_len + new rows)
   spec_verify over [64, 8, 262144] target and [64, 7, 262144] draft logits
-Inputs are synthetic and already resident in HBM when timing starts.  Prints
-one JSON line (rank 0) with cycles/s, the attention roofline and an oracle
-CPU baseline on a bounded sample.
+Inputs are synthetic and already resident in HBM when timing starts.  The K
+timed steps are first run eagerly (per-kernel HIP events; "eager_ms_per_step")
+and then replayed from one HIP graph per step, captured with the same Philox
+offsets (the reported "ms_per_step" and value): the same kernels and work,
+without the per-launch gaps of 13 back-to-back launches.  Prints one JSON line
+(rank 0) with cycles/s, the attention roofline and an oracle CPU baseline on a
+bounded sample.
 
 After the timed cycles (outside the timed region) it also times the prefill
 workload's context fusion (one 32768-token prompt: the [32768,12800]x[12800,2560]
@@ -14,7 +18,7 @@ fusion GEMM, the five layers' K/V projection with k_norm + RoPE + cache write)
 and its verify-only step over [256,8,262144] logits at T = 0.7, reported under
 "kernels" as the fusion's MFMA fraction and the verification's HBM fraction.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill] [--eager]
 """
 
 import argparse
@@ -44,6 +48,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill fusion / B=256 verify timings")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches only (default: also replay each step from a HIP graph)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (5 times), the known-size "
                          "reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
@@ -332,13 +338,35 @@ def main():
         wl.step(args.warmup + i, per_step[i])
     end.record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
+    eager_ms = start.elapsed_time(end)
     for e in per_step:
         fuse_ms.append(e["fuse"][0].elapsed_time(e["fuse"][1]))
         ver_ms.append(e["verify"][0].elapsed_time(e["verify"][1]))
         attn_ms.extend(a.elapsed_time(b) for a, b in e["attn_done"])
-    ms_step = total_ms / K
-    log(f"[bench] {K} steps: {ms_step:.3f} ms/step")
+    eager_step = eager_ms / K
+    log(f"[bench] {K} eager steps: {eager_step:.3f} ms/step")
+    ms_step = eager_step
+    launch = "eager"
+    if not args.eager:
+        # The same K steps (same Philox offsets) captured as one HIP graph each:
+        # identical kernels and work, without per-launch gaps on the stream.
+        graphs = []
+        for i in range(K):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                wl.step(args.warmup + i)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        start.record()
+        for g in graphs:
+            g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        ms_step = start.elapsed_time(end) / K
+        launch = "hip graph per step"
+        log(f"[bench] {K} graph-replayed steps: {ms_step:.3f} ms/step")
 
     a_bytes = attn_bytes(wl.lens)
     a_ms = float(np.mean(attn_ms))
@@ -356,6 +384,7 @@ def main():
         "unit": "cycles/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "eager_ms_per_step": round(eager_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -364,7 +393,8 @@ def main():
         "config": {"workload": "serving batch: B=64, cached context 8192 + 1..8 newly verified rows per "
                                "sequence (shuffled 16-token pages), 5 draft layers, ctx-fuse of the new rows, "
                                "block attention per layer, spec-verify over V=262144 (32 greedy, 32 at T=0.7)",
-                   "B": B, "S": S_CTX, "new_rows": int(wl.M), "layers": LAYERS, "V": V, "parallelism": "none"},
+                   "B": B, "S": S_CTX, "new_rows": int(wl.M), "layers": LAYERS, "V": V, "parallelism": "none",
+                   "launch": launch},
         "roofline": {"kernel": "block_attn (attn_bf16_kernel" + (" + attn_merge_kernel)" if wl.attn[0].ws_bytes else
                                                                   ", one split per sequence: no merge launch)"),
                      "bound": "hbm",

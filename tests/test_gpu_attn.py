@@ -66,7 +66,7 @@ def test_attn_bf16_window(split):
     assert err <= TOL[BF16]
 
 
-def test_attn_fp32_config1_tiny():
+def test_attn_fp32_tiny_context():
     """B=1, S=128, fp32: one draft layer of the tiny configuration."""
     out, lse, ref, ref_lse = _case([128], F32, 0)
     err = np.max(np.abs(out - ref))

@@ -52,7 +52,7 @@ def test_fuse_bf16_small_scattered():
     assert np.all(kk == -7.0)
 
 
-def test_fuse_fp32_config1_tiny():
+def test_fuse_fp32_tiny_context():
     """M=128 context rows, one draft layer, fp32, positions 0..127."""
     M, L, npages = 128, 1, 8
     slots = np.arange(M, dtype=np.int64)
@@ -148,3 +148,17 @@ def test_fuse_large_contiguous_slots_page_offsets(shift):
     for cache, offs in ((kcs[0], k_offsets()), (vcs[0], v_offsets())):
         vals = read_slots(exact(cache), untouched, offs)
         assert np.all(vals == -7.0)
+
+
+def test_fuse_single_stream_context_4096():
+    """Single-stream shape: the 4096 context rows of one sequence fused into
+    five layers (split-K path), slots and positions 0..4095; sampled rows."""
+    M, L = 4096, 5
+    npages = M // 16
+    slots = np.arange(M, dtype=np.int64)
+    pos = np.arange(M, dtype=np.int32)
+    rows = np.sort(np.random.default_rng(13).choice(M, 32, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    ht_err, kv_err, _, _ = _run(M, L, BF16, 8, npages, slots, pos, rows=rows)
+    note(f"fuse single stream M=4096 L=5: H_t err {ht_err:.3e}, K/V err {kv_err:.3e}")
+    assert ht_err <= TOL[BF16] and kv_err <= TOL[BF16]

@@ -37,7 +37,7 @@ def test_verify_mixed_ragged_vocab(dtype):
     assert np.all((lens >= 1) & (lens <= 8))
 
 
-def test_verify_config1_fp32_tiny():
+def test_verify_fp32_tiny_vocab():
     """B=1, V=4096, fp32, logits N(0, 3^2): independent draft rows, rows with
     draft = target + N(0,1), and planted matches; greedy and T=1."""
     V = 4096
@@ -54,7 +54,7 @@ def test_verify_config1_fp32_tiny():
                 d = np.argmax(zt[:, :7], -1).astype(np.int32)
             else:
                 d = synth.sample_drafts(0, zd, temp)
-            note(f"verify config1 {variant} T={T}")
+            note(f"verify tiny fp32 {variant} T={T}")
             toks, lens, nt, tr, _ = _run(zt, zd, d, temp, 0, 0, F32)
             compare_verify(toks, lens, tr)
             if variant == "planted" and T == 0.0:
@@ -172,3 +172,22 @@ def test_verify_only_step_b256_sampled_sequences():
         excl += compare_verify(toks[b:b + 1], lens[b:b + 1], tr)
     note(f"  checked {len(pick)} sequences, excluded {excl}, near-ties {nt}")
     assert excl <= 2
+
+
+def test_verify_single_stream_t1():
+    """Single-stream shape: B = 1, V = 262144 bf16, N(0, 4^2) target, draft =
+    target + N(0, 1), T = 1, four Philox offsets."""
+    B, V, seed = 1, 262144, 31
+    zt, zd = synth.logits(seed, B, V, 4.0, 1.0)
+    temp = np.ones(B, dtype=np.float32)
+    zt_d, zd_d = dev(zt, BF16), dev(zd, BF16)
+    d = synth.sample_drafts(seed, exact(zd_d), temp)
+    import block_speculative_decoding_amd as dfl
+    excl = 0
+    for off in range(4):
+        toks, lens, nt = dfl.spec_verify(zt_d, zd_d, dev(d, torch.int32), dev(temp, F32), seed=seed, offset=off)
+        torch.cuda.synchronize()
+        tr = oracle.spec_verify_ref(exact(zt_d), exact(zd_d), d, temp, seed, off)
+        excl += compare_verify(toks.cpu().numpy(), lens.cpu().numpy(), tr)
+        note(f"  offset {off}: len {int(lens.cpu()[0])}")
+    assert excl <= 1

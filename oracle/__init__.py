@@ -24,6 +24,9 @@ Modules:
 * ``ctx_fuse``    -- context fusion + K/V injection.
 * ``block_attn``  -- non-causal block attention over cached context + block.
 * ``spec_verify`` -- exact speculative verification (greedy and sampled).
+* ``draft_layer`` -- the rest of a draft layer around block attention: block
+                     embedding, input norm + fused Q/K/V projection, output
+                     projection + residual, SwiGLU MLP, final norm.
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test
 against values printed on the pages, closed forms, invariants, brute force
@@ -35,6 +38,7 @@ from .philox import philox4x64_10, uniforms, gumbel
 from .ctx_fuse import ctx_fuse_ref, concat_capture
 from .block_attn import block_attn_ref, attend, prep_block
 from .spec_verify import spec_verify_ref, VerifyTrace
+from .draft_layer import embed_block, qkv_ref, mlp_ref, silu, layer_weight_shapes
 
 __all__ = [
     "bf16_round", "rms_norm", "rope_rotate_half", "rope_angles",
@@ -42,4 +46,5 @@ __all__ = [
     "ctx_fuse_ref", "concat_capture",
     "block_attn_ref", "attend", "prep_block",
     "spec_verify_ref", "VerifyTrace",
+    "embed_block", "qkv_ref", "mlp_ref", "silu", "layer_weight_shapes",
 ]

@@ -16,7 +16,10 @@ After the timed cycles (outside the timed region) it also times the prefill
 workload's context fusion (one 32768-token prompt: the [32768,12800]x[12800,2560]
 fusion GEMM, the five layers' K/V projection with k_norm + RoPE + cache write)
 and its verify-only step over [256,8,262144] logits at T = 0.7, reported under
-"kernels" as the fusion's MFMA fraction and the verification's HBM fraction.
+"kernels" as the fusion's MFMA fraction and the verification's HBM fraction,
+and one layer's block attention over the long-context workload (B = 4
+sequences of 131072 cached tokens on shuffled pages: 16 splits of each
+sequence and the log-sum-exp merge launch).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill] [--eager]
 """
@@ -47,7 +50,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill fusion / B=256 verify timings")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill fusion / B=256 verify / long-context attention timings")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches only (default: also replay each step from a HIP graph)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -299,6 +303,32 @@ def prefill_measurements(torch, dfl, synth):
     return out
 
 
+def long_context_measurement(torch, dfl, synth):
+    """One layer's block attention over 4 sequences of 131072 cached tokens
+    (shuffled 16-token pages, 2.15 GB of K and V): split-K over each sequence,
+    then the log-sum-exp merge."""
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    Bl, Sl = 4, 131072
+    lens = np.full(Bl, Sl, dtype=np.int32)
+    table, npages = synth.page_table(SEED + 2, lens)
+    g = torch.Generator(device=dev).manual_seed(SEED + 2)
+    kc = torch.randn((npages, 8, 2048), generator=g, device=dev, dtype=torch.float32).to(bf)
+    vc = torch.randn((npages, 8, 2048), generator=g, device=dev, dtype=torch.float32).to(bf)
+    blk = {k: torch.from_numpy(np.ascontiguousarray(v)).to(bf).to(dev) for k, v in synth.attn_block(SEED + 2, Bl).items()}
+    att = dfl.prepare_block_attn(blk["q"], blk["k_blk"], blk["v_blk"], blk["gq"], blk["gk"], kc, vc,
+                                 torch.from_numpy(table).to(dev), torch.from_numpy(lens).to(dev))
+    ms = timed(torch, att, warmup=2, reps=10)
+    nbytes = attn_bytes(lens)
+    out = {"long_context_attn_b4_s131072": {
+        "ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
+        "merge_launch": bool(att.ws_bytes)}}
+    del kc, vc, att
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -415,6 +445,8 @@ def main():
     if not args.no_prefill:
         log("[bench] prefill workload: ctx_fuse M=32768, verify B=256")
         res["kernels"].update(prefill_measurements(torch, dfl, synth))
+        log("[bench] long-context workload: block_attn B=4, S=131072")
+        res["kernels"].update(long_context_measurement(torch, dfl, synth))
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(wl)

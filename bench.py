@@ -19,7 +19,10 @@ and its verify-only step over [256,8,262144] logits at T = 0.7, reported under
 "kernels" as the fusion's MFMA fraction and the verification's HBM fraction,
 and one layer's block attention over the long-context workload (B = 4
 sequences of 131072 cached tokens on shuffled pages: 16 splits of each
-sequence and the log-sum-exp merge launch).
+sequence and the log-sum-exp merge launch), and the serving batch's draft
+forward around block attention (block embedding, 5 x [input norm + Q/K/V
+projection, block attention, output projection + SwiGLU MLP], final norm),
+whole and its dense part alone.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill] [--eager]
 """
@@ -51,7 +54,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
-                    help="skip the prefill fusion / B=256 verify / long-context attention timings")
+                    help="skip the timings outside the serving cycle (prefill fusion, B=256 verify, "
+                         "long-context attention, draft forward)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches only (default: also replay each step from a HIP graph)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -329,6 +333,66 @@ def long_context_measurement(torch, dfl, synth):
     return out
 
 
+def draft_measurement(torch, dfl, synth, wl):
+    """The serving batch's draft forward around block attention: the block
+    embedding, then per layer the input norm + Q/K/V projection, block
+    attention over the workload's caches and the output projection + MLP
+    (final norm after the last layer).  Reports the whole forward and its
+    dense part (embedding, projections, norms, MLP) on its own."""
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev).manual_seed(SEED + 3)
+    emb = torch.randn((V, 2560), generator=g, device=dev, dtype=torch.float32).to(bf)
+    anchors = torch.from_numpy(synth.anchors(SEED, B, V)).to(dev)
+    d = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(bf).to(dev)
+    embed = dfl.prepare_draft_embed(emb, anchors, 3)
+    x = embed.out
+    dense, layers = [embed], []
+    y = torch.empty_like(x)
+    for l in range(LAYERS):
+        w = {k: d(v) for k, v in synth.draft_layer_weights(SEED, l).items()}
+        blk = wl.blk_np[l]
+        qkv = dfl.prepare_draft_qkv(x, w["g_in"], w["w_qkv"])
+        q, kb, vb = qkv.outputs
+        att = dfl.prepare_block_attn(q, kb, vb, d(blk["gq"]), d(blk["gk"]), wl.kc[l], wl.vc[l],
+                                     wl.block_table, wl.ctx_len)
+        last = l == LAYERS - 1
+        mlp = dfl.prepare_draft_mlp(x, att.out, w["w_o"], w["g_post"], w["w_gu"], w["w_d"],
+                                    g_final=d(synth.final_norm(SEED)) if last else None, x_out=x,
+                                    y_out=y if last else None)
+        layers.append((qkv, att, mlp))
+        dense += [qkv, mlp]
+
+    def forward():
+        embed()
+        for qkv, att, mlp in layers:
+            qkv()
+            att()
+            mlp()
+
+    def dense_only():
+        for p in dense:
+            p()
+
+    f_ms = timed(torch, forward, warmup=2, reps=10)
+    d_ms = timed(torch, dense_only, warmup=2, reps=10)
+    per_layer = (6144 * 2560 + 2560 * 4096 + 10240 * 2560 + 2560 * 5120)
+    M = 8 * B
+    flops = 2 * M * per_layer * LAYERS
+    # Algorithmic bytes: every weight once, plus per layer and block row the
+    # layer input (read twice: projection and residual), Q/K/V out, the
+    # attention output in and the layer output; the embedding writes M rows.
+    nbytes = per_layer * 2 * LAYERS + LAYERS * M * 2 * (2 * 2560 + 6144 + 4096 + 2560) + M * 2560 * 2
+    del emb, embed, dense, layers
+    torch.cuda.empty_cache()
+    return {"draft_forward_b64": {"ms": round(f_ms, 4), "layers": LAYERS, "block_rows": M},
+            "draft_dense_b64": {"ms": round(d_ms, 4), "TFLOP/s": round(flops / (d_ms * 1e-3) / 1e12, 1),
+                                "mfma_frac": round(flops / (d_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                                "GB/s": round(nbytes / (d_ms * 1e-3) / 1e9, 1),
+                                "hbm_frac": round(nbytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                "weight_bytes": per_layer * 2 * LAYERS}}
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -447,6 +511,8 @@ def main():
         res["kernels"].update(prefill_measurements(torch, dfl, synth))
         log("[bench] long-context workload: block_attn B=4, S=131072")
         res["kernels"].update(long_context_measurement(torch, dfl, synth))
+        log("[bench] draft forward around attention: B=64, 5 layers")
+        res["kernels"].update(draft_measurement(torch, dfl, synth, wl))
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(wl)

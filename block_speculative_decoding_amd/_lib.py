@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdflash.so")
 
 DFLASH_BF16, DFLASH_F32 = 0, 1
-D, NCAPTURE, HQ, HKV, HEAD_DIM, BLOCK, PAGE = 2560, 5, 32, 8, 128, 8, 16
+D, NCAPTURE, HQ, HKV, HEAD_DIM, BLOCK, PAGE, INTER = 2560, 5, 32, 8, 128, 8, 16, 5120
 
 _P = ctypes.c_void_p
 _I32, _I64, _U64, _F32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
@@ -56,9 +56,30 @@ class VerifyArgs(ctypes.Structure):
                 ("out_tokens", _P), ("out_len", _P), ("near_ties", _P)]
 
 
+class EmbedArgs(ctypes.Structure):
+    _fields_ = [("dtype", _I32), ("B", _I32), ("V", _I64),
+                ("emb", _P), ("anchor", _P), ("mask_id", _I32), ("x", _P)]
+
+
+class QkvArgs(ctypes.Structure):
+    _fields_ = [("dtype", _I32), ("B", _I32),
+                ("x", _P), ("g_in", _P), ("w_qkv", _P), ("eps", _F32),
+                ("q", _P), ("k_blk", _P), ("v_blk", _P)]
+
+
+class MlpArgs(ctypes.Structure):
+    _fields_ = [("dtype", _I32), ("B", _I32),
+                ("x", _P), ("o", _P), ("w_o", _P), ("g_post", _P), ("w_gu", _P), ("w_d", _P),
+                ("g_final", _P), ("eps", _F32), ("x_out", _P), ("y_out", _P), ("h_out", _P)]
+
+
+ARG_STRUCTS = (FuseArgs, AttnArgs, VerifyArgs, EmbedArgs, QkvArgs, MlpArgs)
+
 EXPORTS = ["dflash_version", "dflash_last_error", "dflash_args_size",
            "dflash_fuse_workspace_size", "dflash_attn_workspace_size", "dflash_verify_workspace_size",
-           "dflash_ctx_fuse", "dflash_block_attn", "dflash_spec_verify"]
+           "dflash_draft_qkv_workspace_size", "dflash_draft_mlp_workspace_size",
+           "dflash_ctx_fuse", "dflash_block_attn", "dflash_spec_verify",
+           "dflash_draft_embed", "dflash_draft_qkv", "dflash_draft_mlp"]
 
 _lib = None
 
@@ -75,16 +96,20 @@ def load():
     lib.dflash_last_error.restype = ctypes.c_char_p
     lib.dflash_args_size.restype = ctypes.c_size_t
     lib.dflash_args_size.argtypes = [ctypes.c_int]
-    for name, st in (("fuse", FuseArgs), ("attn", AttnArgs), ("verify", VerifyArgs)):
+    for name, st in (("fuse", FuseArgs), ("attn", AttnArgs), ("verify", VerifyArgs),
+                     ("draft_qkv", QkvArgs), ("draft_mlp", MlpArgs)):
         f = getattr(lib, f"dflash_{name}_workspace_size")
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.POINTER(st), ctypes.POINTER(ctypes.c_size_t)]
     for name, st in (("dflash_ctx_fuse", FuseArgs), ("dflash_block_attn", AttnArgs),
-                     ("dflash_spec_verify", VerifyArgs)):
+                     ("dflash_spec_verify", VerifyArgs), ("dflash_draft_qkv", QkvArgs),
+                     ("dflash_draft_mlp", MlpArgs)):
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.POINTER(st), _P, ctypes.c_size_t, _P]
-    for kind, st in enumerate((FuseArgs, AttnArgs, VerifyArgs)):
+    lib.dflash_draft_embed.restype = ctypes.c_int
+    lib.dflash_draft_embed.argtypes = [ctypes.POINTER(EmbedArgs), _P]
+    for kind, st in enumerate(ARG_STRUCTS):
         got = lib.dflash_args_size(kind)
         if got != ctypes.sizeof(st):
             raise DFlashError(-101, f"struct mirror {st.__name__} is {ctypes.sizeof(st)} bytes, library has {got}")
@@ -316,5 +341,139 @@ def prepare_spec_verify(target_logits, draft_logits, draft_tokens, temperature, 
 
 def spec_verify(*args, stream=None, **kw):
     prep = prepare_spec_verify(*args, **kw)
+    prep(stream)
+    return prep.outputs
+
+
+# ---------------------------------------------------------------- draft layer
+class PreparedEmbed:
+    """dflash_draft_embed has no workspace."""
+
+    def __init__(self, args, keep):
+        self.args, self._keep = args, keep
+
+    def __call__(self, stream=None):
+        _check(load().dflash_draft_embed(ctypes.byref(self.args), _stream(stream)))
+
+
+def prepare_draft_embed(emb, anchor, mask_id, x=None):
+    """Block input of the first draft layer (include/dflash.h, dflash_draft_embed).
+
+    emb [V, 2560]; anchor int32 [B]; x [B, 8, 2560] (allocated if None).
+    """
+    load()
+    dt = emb.dtype
+    _need(emb, "emb", dt)
+    if emb.dim() != 2 or emb.shape[1] != D:
+        raise DFlashError(-1, "emb must be [V, 2560]")
+    B = anchor.shape[0]
+    _need(anchor, "anchor", torch.int32, (B,))
+    if x is None:
+        x = torch.empty((B, BLOCK, D), dtype=dt, device=emb.device)
+    _need(x, "x", dt, (B, BLOCK, D))
+    a = EmbedArgs()
+    a.dtype, a.B, a.V = _dtype_code(emb), B, emb.shape[0]
+    a.emb, a.anchor, a.mask_id, a.x = emb.data_ptr(), anchor.data_ptr(), int(mask_id), x.data_ptr()
+    prep = PreparedEmbed(a, (emb, anchor, x))
+    prep.out = x
+    return prep
+
+
+def draft_embed(*args, stream=None, **kw):
+    prep = prepare_draft_embed(*args, **kw)
+    prep(stream)
+    return prep.out
+
+
+def prepare_draft_qkv(x, g_in, w_qkv, q=None, k_blk=None, v_blk=None, eps=1e-6, workspace=None):
+    """Input RMSNorm + fused Q/K/V projection (include/dflash.h, dflash_draft_qkv).
+
+    x [B, 8, 2560]; g_in [2560]; w_qkv [6144, 2560].  Outputs q [B,32,8,128],
+    k_blk and v_blk [B,8,8,128] (allocated if None), the inputs of block_attn.
+    """
+    lib = load()
+    dt = x.dtype
+    B = x.shape[0]
+    _need(x, "x", dt, (B, BLOCK, D))
+    _need(g_in, "g_in", dt, (D,))
+    _need(w_qkv, "w_qkv", dt, ((HQ + 2 * HKV) * HEAD_DIM, D))
+    dev = x.device
+    if q is None:
+        q = torch.empty((B, HQ, BLOCK, HEAD_DIM), dtype=dt, device=dev)
+    if k_blk is None:
+        k_blk = torch.empty((B, HKV, BLOCK, HEAD_DIM), dtype=dt, device=dev)
+    if v_blk is None:
+        v_blk = torch.empty((B, HKV, BLOCK, HEAD_DIM), dtype=dt, device=dev)
+    _need(q, "q", dt, (B, HQ, BLOCK, HEAD_DIM))
+    _need(k_blk, "k_blk", dt, (B, HKV, BLOCK, HEAD_DIM))
+    _need(v_blk, "v_blk", dt, (B, HKV, BLOCK, HEAD_DIM))
+    a = QkvArgs()
+    a.dtype, a.B = _dtype_code(x), B
+    a.x, a.g_in, a.w_qkv, a.eps = x.data_ptr(), g_in.data_ptr(), w_qkv.data_ptr(), eps
+    a.q, a.k_blk, a.v_blk = q.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr()
+    nbytes = ctypes.c_size_t()
+    _check(lib.dflash_draft_qkv_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
+    ws, wsb = _workspace(nbytes.value, workspace, dev)
+    prep = Prepared(lib.dflash_draft_qkv, a, ws, wsb, (x, g_in, w_qkv, q, k_blk, v_blk))
+    prep.outputs = (q, k_blk, v_blk)
+    return prep
+
+
+def draft_qkv(*args, stream=None, **kw):
+    prep = prepare_draft_qkv(*args, **kw)
+    prep(stream)
+    return prep.outputs
+
+
+def prepare_draft_mlp(x, o, w_o, g_post, w_gu, w_d, g_final=None, x_out=None, y_out=None, h_out=None, eps=1e-6,
+                      workspace=None):
+    """Output projection + residual, RMSNorm, SwiGLU MLP + residual and the
+    optional final RMSNorm (include/dflash.h, dflash_draft_mlp).
+
+    x [B, 8, 2560] layer input; o [B, 32, 8, 128] attention output;
+    w_o [2560, 4096]; g_post [2560]; w_gu [10240, 2560]; w_d [2560, 5120];
+    g_final [2560] or None.  Outputs x_out (may be x), with g_final y_out,
+    and the stored residual h in h_out when that is given.
+    """
+    lib = load()
+    dt = x.dtype
+    B = x.shape[0]
+    _need(x, "x", dt, (B, BLOCK, D))
+    _need(o, "o", dt, (B, HQ, BLOCK, HEAD_DIM))
+    _need(w_o, "w_o", dt, (D, HQ * HEAD_DIM))
+    _need(g_post, "g_post", dt, (D,))
+    _need(w_gu, "w_gu", dt, (2 * INTER, D))
+    _need(w_d, "w_d", dt, (D, INTER))
+    dev = x.device
+    if x_out is None:
+        x_out = torch.empty((B, BLOCK, D), dtype=dt, device=dev)
+    _need(x_out, "x_out", dt, (B, BLOCK, D))
+    if g_final is not None:
+        _need(g_final, "g_final", dt, (D,))
+        if y_out is None:
+            y_out = torch.empty((B, BLOCK, D), dtype=dt, device=dev)
+        _need(y_out, "y_out", dt, (B, BLOCK, D))
+    if h_out is not None:
+        _need(h_out, "h_out", dt, (B, BLOCK, D))
+    a = MlpArgs()
+    a.dtype, a.B = _dtype_code(x), B
+    a.x, a.o, a.w_o, a.g_post = x.data_ptr(), o.data_ptr(), w_o.data_ptr(), g_post.data_ptr()
+    a.w_gu, a.w_d = w_gu.data_ptr(), w_d.data_ptr()
+    a.g_final = None if g_final is None else g_final.data_ptr()
+    a.eps = eps
+    a.x_out = x_out.data_ptr()
+    a.y_out = None if y_out is None else y_out.data_ptr()
+    a.h_out = None if h_out is None else h_out.data_ptr()
+    nbytes = ctypes.c_size_t()
+    _check(lib.dflash_draft_mlp_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
+    ws, wsb = _workspace(nbytes.value, workspace, dev)
+    prep = Prepared(lib.dflash_draft_mlp, a, ws, wsb,
+                    (x, o, w_o, g_post, w_gu, w_d, g_final, x_out, y_out, h_out))
+    prep.outputs = (x_out, y_out, h_out)
+    return prep
+
+
+def draft_mlp(*args, stream=None, **kw):
+    prep = prepare_draft_mlp(*args, **kw)
     prep(stream)
     return prep.outputs

@@ -93,6 +93,23 @@ int validate_verify_sizes(const char* fn, const dflash_verify_args* a) {
     return DFLASH_OK;
 }
 
+int validate_draft_b(const char* fn, int dtype, int B) {
+    int rc = check_dtype(fn, dtype);
+    if (rc) return rc;
+    if (B < 1 || B > 8192) return fail(DFLASH_EINVAL, "%s: B %d outside [1, 8192]", fn, B);
+    return DFLASH_OK;
+}
+
+int validate_qkv_sizes(const char* fn, const dflash_qkv_args* a) {
+    if (!a) return fail(DFLASH_EINVAL, "%s: null args", fn);
+    return validate_draft_b(fn, a->dtype, a->B);
+}
+
+int validate_mlp_sizes(const char* fn, const dflash_mlp_args* a) {
+    if (!a) return fail(DFLASH_EINVAL, "%s: null args", fn);
+    return validate_draft_b(fn, a->dtype, a->B);
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,6 +123,9 @@ size_t dflash_args_size(int kind) {
         case 0: return sizeof(dflash_fuse_args);
         case 1: return sizeof(dflash_attn_args);
         case 2: return sizeof(dflash_verify_args);
+        case 3: return sizeof(dflash_embed_args);
+        case 4: return sizeof(dflash_qkv_args);
+        case 5: return sizeof(dflash_mlp_args);
         default: return 0;
     }
 }
@@ -134,6 +154,24 @@ int dflash_verify_workspace_size(const dflash_verify_args* a, size_t* bytes) {
     int rc = validate_verify_sizes(fn, a);
     if (rc) return rc;
     *bytes = dflash::verify_workspace_bytes(a->B, a->V);
+    return ok();
+}
+
+int dflash_draft_qkv_workspace_size(const dflash_qkv_args* a, size_t* bytes) {
+    const char* fn = "dflash_draft_qkv_workspace_size";
+    if (!bytes) return fail(DFLASH_EINVAL, "%s: null output", fn);
+    int rc = validate_qkv_sizes(fn, a);
+    if (rc) return rc;
+    *bytes = dflash::draft_qkv_plan(*a).ws_bytes;
+    return ok();
+}
+
+int dflash_draft_mlp_workspace_size(const dflash_mlp_args* a, size_t* bytes) {
+    const char* fn = "dflash_draft_mlp_workspace_size";
+    if (!bytes) return fail(DFLASH_EINVAL, "%s: null output", fn);
+    int rc = validate_mlp_sizes(fn, a);
+    if (rc) return rc;
+    *bytes = dflash::draft_mlp_plan(*a).ws_bytes;
     return ok();
 }
 
@@ -212,6 +250,60 @@ int dflash_spec_verify(const dflash_verify_args* a, void* ws, size_t ws_bytes, v
     rc = check_ws(fn, need, ws, ws_bytes);
     if (rc) return rc;
     return launched(fn, dflash::launch_verify(*a, ws, static_cast<hipStream_t>(stream)));
+}
+
+int dflash_draft_embed(const dflash_embed_args* a, void* stream) {
+    const char* fn = "dflash_draft_embed";
+    if (!a) return fail(DFLASH_EINVAL, "%s: null args", fn);
+    int rc = validate_draft_b(fn, a->dtype, a->B);
+    if (rc) return rc;
+    if (a->V < 1 || a->V > INT_MAX) return fail(DFLASH_EINVAL, "%s: V %lld outside [1, 2^31)", fn, (long long)a->V);
+    if (a->mask_id < 0 || a->mask_id >= a->V)
+        return fail(DFLASH_EINVAL, "%s: mask_id %d outside [0, V)", fn, a->mask_id);
+    REQUIRE_PTR(a->emb);
+    REQUIRE_PTR(a->anchor);
+    REQUIRE_PTR(a->x);
+    return launched(fn, dflash::launch_embed(*a, static_cast<hipStream_t>(stream)));
+}
+
+int dflash_draft_qkv(const dflash_qkv_args* a, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "dflash_draft_qkv";
+    int rc = validate_qkv_sizes(fn, a);
+    if (rc) return rc;
+    REQUIRE_PTR(a->x);
+    REQUIRE_PTR(a->g_in);
+    REQUIRE_PTR(a->w_qkv);
+    REQUIRE_PTR(a->q);
+    REQUIRE_PTR(a->k_blk);
+    REQUIRE_PTR(a->v_blk);
+    if (!(a->eps > 0.f)) return fail(DFLASH_EINVAL, "%s: eps must be > 0", fn);
+    const dflash::DraftQkvPlan pl = dflash::draft_qkv_plan(*a);
+    rc = check_ws(fn, pl.ws_bytes, ws, ws_bytes);
+    if (rc) return rc;
+    return launched(fn, dflash::launch_draft_qkv(*a, pl, ws, static_cast<hipStream_t>(stream)));
+}
+
+int dflash_draft_mlp(const dflash_mlp_args* a, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "dflash_draft_mlp";
+    int rc = validate_mlp_sizes(fn, a);
+    if (rc) return rc;
+    REQUIRE_PTR(a->x);
+    REQUIRE_PTR(a->o);
+    REQUIRE_PTR(a->w_o);
+    REQUIRE_PTR(a->g_post);
+    REQUIRE_PTR(a->w_gu);
+    REQUIRE_PTR(a->w_d);
+    REQUIRE_PTR(a->x_out);
+    if (a->g_final) {
+        if (!aligned16(a->g_final)) return fail(DFLASH_EINVAL, "%s: g_final is not 16-byte aligned", fn);
+        REQUIRE_PTR(a->y_out);
+    }
+    if (a->h_out && !aligned16(a->h_out)) return fail(DFLASH_EINVAL, "%s: h_out is not 16-byte aligned", fn);
+    if (!(a->eps > 0.f)) return fail(DFLASH_EINVAL, "%s: eps must be > 0", fn);
+    const dflash::DraftMlpPlan pl = dflash::draft_mlp_plan(*a);
+    rc = check_ws(fn, pl.ws_bytes, ws, ws_bytes);
+    if (rc) return rc;
+    return launched(fn, dflash::launch_draft_mlp(*a, pl, ws, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -1,0 +1,66 @@
+// Split-K bf16 GEMM and plain fp32 GEMM (gfx950), shared by the context
+// fusion and the draft-layer paths.  Both compute fp32 partial products
+//   part[s][m][n] = sum over k in split s of A[m][k] * B[n][k]
+// with A given as up to five column segments (columns [s*seg_w, (s+1)*seg_w)
+// of A come from aseg[s], rows a_stride elements apart) and B [N][K]
+// row-major; the caller sums the ks partials in its epilogue.
+#pragma once
+
+#include "kernels.h"
+
+namespace dflash {
+
+constexpr int kGemmXcds = 8;      // XCDs of the part; tiles are laid out contiguously per XCD
+constexpr int kGemmGroupM = 8;    // M tiles per group sharing one B panel
+constexpr int kGemmMaxKs = 16;    // largest split-K factor (epilogues unroll to it)
+
+struct GemmParams {
+    const void* aseg[5];  // A segments: columns [s*seg_w, (s+1)*seg_w) come from aseg[s]
+    int64_t a_stride;     // elements between A rows
+    int seg_w;
+    const void* b;        // [N][K] row-major
+    int M, N, K;
+    int ks, kt_per_split;
+    float* part;          // [ks][M][N]
+};
+
+// Tile id for this workgroup: XCD-contiguous ranges, then 8-row M groups.
+struct TileId { int tm, tn, ks; bool valid; };
+__device__ __forceinline__ TileId tile_id(const GemmParams& p, int tiles_m, int tiles_n) {
+    const int total = tiles_m * tiles_n * p.ks;
+    const int nblk = gridDim.x;  // padded to a multiple of kGemmXcds
+    const int bid = blockIdx.x;
+    const int per_xcd = nblk / kGemmXcds;
+    const int L = (bid % kGemmXcds) * per_xcd + bid / kGemmXcds;
+    TileId t;
+    t.valid = L < total;
+    const int per_split = tiles_m * tiles_n;
+    t.ks = L / per_split;
+    const int r = L % per_split;
+    const int in_group = kGemmGroupM * tiles_n;
+    const int grp = r / in_group;
+    const int first_m = grp * kGemmGroupM;
+    const int gm = min(tiles_m - first_m, kGemmGroupM);
+    const int q = r % in_group;
+    t.tm = first_m + q % gm;
+    t.tn = q / gm;
+    return t;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Split-K factor for the bf16 kernel: one residency round (two workgroups per
+// CU on 256 CUs), at least 8 k-tiles per split, at most kGemmMaxKs, and every
+// split owns at least one k-tile.
+int gemm_split(int M, int N, int K);
+// Sets g.ks and g.kt_per_split for this dtype (the fp32 kernel ignores them
+// and needs ks = 1).
+void gemm_set_split(GemmParams& g, int dtype, int ks);
+// bf16: 128x128 tiles, N % 128 == 0, K and seg_w multiples of 32, 16-byte
+// aligned rows; fp32: 64x64 tiles, N % 64 == 0, K and seg_w multiples of 16.
+hipError_t launch_gemm(const GemmParams& g, int dtype, hipStream_t s);
+
+}  // namespace dflash

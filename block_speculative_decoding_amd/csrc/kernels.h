@@ -31,4 +31,19 @@ struct FusePlan {
 FusePlan fuse_plan(const dflash_fuse_args& a);
 hipError_t launch_fuse(const dflash_fuse_args& a, const FusePlan& plan, void* ws, hipStream_t s);
 
+// ---- draft layer around block attention ----
+hipError_t launch_embed(const dflash_embed_args& a, hipStream_t s);
+struct DraftQkvPlan {
+    int ks;                      // split-K factor of the Q/K/V GEMM
+    size_t off_a, off_part, ws_bytes;
+};
+DraftQkvPlan draft_qkv_plan(const dflash_qkv_args& a);
+hipError_t launch_draft_qkv(const dflash_qkv_args& a, const DraftQkvPlan& plan, void* ws, hipStream_t s);
+struct DraftMlpPlan {
+    int ks_o, ks_gu, ks_d;       // split-K factors of the three GEMMs
+    size_t off_ao, off_part, off_h, off_c, off_s, ws_bytes;
+};
+DraftMlpPlan draft_mlp_plan(const dflash_mlp_args& a);
+hipError_t launch_draft_mlp(const dflash_mlp_args& a, const DraftMlpPlan& plan, void* ws, hipStream_t s);
+
 }  // namespace dflash

@@ -6,7 +6,7 @@ of the method's arithmetic.  Every generator is keyed by (seed, tensor name),
 so tensors do not shift when shapes elsewhere change.
 
 Distributions follow the workload descriptions: hidden states N(0, 1);
-weights N(0, 0.02^2); norm gains 1 + 0.1 N(0, 1); block Q/K/V and cache
+weights N(0, 0.02^2); norm gains 1 + 0.1 N(0, 1); embeddings, block Q/K/V and cache
 contents N(0, 1); target logits N(0, sigma^2) and draft logits = target
 logits + N(0, noise^2).  Cache pages are physically shuffled.
 """
@@ -15,7 +15,7 @@ import zlib
 
 import numpy as np
 
-D, NCAPTURE, HQ, HKV, HEAD_DIM, BLOCK, PAGE = 2560, 5, 32, 8, 128, 8, 16
+D, NCAPTURE, HQ, HKV, HEAD_DIM, BLOCK, PAGE, INTER = 2560, 5, 32, 8, 128, 8, 16, 5120
 
 
 def gen(seed, name):
@@ -84,6 +84,35 @@ def ragged_lengths(seed, B, lo, hi):
 def new_rows(seed, B, lo=1, hi=8):
     """Newly verified rows per sequence, uniform on [lo, hi]."""
     return gen(seed, "new_rows").integers(lo, hi + 1, size=B).astype(np.int32)
+
+
+def draft_layer_weights(seed, layer=0):
+    """One draft layer around attention: g_in [2560], W_QKV [6144, 2560],
+    W_O [2560, 4096], g_post [2560], W_GU [10240, 2560], W_D [2560, 5120]."""
+    t = f"L{layer}"
+    return {
+        "g_in": normal(seed, "g_in" + t, (D,), std=0.1, mean=1.0),
+        "w_qkv": normal(seed, "w_qkv" + t, ((HQ + 2 * HKV) * HEAD_DIM, D), std=0.02),
+        "w_o": normal(seed, "w_o" + t, (D, HQ * HEAD_DIM), std=0.02),
+        "g_post": normal(seed, "g_post" + t, (D,), std=0.1, mean=1.0),
+        "w_gu": normal(seed, "w_gu" + t, (2 * INTER, D), std=0.02),
+        "w_d": normal(seed, "w_d" + t, (D, INTER), std=0.02),
+    }
+
+
+def final_norm(seed):
+    """Final RMSNorm gain [2560] after the last draft layer."""
+    return normal(seed, "g_final", (D,), std=0.1, mean=1.0)
+
+
+def embedding(seed, V):
+    """Shared embedding table [V, 2560] ~ N(0, 1)."""
+    return normal(seed, "emb", (V, D))
+
+
+def anchors(seed, B, V):
+    """Last verified token of each sequence, uniform on [0, V)."""
+    return gen(seed, "anchors").integers(0, V, size=B).astype(np.int32)
 
 
 def logits(seed, B, V, sigma, noise):

@@ -1,11 +1,19 @@
 /*
  * dflash.h -- C ABI of the DFlash draft-verify hot path on AMD MI355X (gfx950).
  *
- * Three operations, each one call on a caller-supplied HIP stream:
+ * Three operations of the draft-verify hot path, each one call on a
+ * caller-supplied HIP stream:
  *
  *   dflash_ctx_fuse    context fusion + K/V injection into the draft caches
  *   dflash_block_attn  one draft layer's non-causal attention for the 8-token block
  *   dflash_spec_verify exact speculative verification of the 7 proposals
+ *
+ * and the rest of a draft layer around block attention:
+ *
+ *   dflash_draft_embed anchor + mask embeddings: the first layer's block input
+ *   dflash_draft_qkv   input RMSNorm + fused Q/K/V projection of the block
+ *   dflash_draft_mlp   output projection + residual, RMSNorm, SwiGLU MLP +
+ *                      residual, optional final RMSNorm
  *
  * Sources (web pages; cited by title and section):
  *   [E4B] "Nemotron 3.5 Bolt E4B: Block-Parallel Speculation with DFlash"
@@ -78,8 +86,9 @@ extern "C" {
 #define DFLASH_BLOCK      8      /* 1 anchor + 7 mask positions */
 #define DFLASH_PAGE       16     /* tokens per cache page */
 #define DFLASH_MAX_LAYERS 5      /* draft layers */
+#define DFLASH_INTER      5120   /* SwiGLU width (derived from the parameter count) */
 
-#define DFLASH_VERSION 10000     /* 1.0.0 */
+#define DFLASH_VERSION 10100     /* 1.1.0 */
 
 /*
  * dflash_ctx_fuse -- context fusion and K/V injection.
@@ -201,6 +210,81 @@ typedef struct dflash_verify_args {
     unsigned long long* near_ties; /* device [1]; incremented, never cleared */
 } dflash_verify_args;
 
+/*
+ * dflash_draft_embed -- block input of the first draft layer.
+ * [E4B] "The released serving cycle" (the block is one real anchor followed
+ * by seven mask tokens) and [DF2] 4.2 (input representations come from the
+ * target's embedding table, shared with the drafter).
+ *   x[b][0] = emb[anchor[b]],  x[b][j] = emb[mask_id] for j = 1..7
+ * An anchor id outside [0, V) gives a zero row.
+ */
+typedef struct dflash_embed_args {
+    int32_t dtype;            /* DFLASH_BF16 or DFLASH_F32 */
+    int32_t B;                /* sequences, 1..8192 */
+    int64_t V;                /* rows of emb, >= 1 */
+    const void* emb;          /* device [V][2560] embedding table */
+    const int32_t* anchor;    /* device [B] last verified token per sequence */
+    int32_t mask_id;          /* mask token id, in [0, V) */
+    void* x;                  /* device [B][8][2560] (dtype), copied rows */
+} dflash_embed_args;
+
+/*
+ * dflash_draft_qkv -- input RMSNorm and fused Q/K/V projection of one draft
+ * layer's block.  [DF2] 4.1 (Q_i = W_i^Q H_d; the H_d halves of K_i, V_i) and
+ * [E4B] "Five target states become persistent draft context" (Q [B,32,8,128],
+ * block K/V [B,8,8,128]); the pre-norm layer is the reading of the drafter as
+ * "Qwen3-style" ([E4B], opening section).
+ *   a = g_in * x / sqrt(mean(x^2) + eps)                        (stored in dtype)
+ *   y = a . w_qkv^T                                             (6144 columns)
+ *   q[b][h][j][d] = y[8b+j][128h+d],  k_blk[b][g][j][d] = y[8b+j][4096+128g+d],
+ *   v_blk[b][g][j][d] = y[8b+j][5120+128g+d]                     (rounded to dtype)
+ * The outputs are the inputs of dflash_block_attn (before its Q/K norm and
+ * RoPE).  Outputs must not overlap x.
+ */
+typedef struct dflash_qkv_args {
+    int32_t dtype;            /* DFLASH_BF16 or DFLASH_F32 */
+    int32_t B;                /* sequences, 1..8192 */
+    const void* x;            /* device [B][8][2560] layer input */
+    const void* g_in;         /* device [2560] input-norm weight */
+    const void* w_qkv;        /* device [6144][2560] row-major (out, in): W_Q | W_K | W_V */
+    float eps;                /* RMSNorm epsilon (> 0) */
+    void* q;                  /* device [B][32][8][128] */
+    void* k_blk;              /* device [B][8][8][128] */
+    void* v_blk;              /* device [B][8][8][128] */
+} dflash_qkv_args;
+
+/*
+ * dflash_draft_mlp -- the layer after block attention: output projection and
+ * residual, post-attention RMSNorm, SwiGLU MLP and residual, and (after the
+ * last layer) the final RMSNorm.  Same reading and sources as
+ * dflash_draft_qkv; [E4B] "The parameter count exposes the real cost" fixes
+ * the shapes (intermediate width 5120, derived).
+ *   o'[8b+j][128h+d] = o[b][h][j][d]
+ *   h  = x + o' . w_o^T                                          (stored)
+ *   c  = g_post * h / sqrt(mean(h^2) + eps)                      (stored)
+ *   s  = silu(c . w_gu[0:5120]^T) * (c . w_gu[5120:10240]^T)     (stored)
+ *   x_out = h + s . w_d^T                                        (rounded to dtype)
+ *   y  = g_final * x_out / sqrt(mean(x_out^2) + eps)  when g_final != NULL
+ * Every "stored" value is rounded to dtype once and the next step reads the
+ * rounded value.  x_out may be x itself (in place); y_out and h_out must not
+ * overlap x, o, x_out or each other.
+ */
+typedef struct dflash_mlp_args {
+    int32_t dtype;            /* DFLASH_BF16 or DFLASH_F32 */
+    int32_t B;                /* sequences, 1..8192 */
+    const void* x;            /* device [B][8][2560] layer input (the residual) */
+    const void* o;            /* device [B][32][8][128] block attention output */
+    const void* w_o;          /* device [2560][4096] (out, in = 128*head + dim) */
+    const void* g_post;       /* device [2560] post-attention norm weight */
+    const void* w_gu;         /* device [10240][2560]: 5120 gate rows, then 5120 up rows */
+    const void* w_d;          /* device [2560][5120] */
+    const void* g_final;      /* optional device [2560] final-norm weight; NULL = no final norm */
+    float eps;                /* RMSNorm epsilon (> 0) */
+    void* x_out;              /* device [B][8][2560] layer output */
+    void* y_out;              /* device [B][8][2560] final-norm output; required iff g_final != NULL */
+    void* h_out;              /* optional device [B][8][2560] copy of h (dtype); NULL = not written */
+} dflash_mlp_args;
+
 /* Library version (DFLASH_VERSION of the build). */
 int dflash_version(void);
 
@@ -208,7 +292,8 @@ int dflash_version(void);
 const char* dflash_last_error(void);
 
 /* sizeof of the argument structs as compiled into the library:
- * kind 0 = dflash_fuse_args, 1 = dflash_attn_args, 2 = dflash_verify_args;
+ * kind 0 = dflash_fuse_args, 1 = dflash_attn_args, 2 = dflash_verify_args,
+ * 3 = dflash_embed_args, 4 = dflash_qkv_args, 5 = dflash_mlp_args;
  * returns 0 for any other kind.  Lets bindings check their struct mirrors. */
 size_t dflash_args_size(int kind);
 
@@ -217,6 +302,8 @@ size_t dflash_args_size(int kind);
 int dflash_fuse_workspace_size(const dflash_fuse_args* args, size_t* bytes);
 int dflash_attn_workspace_size(const dflash_attn_args* args, size_t* bytes);
 int dflash_verify_workspace_size(const dflash_verify_args* args, size_t* bytes);
+int dflash_draft_qkv_workspace_size(const dflash_qkv_args* args, size_t* bytes);
+int dflash_draft_mlp_workspace_size(const dflash_mlp_args* args, size_t* bytes);
 
 /* The three operations.  `workspace` must hold at least the size returned
  * above (it may be NULL when that size is 0); its contents are scratch. */
@@ -226,6 +313,14 @@ int dflash_block_attn(const dflash_attn_args* args, void* workspace,
                       size_t workspace_bytes, void* stream);
 int dflash_spec_verify(const dflash_verify_args* args, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/* The draft layer around block attention (dflash_draft_embed needs no
+ * workspace). */
+int dflash_draft_embed(const dflash_embed_args* args, void* stream);
+int dflash_draft_qkv(const dflash_qkv_args* args, void* workspace,
+                     size_t workspace_bytes, void* stream);
+int dflash_draft_mlp(const dflash_mlp_args* args, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

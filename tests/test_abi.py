@@ -31,12 +31,13 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(dflash_\w+)\s*\(", text, re.M)))
 
 
-def test_header_declares_the_three_operations():
+def test_header_declares_every_operation():
     fns = declared_functions()
     for f in ("dflash_ctx_fuse", "dflash_block_attn", "dflash_spec_verify",
               "dflash_fuse_workspace_size", "dflash_attn_workspace_size",
               "dflash_verify_workspace_size", "dflash_last_error", "dflash_version",
-              "dflash_args_size"):
+              "dflash_args_size", "dflash_draft_embed", "dflash_draft_qkv", "dflash_draft_mlp",
+              "dflash_draft_qkv_workspace_size", "dflash_draft_mlp_workspace_size"):
         assert f in fns
 
 
@@ -52,11 +53,10 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_struct_sizes_and_version(lib):
     from block_speculative_decoding_amd import _lib
-    assert lib.dflash_version() == 10000
-    assert lib.dflash_args_size(0) == ctypes.sizeof(_lib.FuseArgs)
-    assert lib.dflash_args_size(1) == ctypes.sizeof(_lib.AttnArgs)
-    assert lib.dflash_args_size(2) == ctypes.sizeof(_lib.VerifyArgs)
-    assert lib.dflash_args_size(3) == 0
+    assert lib.dflash_version() == 10100
+    for kind, st in enumerate(_lib.ARG_STRUCTS):
+        assert lib.dflash_args_size(kind) == ctypes.sizeof(st)
+    assert lib.dflash_args_size(len(_lib.ARG_STRUCTS)) == 0
 
 
 def test_page_layouts_are_permutations():
@@ -189,3 +189,65 @@ def test_binding_refuses_host_tensors(lib):
     z = torch.zeros((2, 8, 64), dtype=torch.bfloat16)
     with pytest.raises(dfl.DFlashError):
         dfl.spec_verify(z, z[:, :7], torch.zeros((2, 7), dtype=torch.int32), torch.zeros(2))
+
+
+def _qkv_args(**kw):
+    from block_speculative_decoding_amd import _lib
+    a = _lib.QkvArgs()
+    a.dtype, a.B, a.eps = 0, 64, 1e-6
+    a.x = a.g_in = a.w_qkv = a.q = a.k_blk = a.v_blk = FAKE
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _mlp_args(**kw):
+    from block_speculative_decoding_amd import _lib
+    a = _lib.MlpArgs()
+    a.dtype, a.B, a.eps = 0, 64, 1e-6
+    a.x = a.o = a.w_o = a.g_post = a.w_gu = a.w_d = a.x_out = FAKE
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _embed_args(**kw):
+    from block_speculative_decoding_amd import _lib
+    a = _lib.EmbedArgs()
+    a.dtype, a.B, a.V, a.mask_id = 0, 4, 1000, 999
+    a.emb = a.anchor = a.x = FAKE
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_draft_layer_validation(lib):
+    # Only calls that fail validation are made: nothing reaches the GPU.
+    rc, n = _ws(lib, "draft_qkv", _qkv_args())
+    assert rc == 0 and n > 0
+    assert _ws(lib, "draft_qkv", _qkv_args(B=0))[0] == -1
+    assert _ws(lib, "draft_qkv", _qkv_args(B=8193))[0] == -1
+    assert _ws(lib, "draft_qkv", _qkv_args(dtype=5))[0] == -2
+    assert _ws(lib, "draft_qkv", _qkv_args(B=128))[1] > n
+    assert _call(lib, "dflash_draft_qkv", _qkv_args(x=None), FAKE, n) == -1
+    assert _call(lib, "dflash_draft_qkv", _qkv_args(w_qkv=FAKE + 8), FAKE, n) == -1
+    assert _call(lib, "dflash_draft_qkv", _qkv_args(eps=0.0), FAKE, n) == -1
+    assert _call(lib, "dflash_draft_qkv", _qkv_args(), FAKE, n - 1) == -4
+
+    rc, m = _ws(lib, "draft_mlp", _mlp_args())
+    assert rc == 0 and m > 0
+    assert _ws(lib, "draft_mlp", _mlp_args(B=0))[0] == -1
+    assert _call(lib, "dflash_draft_mlp", _mlp_args(w_d=None), FAKE, m) == -1
+    assert _call(lib, "dflash_draft_mlp", _mlp_args(g_final=FAKE), FAKE, m) == -1  # y_out missing
+    assert b"y_out" in lib.dflash_last_error()
+    assert _call(lib, "dflash_draft_mlp", _mlp_args(), None, 0) == -4
+    assert _ws(lib, "draft_mlp", _mlp_args(dtype=1))[1] > 0
+
+    emb = lib.dflash_draft_embed
+    assert emb(ctypes.byref(_embed_args(mask_id=1000)), None) == -1
+    assert emb(ctypes.byref(_embed_args(mask_id=-1)), None) == -1
+    assert emb(ctypes.byref(_embed_args(V=0, mask_id=0)), None) == -1
+    assert emb(ctypes.byref(_embed_args(anchor=None)), None) == -1
+    assert emb(ctypes.byref(_embed_args(B=0)), None) == -1
+    assert emb(ctypes.byref(_embed_args(dtype=9)), None) == -2
+

@@ -38,7 +38,7 @@ from .philox import philox4x64_10, uniforms, gumbel
 from .ctx_fuse import ctx_fuse_ref, concat_capture
 from .block_attn import block_attn_ref, attend, prep_block
 from .spec_verify import spec_verify_ref, VerifyTrace
-from .draft_layer import embed_block, qkv_ref, mlp_ref, silu, layer_weight_shapes
+from .draft_layer import embed_block, qkv_ref, mlp_ref, o_proj_residual_ref, ffn_ref, silu, layer_weight_shapes
 
 __all__ = [
     "bf16_round", "rms_norm", "rope_rotate_half", "rope_angles",
@@ -46,5 +46,5 @@ __all__ = [
     "ctx_fuse_ref", "concat_capture",
     "block_attn_ref", "attend", "prep_block",
     "spec_verify_ref", "VerifyTrace",
-    "embed_block", "qkv_ref", "mlp_ref", "silu", "layer_weight_shapes",
+    "embed_block", "qkv_ref", "mlp_ref", "o_proj_residual_ref", "ffn_ref", "silu", "layer_weight_shapes",
 ]

@@ -100,31 +100,46 @@ def silu(x):
     return x / (1.0 + np.exp(-x))
 
 
-def mlp_ref(x, o, w_o, g_post, w_gu, w_d, eps=1e-6, g_final=None, bf16=True):
-    """Output projection + residual, post-attention RMSNorm, SwiGLU MLP +
-    residual, and (after the last layer) the final RMSNorm.
-
-    x: [B, 8, D] layer input (the residual); o: [B, hq, 8, hd] attention
-    output.  Returns a dict of float64 arrays, each unrounded, all [B*8, .]:
-    h, c, s (the SwiGLU product), x_out and, when g_final is given, y.
-    Each stage consumes the bf16-rounded value of the previous one in bf16
-    mode.
-    """
+def o_proj_residual_ref(x, o, w_o):
+    """h = x + o' W_O^T, o' row (b, j) = concatenation over query heads h of
+    o[b, h, j, :] (input index 128 h + d of W_O).  x: [B, 8, D] layer input;
+    o: [B, hq, 8, hd].  Returns h [B*8, D] float64, unrounded."""
     x = np.asarray(x, dtype=np.float64)
     o = np.asarray(o, dtype=np.float64)
     B, T, d = x.shape
     hq, hd = o.shape[1], o.shape[3]
-    # Row (b, j) of the attention output is the concatenation over query
-    # heads h of o[b, h, j, :] (input index 128 h + d of W_O).
     a_o = o.transpose(0, 2, 1, 3).reshape(B * T, hq * hd)
-    h = x.reshape(B * T, d) + a_o @ np.asarray(w_o, dtype=np.float64).T
-    h_s = _maybe_round(h, bf16)
+    return x.reshape(B * T, d) + a_o @ np.asarray(w_o, dtype=np.float64).T
+
+
+def ffn_ref(h_s, g_post, w_gu, w_d, eps=1e-6, g_final=None, bf16=True):
+    """From the stored residual h_s [M, D]: c = RMSNorm(h_s; g_post),
+    s = silu(c W_G^T) * (c W_U^T), x' = h_s + s W_D^T and, when g_final is
+    given, y = RMSNorm(x'; g_final).  Returns a dict of unrounded float64
+    arrays c, s, x_out (and y); each stage consumes the bf16-rounded value of
+    the previous one in bf16 mode."""
+    h_s = np.asarray(h_s, dtype=np.float64)
     c = rms_norm(h_s, g_post, eps)
     gu = _maybe_round(c, bf16) @ np.asarray(w_gu, dtype=np.float64).T
     inter = gu.shape[1] // 2
     s = silu(gu[:, :inter]) * gu[:, inter:]
     x_out = h_s + _maybe_round(s, bf16) @ np.asarray(w_d, dtype=np.float64).T
-    out = {"h": h, "c": c, "s": s, "x_out": x_out}
+    out = {"c": c, "s": s, "x_out": x_out}
     if g_final is not None:
         out["y"] = rms_norm(_maybe_round(x_out, bf16), g_final, eps)
+    return out
+
+
+def mlp_ref(x, o, w_o, g_post, w_gu, w_d, eps=1e-6, g_final=None, bf16=True):
+    """Output projection + residual, post-attention RMSNorm, SwiGLU MLP +
+    residual, and (after the last layer) the final RMSNorm: the composition
+    of o_proj_residual_ref and ffn_ref on the stored h.
+
+    x: [B, 8, D] layer input (the residual); o: [B, hq, 8, hd] attention
+    output.  Returns a dict of float64 arrays, each unrounded, all [B*8, .]:
+    h, c, s (the SwiGLU product), x_out and, when g_final is given, y.
+    """
+    h = o_proj_residual_ref(x, o, w_o)
+    out = ffn_ref(_maybe_round(h, bf16), g_post, w_gu, w_d, eps, g_final, bf16)
+    out["h"] = h
     return out

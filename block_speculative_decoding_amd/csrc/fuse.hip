@@ -63,30 +63,6 @@ constexpr int kBigStageBytes = 2 * BMB * kBigPitch;
 constexpr int kBigPartsA = BMB * 8 / kBigThreads;  // buffer loads per thread per stage and operand (4)
 __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) uint32_t* lds,
-                                                           int size, int voffset, int soffset, int offset,
-                                                           int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
-// Raw buffer descriptor: 48-bit base, stride 0, range in bytes.
-__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t a = (uint64_t)(uintptr_t)base;
-    i32x4 r;
-    r[0] = (int)(uint32_t)a;
-    r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);
-    r[2] = (int)bytes;
-    r[3] = 0x00020000;
-    return r;
-}
-template <int N>
-__device__ __forceinline__ void wait_lgkm() {
-    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
-}
-template <int OFF>
-__device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
-    bf16x8 r;
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-    return r;
-}
 
 struct KvEpilogue {
     const float2* cs;      // [M][64] (cos, sin) of pos[row] * inv_freq[i]

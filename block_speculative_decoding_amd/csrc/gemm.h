@@ -6,6 +6,7 @@
 // row-major; the caller sums the ks partials in its epilogue.
 #pragma once
 
+#include "device_common.h"
 #include "kernels.h"
 
 namespace dflash {
@@ -50,6 +51,39 @@ __device__ __forceinline__ TileId tile_id(const GemmParams& p, int tiles_m, int 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 16-byte LDS read into an MFMA operand register; issued as inline asm so
+// that the caller places the lgkmcnt waits (the compiler's own placement
+// drains every outstanding read before each matrix instruction).
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
+    bf16x8 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+
+// Buffer load of 16 bytes per lane written straight to LDS (lane l at the
+// M0 base + 16 l), through a raw buffer descriptor: bytes past the
+// descriptor's range read as zero.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) uint32_t* lds,
+                                                           int size, int voffset, int soffset, int offset,
+                                                           int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+// Raw buffer descriptor: 48-bit base, stride 0, range in bytes.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    i32x4 r;
+    r[0] = (int)(uint32_t)a;
+    r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);
+    r[2] = (int)bytes;
+    r[3] = 0x00020000;
+    return r;
 }
 
 // Split-K factor for the bf16 kernel: one residency round (two workgroups per

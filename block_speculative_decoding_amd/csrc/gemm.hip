@@ -1,7 +1,7 @@
 // Split-K bf16 GEMM and plain fp32 GEMM (gfx950); interface in gemm.h.
 //
 // The bf16 kernel runs the 32x32x16 bf16 matrix instruction on operands
-// staged through LDS by loads that write LDS directly; tiles are laid out
+// staged through LDS by buffer loads that write LDS directly; tiles are laid out
 // contiguously per XCD in 8-row groups so that tiles sharing a B panel run on
 // the same L2.  Used where the row count is a few hundred to a few thousand
 // (context fusion of newly verified rows, the draft layer's projections over
@@ -16,21 +16,19 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int BM = 128, BN = 128;
 
-// ---- bf16 GEMM: 128x128 tile, BK = 32, four-stage LDS ring filled by the
-// gfx950 direct global->LDS load (global_load_lds_dwordx4: lane l's 16 bytes
-// land at the wave's LDS base + 16 l).  A stage holds A and B as [128 rows][4
-// chunks of 8 bf16]; chunk c of row r sits at position 4r + (c ^ swz(r)), an
-// XOR pattern that keeps the 16-byte operand reads of 8 or 16 consecutive
-// rows on distinct banks.  The swizzle is applied to the global address each
-// lane fetches, because the LDS position is fixed by the lane index.
-constexpr int BKD = 32;                      // k per stage
-constexpr int kStages = 4;
-constexpr int kStageChunks = 2 * BM * 4;     // A then B, 16-byte chunks
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-
-__device__ __forceinline__ void dma16(const void* g, uint4* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
-}
+// ---- bf16 GEMM: 128x128 tile, BK = 64, four waves of 64x64 (2x2 blocks of
+// the 32x32x16 instruction), a two-stage LDS ring of 32 KiB stages (two
+// workgroups per CU).  A stage holds A then B as [128 rows][8 chunks of 16 B];
+// chunk c of row r sits at unit 8r + (c ^ swz8(r)), swz8(r) = (r >> 1) & 7.
+// Operands reach LDS through buffer loads that write LDS directly, with fixed
+// per-lane offsets; A rows past M read as zero (descriptor range).  The next
+// substep's operand reads are in flight while the current one multiplies
+// (inline-asm reads with explicit lgkmcnt waits), and the next stage's eight
+// loads per thread go out between the four MFMAs of the last substep.
+constexpr int BKD = 64;                      // k per stage (and per k-tile)
+constexpr int kUnits = 2 * BM * 8;           // A then B, 16-byte units per stage
+constexpr int kStageBytes = kUnits * 16;     // 32 KiB
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
 __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = p.N / BN;
@@ -42,39 +40,39 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
     if (kt0 >= kt1) return;
     const int nloc = kt1 - kt0;
 
-    __shared__ __attribute__((aligned(16))) uint4 lds[kStages * kStageChunks];
+    __shared__ __attribute__((aligned(1024))) uint4 lds[2 * kUnits];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m0 = t.tm * BM, n0 = t.tn * BN;
-    const uint16_t* bmat = static_cast<const uint16_t*>(p.b);
+    const uint16_t* bmat = static_cast<const uint16_t*>(p.b) + (int64_t)n0 * p.K;
+    const void *aseg0 = p.aseg[0], *aseg1 = p.aseg[1], *aseg2 = p.aseg[2], *aseg3 = p.aseg[3], *aseg4 = p.aseg[4];
+    const uint32_t arows = (uint32_t)min(p.M - m0, BM);
 
-    // Each thread issues 4 DMA chunks per stage at positions P = (j & 1) * 256 +
-    // tid of the A half (j = 0, 1) or the B half (j = 2, 3).  Rows past M
-    // read row M-1 (valid memory); their results are never stored.
-    int src_r[4], src_c[4];
+    // Load j (0..3) of a thread covers unit P = j * 256 + tid of the A (or B)
+    // half: row P >> 3, chunk (P & 7) ^ swz8(row).
+    uint32_t voa[4], vob[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int P = (j & 1) * 256 + tid;
-        src_r[j] = P >> 2;
-        src_c[j] = (P & 3) ^ swz(P >> 2);
+        const int P = j * kThreads + tid, r = P >> 3, c = (P & 7) ^ swz8(r);
+        voa[j] = (uint32_t)(r * (int)p.a_stride + 8 * c) * 2u;
+        vob[j] = (uint32_t)(r * p.K + 8 * c) * 2u;
     }
-    // The five segment pointers stay in registers: indexing p.aseg with a
-    // run-time segment is a scalar memory load whose wait would sit in front
-    // of every stage's loads.
-    const void *aseg0 = p.aseg[0], *aseg1 = p.aseg[1], *aseg2 = p.aseg[2], *aseg3 = p.aseg[3], *aseg4 = p.aseg[4];
-    auto issue = [&](int kt, int slot) {
+    auto load_part = [&](int kt, int slot, int part) {
         const int kg = kt * BKD;
-        const int seg = kg / p.seg_w;
-        const int kc = kg - seg * p.seg_w;
-        const uint16_t* a = static_cast<const uint16_t*>(
-            seg == 0 ? aseg0 : seg == 1 ? aseg1 : seg == 2 ? aseg2 : seg == 3 ? aseg3 : aseg4);
-        uint4* sbase = lds + slot * kStageChunks;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint16_t* g = j < 2 ? a + (int64_t)min(m0 + src_r[j], p.M - 1) * p.a_stride + kc + 8 * src_c[j]
-                                      : bmat + (int64_t)(n0 + src_r[j]) * p.K + kg + 8 * src_c[j];
-            // wave-uniform LDS base of this instruction
-            dma16(g, sbase + (j >> 1) * (BM * 4) + (j & 1) * 256 + wave * 64);
+        uint4* sb = lds + slot * kUnits + wave * 64;
+        if (part < 4) {
+            const int seg = kg / p.seg_w;
+            const int kc = kg - seg * p.seg_w;
+            const void* av = seg == 0 ? aseg0 : seg == 1 ? aseg1 : seg == 2 ? aseg2 : seg == 3 ? aseg3 : aseg4;
+            const uint16_t* a = static_cast<const uint16_t*>(av) + (int64_t)m0 * p.a_stride + kc;
+            const i32x4 rs = buffer_rsrc(a, arows * (uint32_t)p.a_stride * 2u - (uint32_t)kc * 2u);
+            llvm_amdgcn_raw_buffer_load_lds(rs, (__attribute__((address_space(3))) uint32_t*)(sb + part * kThreads), 16,
+                                            (int)voa[part], 0, 0, 0);
+        } else {
+            const int j = part - 4;
+            const i32x4 rs = buffer_rsrc(bmat + kg, (uint32_t)BN * (uint32_t)p.K * 2u - (uint32_t)kg * 2u);
+            llvm_amdgcn_raw_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) uint32_t*)(sb + BM * 8 + j * kThreads), 16, (int)vob[j], 0, 0, 0);
         }
     };
 
@@ -86,42 +84,70 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
 
     const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;
     const int lr = lane & 31, lh = lane >> 5;
-
-    // Prologue: stages 0..kStages-2 (clamped re-reads past the end are harmless).
+    // Rows wr + 32 i + lr (A) and wc + 32 j + lr (B) all have swizzle
+    // swz8(lr); substep s flips chunk bits 1-2 (address ^ 32 s), block 1 adds
+    // 32 rows (4096 bytes).
+    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint4*)lds);
+    const uint32_t a_lane = lds0 + 128u * (wr + lr) + 16u * (lh ^ swz8(lr));
+    const uint32_t b_lane = lds0 + 16u * BM * 8 + 128u * (wc + lr) + 16u * (lh ^ swz8(lr));
+    auto rd = [&](int slot, int ks, bf16x8* a, bf16x8* b) {
+        const uint32_t so = (uint32_t)slot * kStageBytes, x = 32u * ks;
+        const uint32_t aa = (a_lane + so) ^ x, bb = (b_lane + so) ^ x;
+        a[0] = lds_read16<0>(aa);
+        a[1] = lds_read16<4096>(aa);
+        b[0] = lds_read16<0>(bb);
+        b[1] = lds_read16<4096>(bb);
+    };
+    auto mm = [&](const bf16x8* a, const bf16x8* b) {
 #pragma unroll
-    for (int s0 = 0; s0 < kStages - 1; ++s0) issue(kt0 + min(s0, nloc - 1), s0);
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    };
 
+    bf16x8 fa[2][2], fb[2][2];
+#pragma unroll
+    for (int s0 = 0; s0 < 2; ++s0)
+#pragma unroll
+        for (int t2 = 0; t2 < 8; ++t2) load_part(kt0 + min(s0, nloc - 1), s0, t2);
+    wait_vm<8>();  // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    rd(0, 0, fa[0], fb[0]);
     for (int i = 0; i < nloc; ++i) {
-        wait_vm<4 * (kStages - 2)>();  // stage i landed; the two newer ones may be in flight
-        // Plain s_barrier: __syncthreads() would also drain every outstanding
-        // load.  A wave's reads of stage i-1 completed before its MFMAs ran.
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        issue(kt0 + min(i + kStages - 1, nloc - 1), (i + kStages - 1) % kStages);
-        const uint4* sa = lds + (i % kStages) * kStageChunks;
-        const uint4* sb = sa + BM * 4;
-        bf16x8 af[2][2], bfr[2][2];  // [k-step][block]: all operand reads first
+        const int slot = i & 1;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int ch = 2 * ks + lh;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int ra = wr + 32 * q + lr, rb = wc + 32 * q + lr;
-                af[ks][q] = __builtin_bit_cast(bf16x8, sa[4 * ra + (ch ^ swz(ra))]);
-                bfr[ks][q] = __builtin_bit_cast(bf16x8, sb[4 * rb + (ch ^ swz(rb))]);
-            }
+        for (int s = 0; s < 3; ++s) {
+            rd(slot, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+            wait_lgkm<4>();  // substep s's reads (issued before these 4) are back
+            __builtin_amdgcn_sched_barrier(0);
+            mm(fa[s & 1], fb[s & 1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        wait_lgkm<0>();
+        wait_vm<0>();                  // stage i+1 landed
+        __builtin_amdgcn_s_barrier();  // and every wave is done reading stage i
+        asm volatile("" ::: "memory");
+        rd(slot ^ 1, 0, fa[0], fb[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int kn = kt0 + min(i + 2, nloc - 1);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[q][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][q], bfr[ks][j], acc[q][j], 0, 0, 0);
+        for (int t2 = 0; t2 < 8; ++t2) {
+            if ((t2 & 1) == 0) {
+                const int q = t2 >> 1;
+                acc[q >> 1][q & 1] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][q >> 1], fb[1][q & 1], acc[q >> 1][q & 1], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            load_part(kn, slot, t2);  // stage i+2 into the slot stage i used
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     wait_vm<0>();  // the clamped trailing loads must land before the workgroup exits
+    wait_lgkm<0>();
 
-    // Lane holds column lr of each 32x32 block, rows 8*jj + 4*lh + r.
+    // Lane holds column lr of each 32x32 block, rows 8*(r/4) + 4*lh + (r%4).
     float* out = p.part + (int64_t)t.ks * p.M * p.N;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -176,7 +202,7 @@ int gemm_split(int M, int N, int K) {
     const int tiles = ((M + BM - 1) / BM) * (N / BN);
     const int nk = K / BKD;
     int ks = 512 / tiles;                 // 2 workgroups per CU on 256 CUs, one round
-    if (ks > nk / 8) ks = nk / 8;         // keep >= 8 k-tiles per split
+    if (ks > nk / 4) ks = nk / 4;         // keep >= 4 k-tiles (256 k) per split
     if (ks > kGemmMaxKs) ks = kGemmMaxKs;
     if (ks < 1) ks = 1;
     // Every split must own at least one k-tile: recount after rounding.

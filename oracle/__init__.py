@@ -27,6 +27,8 @@ Modules:
 * ``draft_layer`` -- the rest of a draft layer around block attention: block
                      embedding, input norm + fused Q/K/V projection, output
                      projection + residual, SwiGLU MLP, final norm.
+* ``window_cache`` -- the sliding-window draft cache as a ring of pages:
+                     capacity, append slots, wrapped block table.
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test
 against values printed on the pages, closed forms, invariants, brute force
@@ -39,6 +41,7 @@ from .ctx_fuse import ctx_fuse_ref, concat_capture
 from .block_attn import block_attn_ref, attend, prep_block
 from .spec_verify import spec_verify_ref, VerifyTrace
 from .draft_layer import embed_block, qkv_ref, mlp_ref, o_proj_residual_ref, ffn_ref, silu, layer_weight_shapes
+from .window_cache import ring_pages, ring_append, ring_block_table
 
 __all__ = [
     "bf16_round", "rms_norm", "rope_rotate_half", "rope_angles",
@@ -47,4 +50,5 @@ __all__ = [
     "block_attn_ref", "attend", "prep_block",
     "spec_verify_ref", "VerifyTrace",
     "embed_block", "qkv_ref", "mlp_ref", "o_proj_residual_ref", "ffn_ref", "silu", "layer_weight_shapes",
+    "ring_pages", "ring_append", "ring_block_table",
 ]

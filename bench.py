@@ -22,7 +22,8 @@ sequences of 131072 cached tokens on shuffled pages: 16 splits of each
 sequence and the log-sum-exp merge launch), and the serving batch's draft
 forward around block attention (block embedding, 5 x [input norm + Q/K/V
 projection, block attention, output projection + SwiGLU MLP], final norm),
-whole and its dense part alone.
+whole and its dense part alone, and one layer's attention restricted to the
+drafter's 1024-token window.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill] [--eager]
 """
@@ -55,7 +56,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the timings outside the serving cycle (prefill fusion, B=256 verify, "
-                         "long-context attention, draft forward)")
+                         "long-context and windowed attention, draft forward)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches only (default: also replay each step from a HIP graph)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -333,6 +334,21 @@ def long_context_measurement(torch, dfl, synth):
     return out
 
 
+def window_measurement(torch, dfl, wl):
+    """One layer's block attention at the serving batch restricted to the
+    latest 1024 cached tokens (the drafter's window)."""
+    W = 1024
+    blk = wl.blk_np[0]
+    d = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).to("cuda:0")
+    att = dfl.prepare_block_attn(d(blk["q"]), d(blk["k_blk"]), d(blk["v_blk"]), d(blk["gq"]), d(blk["gk"]),
+                                 wl.kc[0], wl.vc[0], wl.block_table, wl.ctx_len, window=W)
+    ms = timed(torch, att, warmup=3, reps=20)
+    nbytes = attn_bytes(np.minimum(wl.lens, W))
+    return {"window_attn_b64_w1024": {"ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                      "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                      "algorithmic_bytes": nbytes}}
+
+
 def draft_measurement(torch, dfl, synth, wl):
     """The serving batch's draft forward around block attention: the block
     embedding, then per layer the input norm + Q/K/V projection, block
@@ -511,6 +527,8 @@ def main():
         res["kernels"].update(prefill_measurements(torch, dfl, synth))
         log("[bench] long-context workload: block_attn B=4, S=131072")
         res["kernels"].update(long_context_measurement(torch, dfl, synth))
+        log("[bench] windowed attention: B=64, latest 1024 tokens")
+        res["kernels"].update(window_measurement(torch, dfl, wl))
         log("[bench] draft forward around attention: B=64, 5 layers")
         res["kernels"].update(draft_measurement(torch, dfl, synth, wl))
     if not args.no_cpu_baseline:

@@ -8,9 +8,11 @@ DFlashError if it has not been built.
 from ._lib import (DFlashError, load, ctx_fuse, block_attn, spec_verify,
                    prepare_ctx_fuse, prepare_block_attn, prepare_spec_verify,
                    draft_embed, draft_qkv, draft_mlp,
-                   prepare_draft_embed, prepare_draft_qkv, prepare_draft_mlp, EXPORTS)
+                   prepare_draft_embed, prepare_draft_qkv, prepare_draft_mlp,
+                   ring_append, prepare_ring_append, EXPORTS)
 
 __all__ = ["DFlashError", "load", "ctx_fuse", "block_attn", "spec_verify",
            "prepare_ctx_fuse", "prepare_block_attn", "prepare_spec_verify",
            "draft_embed", "draft_qkv", "draft_mlp",
-           "prepare_draft_embed", "prepare_draft_qkv", "prepare_draft_mlp", "EXPORTS"]
+           "prepare_draft_embed", "prepare_draft_qkv", "prepare_draft_mlp",
+           "ring_append", "prepare_ring_append", "EXPORTS"]

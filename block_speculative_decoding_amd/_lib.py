@@ -73,13 +73,18 @@ class MlpArgs(ctypes.Structure):
                 ("g_final", _P), ("eps", _F32), ("x_out", _P), ("y_out", _P), ("h_out", _P)]
 
 
-ARG_STRUCTS = (FuseArgs, AttnArgs, VerifyArgs, EmbedArgs, QkvArgs, MlpArgs)
+class RingArgs(ctypes.Structure):
+    _fields_ = [("B", _I32), ("ring_pages", _I32), ("ring", _P), ("ctx_len", _P), ("n_new", _P),
+                ("rows_per_seq", _I32), ("slot", _P), ("pos", _P)]
+
+
+ARG_STRUCTS = (FuseArgs, AttnArgs, VerifyArgs, EmbedArgs, QkvArgs, MlpArgs, RingArgs)
 
 EXPORTS = ["dflash_version", "dflash_last_error", "dflash_args_size",
            "dflash_fuse_workspace_size", "dflash_attn_workspace_size", "dflash_verify_workspace_size",
            "dflash_draft_qkv_workspace_size", "dflash_draft_mlp_workspace_size",
            "dflash_ctx_fuse", "dflash_block_attn", "dflash_spec_verify",
-           "dflash_draft_embed", "dflash_draft_qkv", "dflash_draft_mlp"]
+           "dflash_draft_embed", "dflash_draft_qkv", "dflash_draft_mlp", "dflash_ring_append"]
 
 _lib = None
 
@@ -109,6 +114,8 @@ def load():
         f.argtypes = [ctypes.POINTER(st), _P, ctypes.c_size_t, _P]
     lib.dflash_draft_embed.restype = ctypes.c_int
     lib.dflash_draft_embed.argtypes = [ctypes.POINTER(EmbedArgs), _P]
+    lib.dflash_ring_append.restype = ctypes.c_int
+    lib.dflash_ring_append.argtypes = [ctypes.POINTER(RingArgs), _P]
     for kind, st in enumerate(ARG_STRUCTS):
         got = lib.dflash_args_size(kind)
         if got != ctypes.sizeof(st):
@@ -477,3 +484,50 @@ def draft_mlp(*args, stream=None, **kw):
     prep = prepare_draft_mlp(*args, **kw)
     prep(stream)
     return prep.outputs
+
+
+# ---------------------------------------------------------------- window cache
+class PreparedRing:
+    """dflash_ring_append has no workspace."""
+
+    def __init__(self, args, keep):
+        self.args, self._keep = args, keep
+
+    def __call__(self, stream=None):
+        _check(load().dflash_ring_append(ctypes.byref(self.args), _stream(stream)))
+
+
+def prepare_ring_append(ring, ctx_len, n_new, rows_per_seq=8, slot=None, pos=None):
+    """Slots and positions of a cycle's verified rows in a sliding-window
+    cache kept as a ring of pages (include/dflash.h, dflash_ring_append).
+
+    ring int32 [B, R]; ctx_len int32 [B] (advanced in place); n_new int32
+    [B].  Outputs slot int64 and pos int32 [B * rows_per_seq] (allocated if
+    None), the slot / pos inputs of ctx_fuse.
+    """
+    load()
+    B, R = ring.shape
+    _need(ring, "ring", torch.int32, (B, R))
+    _need(ctx_len, "ctx_len", torch.int32, (B,))
+    _need(n_new, "n_new", torch.int32, (B,))
+    dev = ring.device
+    if slot is None:
+        slot = torch.empty((B * rows_per_seq,), dtype=torch.int64, device=dev)
+    if pos is None:
+        pos = torch.empty((B * rows_per_seq,), dtype=torch.int32, device=dev)
+    _need(slot, "slot", torch.int64, (B * rows_per_seq,))
+    _need(pos, "pos", torch.int32, (B * rows_per_seq,))
+    a = RingArgs()
+    a.B, a.ring_pages, a.rows_per_seq = B, R, rows_per_seq
+    a.ring, a.ctx_len, a.n_new = ring.data_ptr(), ctx_len.data_ptr(), n_new.data_ptr()
+    a.slot, a.pos = slot.data_ptr(), pos.data_ptr()
+    prep = PreparedRing(a, (ring, ctx_len, n_new, slot, pos))
+    prep.outputs = (slot, pos)
+    return prep
+
+
+def ring_append(*args, stream=None, **kw):
+    prep = prepare_ring_append(*args, **kw)
+    prep(stream)
+    return prep.outputs
+

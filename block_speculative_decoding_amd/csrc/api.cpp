@@ -126,6 +126,7 @@ size_t dflash_args_size(int kind) {
         case 3: return sizeof(dflash_embed_args);
         case 4: return sizeof(dflash_qkv_args);
         case 5: return sizeof(dflash_mlp_args);
+        case 6: return sizeof(dflash_ring_args);
         default: return 0;
     }
 }
@@ -304,6 +305,18 @@ int dflash_draft_mlp(const dflash_mlp_args* a, void* ws, size_t ws_bytes, void* 
     rc = check_ws(fn, pl.ws_bytes, ws, ws_bytes);
     if (rc) return rc;
     return launched(fn, dflash::launch_draft_mlp(*a, pl, ws, static_cast<hipStream_t>(stream)));
+}
+
+int dflash_ring_append(const dflash_ring_args* a, void* stream) {
+    const char* fn = "dflash_ring_append";
+    if (!a) return fail(DFLASH_EINVAL, "%s: null args", fn);
+    if (a->B < 1 || a->B > 65535) return fail(DFLASH_EINVAL, "%s: B %d outside [1, 65535]", fn, a->B);
+    if (a->ring_pages < 1) return fail(DFLASH_EINVAL, "%s: ring_pages must be >= 1", fn);
+    if (a->rows_per_seq < 1 || a->rows_per_seq > 64)
+        return fail(DFLASH_EINVAL, "%s: rows_per_seq %d outside [1, 64]", fn, a->rows_per_seq);
+    if (!a->ring || !a->ctx_len || !a->n_new || !a->slot || !a->pos)
+        return fail(DFLASH_EINVAL, "%s: null pointer", fn);
+    return launched(fn, dflash::launch_ring_append(*a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -46,4 +46,7 @@ struct DraftMlpPlan {
 DraftMlpPlan draft_mlp_plan(const dflash_mlp_args& a);
 hipError_t launch_draft_mlp(const dflash_mlp_args& a, const DraftMlpPlan& plan, void* ws, hipStream_t s);
 
+// ---- sliding-window cache ----
+hipError_t launch_ring_append(const dflash_ring_args& a, hipStream_t s);
+
 }  // namespace dflash

@@ -15,6 +15,10 @@
  *   dflash_draft_mlp   output projection + residual, RMSNorm, SwiGLU MLP +
  *                      residual, optional final RMSNorm
  *
+ * and the append step of a sliding-window draft cache kept as a ring:
+ *
+ *   dflash_ring_append slots and positions of a cycle's verified rows
+ *
  * Sources (web pages; cited by title and section):
  *   [E4B] "Nemotron 3.5 Bolt E4B: Block-Parallel Speculation with DFlash"
  *   [DF2] "DFlash & DFlash2: Block-Diffusion LLM-Speedup"
@@ -285,6 +289,35 @@ typedef struct dflash_mlp_args {
     void* h_out;              /* optional device [B][8][2560] copy of h (dtype); NULL = not written */
 } dflash_mlp_args;
 
+/*
+ * dflash_ring_append -- cache slots of the rows a cycle appends to a
+ * sliding-window draft cache kept as a ring of pages.  [E4B] "Five target
+ * states become persistent draft context" (the drafter attends to the latest
+ * 1,024 tokens) and "Cache and latency have separate break-even points"
+ * (20 MiB of K/V per sequence at that window).
+ * Logical page p of sequence b is physical page ring[b][p mod ring_pages];
+ * keeping the slot t % 16, the ring holds the latest 16 * ring_pages tokens,
+ * so ceil(W / 16) pages cover a W-token window.  For row rows_per_seq*b + j,
+ * with n = clamp(n_new[b], 0, rows_per_seq):
+ *   j < n:  t = ctx_len[b] + j,  slot = ring[b][(t/16) mod R] * 16 + t % 16,  pos = t
+ *   else:   slot = -1 (dflash_ctx_fuse skips the row),  pos = 0
+ * and then ctx_len[b] += n.  slot / pos feed dflash_ctx_fuse with
+ * M = B * rows_per_seq rows; dflash_block_attn then reads the ring through a
+ * block table whose entry p is ring[b][p mod R], with window = W.  Only
+ * verified tokens enter the draft cache (block K/V are per cycle), so there
+ * is nothing to roll back.  No workspace.
+ */
+typedef struct dflash_ring_args {
+    int32_t B;                /* sequences, 1..65535 */
+    int32_t ring_pages;       /* R >= 1 pages per sequence */
+    const int32_t* ring;      /* device [B][R] physical page ids */
+    int32_t* ctx_len;         /* device [B] cached tokens; read, then advanced */
+    const int32_t* n_new;     /* device [B] rows verified this cycle (e.g. out_len) */
+    int32_t rows_per_seq;     /* 1..64 fuse rows reserved per sequence */
+    int64_t* slot;            /* device [B * rows_per_seq] */
+    int32_t* pos;             /* device [B * rows_per_seq] */
+} dflash_ring_args;
+
 /* Library version (DFLASH_VERSION of the build). */
 int dflash_version(void);
 
@@ -293,7 +326,8 @@ const char* dflash_last_error(void);
 
 /* sizeof of the argument structs as compiled into the library:
  * kind 0 = dflash_fuse_args, 1 = dflash_attn_args, 2 = dflash_verify_args,
- * 3 = dflash_embed_args, 4 = dflash_qkv_args, 5 = dflash_mlp_args;
+ * 3 = dflash_embed_args, 4 = dflash_qkv_args, 5 = dflash_mlp_args,
+ * 6 = dflash_ring_args;
  * returns 0 for any other kind.  Lets bindings check their struct mirrors. */
 size_t dflash_args_size(int kind);
 
@@ -321,6 +355,9 @@ int dflash_draft_qkv(const dflash_qkv_args* args, void* workspace,
                      size_t workspace_bytes, void* stream);
 int dflash_draft_mlp(const dflash_mlp_args* args, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/* Sliding-window cache append (no workspace). */
+int dflash_ring_append(const dflash_ring_args* args, void* stream);
 
 #ifdef __cplusplus
 }

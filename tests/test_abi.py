@@ -37,7 +37,7 @@ def test_header_declares_every_operation():
               "dflash_fuse_workspace_size", "dflash_attn_workspace_size",
               "dflash_verify_workspace_size", "dflash_last_error", "dflash_version",
               "dflash_args_size", "dflash_draft_embed", "dflash_draft_qkv", "dflash_draft_mlp",
-              "dflash_draft_qkv_workspace_size", "dflash_draft_mlp_workspace_size"):
+              "dflash_draft_qkv_workspace_size", "dflash_draft_mlp_workspace_size", "dflash_ring_append"):
         assert f in fns
 
 
@@ -250,4 +250,23 @@ def test_draft_layer_validation(lib):
     assert emb(ctypes.byref(_embed_args(anchor=None)), None) == -1
     assert emb(ctypes.byref(_embed_args(B=0)), None) == -1
     assert emb(ctypes.byref(_embed_args(dtype=9)), None) == -2
+
+
+def test_ring_append_validation(lib):
+    from block_speculative_decoding_amd import _lib
+
+    def args(**kw):
+        a = _lib.RingArgs()
+        a.B, a.ring_pages, a.rows_per_seq = 4, 64, 8
+        a.ring = a.ctx_len = a.n_new = a.slot = a.pos = FAKE
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+    f = lib.dflash_ring_append
+    assert f(ctypes.byref(args(B=0)), None) == -1
+    assert f(ctypes.byref(args(ring_pages=0)), None) == -1
+    assert f(ctypes.byref(args(rows_per_seq=0)), None) == -1
+    assert f(ctypes.byref(args(rows_per_seq=65)), None) == -1
+    assert f(ctypes.byref(args(n_new=None)), None) == -1
+    assert b"null" in lib.dflash_last_error()
 

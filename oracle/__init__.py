@@ -29,6 +29,8 @@ Modules:
                      projection + residual, SwiGLU MLP, final norm.
 * ``window_cache`` -- the sliding-window draft cache as a ring of pages:
                      capacity, append slots, wrapped block table.
+* ``draft_head``  -- the shared LM head over the block rows and the draft
+                     proposals (argmax, or Gumbel-max on stream 2).
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test
 against values printed on the pages, closed forms, invariants, brute force
@@ -42,6 +44,7 @@ from .block_attn import block_attn_ref, attend, prep_block
 from .spec_verify import spec_verify_ref, VerifyTrace
 from .draft_layer import embed_block, qkv_ref, mlp_ref, o_proj_residual_ref, ffn_ref, silu, layer_weight_shapes
 from .window_cache import ring_pages, ring_append, ring_block_table
+from .draft_head import head_logits_ref, draft_sample_ref
 
 __all__ = [
     "bf16_round", "rms_norm", "rope_rotate_half", "rope_angles",
@@ -51,4 +54,5 @@ __all__ = [
     "spec_verify_ref", "VerifyTrace",
     "embed_block", "qkv_ref", "mlp_ref", "o_proj_residual_ref", "ffn_ref", "silu", "layer_weight_shapes",
     "ring_pages", "ring_append", "ring_block_table",
+    "head_logits_ref", "draft_sample_ref",
 ]

@@ -25,7 +25,7 @@ keeps its top 23 bits).
 
 stream 0: acceptance uniforms (i = 0, k = 1..7)
 stream 1: Gumbel noise of the correction / bonus sample (k = 1..8, i < V)
-stream 2: reserved for harness-side draft sampling.
+stream 2: draft sampling (the proposals of rows 1..7 of the draft head).
 """
 
 import numpy as np

@@ -24,6 +24,23 @@ def exact(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
+def bf16_step(v):
+    """Spacing of bf16 values at |v|: 2^(e-7) for 2^e <= |v| < 2^(e+1)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, 2.0 ** (e - 7), 2.0 ** -133)
+
+
+def bf16_err(gpu, ref, extra=0.0):
+    """Largest error of a stored bf16 output against the oracle's unrounded
+    value, as a fraction of its bound max(2e-2, 1.1 * 2^-8 |ref|) + extra
+    (pass: <= 1).  The first term is the storage rounding (half a step);
+    extra carries one-step differences of stored intermediates."""
+    gpu, ref = np.asarray(gpu, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    bound = np.maximum(TOL[BF16], 1.1 * 2.0 ** -8 * np.abs(ref)) + extra
+    return float(np.max(np.abs(gpu - ref) / bound)) if gpu.size else 0.0
+
+
 def compare_verify(gpu_tokens, gpu_len, tr, gap_tol=GAP_TOL):
     """Bit-exact comparison of emitted tokens and lengths.
 

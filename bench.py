@@ -409,6 +409,39 @@ def draft_measurement(torch, dfl, synth, wl):
                                 "weight_bytes": per_layer * 2 * LAYERS}}
 
 
+def head_measurement(torch, dfl, synth):
+    """The shared LM head over the serving batch's block rows (B = 64, 8 rows
+    each, V = 262144) and the seven proposals per sequence, once with the
+    batch's temperature mix (a quarter greedy) and once all greedy; the
+    difference is the cost of the Gumbel draws."""
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev).manual_seed(SEED + 4)
+    y = torch.randn((B, 8, 2560), generator=g, device=dev, dtype=torch.float32).to(bf)
+    w = (torch.randn((V, 2560), generator=g, device=dev, dtype=torch.float32) * 0.05).to(bf)
+    temp = torch.from_numpy(synth.head_temperatures(SEED, B)).to(dev)
+    mixed = dfl.prepare_draft_head(y, w, temp, seed=SEED, offset=0)
+    logits, d = mixed.outputs
+    greedy = dfl.prepare_draft_head(y, w, torch.zeros_like(temp), seed=SEED, offset=0, logits=logits,
+                                    draft_tokens=d, workspace=mixed.workspace)
+    m_ms = timed(torch, mixed, warmup=2, reps=10)
+    g_ms = timed(torch, greedy, warmup=2, reps=10)
+    M = 8 * B
+    flops = 2 * M * V * 2560
+    # Algorithmic bytes: the head once, the block rows in, the logits out,
+    # the seven proposal rows read back by the sampling pass.
+    nbytes = V * 2560 * 2 + M * 2560 * 2 + M * V * 2 + 7 * B * V * 2
+    n_sampled = int((temp > 0).sum().item())
+    del w, logits, mixed, greedy
+    torch.cuda.empty_cache()
+    return {"draft_head_b64": {"ms": round(m_ms, 4), "greedy_ms": round(g_ms, 4), "V": V, "block_rows": M,
+                               "sampled_sequences": n_sampled,
+                               "TFLOP/s": round(flops / (m_ms * 1e-3) / 1e12, 1),
+                               "mfma_frac": round(flops / (m_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                               "GB/s": round(nbytes / (m_ms * 1e-3) / 1e9, 1),
+                               "hbm_frac": round(nbytes / (m_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -531,6 +564,8 @@ def main():
         res["kernels"].update(window_measurement(torch, dfl, wl))
         log("[bench] draft forward around attention: B=64, 5 layers")
         res["kernels"].update(draft_measurement(torch, dfl, synth, wl))
+        log("[bench] shared LM head and draft proposals: B=64, V=262144")
+        res["kernels"].update(head_measurement(torch, dfl, synth))
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(wl)

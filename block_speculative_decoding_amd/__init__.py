@@ -9,10 +9,10 @@ from ._lib import (DFlashError, load, ctx_fuse, block_attn, spec_verify,
                    prepare_ctx_fuse, prepare_block_attn, prepare_spec_verify,
                    draft_embed, draft_qkv, draft_mlp,
                    prepare_draft_embed, prepare_draft_qkv, prepare_draft_mlp,
-                   ring_append, prepare_ring_append, EXPORTS)
+                   ring_append, prepare_ring_append, draft_head, prepare_draft_head, EXPORTS)
 
 __all__ = ["DFlashError", "load", "ctx_fuse", "block_attn", "spec_verify",
            "prepare_ctx_fuse", "prepare_block_attn", "prepare_spec_verify",
            "draft_embed", "draft_qkv", "draft_mlp",
            "prepare_draft_embed", "prepare_draft_qkv", "prepare_draft_mlp",
-           "ring_append", "prepare_ring_append", "EXPORTS"]
+           "ring_append", "prepare_ring_append", "draft_head", "prepare_draft_head", "EXPORTS"]

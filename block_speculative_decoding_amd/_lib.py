@@ -78,13 +78,20 @@ class RingArgs(ctypes.Structure):
                 ("rows_per_seq", _I32), ("slot", _P), ("pos", _P)]
 
 
-ARG_STRUCTS = (FuseArgs, AttnArgs, VerifyArgs, EmbedArgs, QkvArgs, MlpArgs, RingArgs)
+class HeadArgs(ctypes.Structure):
+    _fields_ = [("dtype", _I32), ("B", _I32), ("V", _I64), ("y", _P), ("w_head", _P), ("temperature", _P),
+                ("seed", _U64), ("offset", _U64), ("logits", _P), ("draft_tokens", _P)]
+
+
+ARG_STRUCTS = (FuseArgs, AttnArgs, VerifyArgs, EmbedArgs, QkvArgs, MlpArgs, RingArgs, HeadArgs)
 
 EXPORTS = ["dflash_version", "dflash_last_error", "dflash_args_size",
            "dflash_fuse_workspace_size", "dflash_attn_workspace_size", "dflash_verify_workspace_size",
            "dflash_draft_qkv_workspace_size", "dflash_draft_mlp_workspace_size",
+           "dflash_draft_head_workspace_size",
            "dflash_ctx_fuse", "dflash_block_attn", "dflash_spec_verify",
-           "dflash_draft_embed", "dflash_draft_qkv", "dflash_draft_mlp", "dflash_ring_append"]
+           "dflash_draft_embed", "dflash_draft_qkv", "dflash_draft_mlp", "dflash_ring_append",
+           "dflash_draft_head"]
 
 _lib = None
 
@@ -102,13 +109,13 @@ def load():
     lib.dflash_args_size.restype = ctypes.c_size_t
     lib.dflash_args_size.argtypes = [ctypes.c_int]
     for name, st in (("fuse", FuseArgs), ("attn", AttnArgs), ("verify", VerifyArgs),
-                     ("draft_qkv", QkvArgs), ("draft_mlp", MlpArgs)):
+                     ("draft_qkv", QkvArgs), ("draft_mlp", MlpArgs), ("draft_head", HeadArgs)):
         f = getattr(lib, f"dflash_{name}_workspace_size")
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.POINTER(st), ctypes.POINTER(ctypes.c_size_t)]
     for name, st in (("dflash_ctx_fuse", FuseArgs), ("dflash_block_attn", AttnArgs),
                      ("dflash_spec_verify", VerifyArgs), ("dflash_draft_qkv", QkvArgs),
-                     ("dflash_draft_mlp", MlpArgs)):
+                     ("dflash_draft_mlp", MlpArgs), ("dflash_draft_head", HeadArgs)):
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.POINTER(st), _P, ctypes.c_size_t, _P]
@@ -531,3 +538,46 @@ def ring_append(*args, stream=None, **kw):
     prep(stream)
     return prep.outputs
 
+
+
+# ---------------------------------------------------------------- LM head
+def prepare_draft_head(y, w_head, temperature, seed=0, offset=0, logits=None, draft_tokens=None, workspace=None):
+    """Shared LM head over the block rows and the seven draft proposals
+    (include/dflash.h, dflash_draft_head).
+
+    y [B, 8, 2560] final-norm output; w_head [V, 2560]; temperature float32
+    [B] (<= 0: greedy).  Outputs logits [B, 8, V] (dtype of y) and
+    draft_tokens int32 [B, 7] (allocated if None); logits[:, 1:] is the
+    draft_logits input of spec_verify.
+    """
+    lib = load()
+    dt = y.dtype
+    B = y.shape[0]
+    V = w_head.shape[0]
+    _need(y, "y", dt, (B, BLOCK, D))
+    _need(w_head, "w_head", dt, (V, D))
+    _need(temperature, "temperature", torch.float32, (B,))
+    dev = y.device
+    if logits is None:
+        logits = torch.empty((B, BLOCK, V), dtype=dt, device=dev)
+    if draft_tokens is None:
+        draft_tokens = torch.empty((B, BLOCK - 1), dtype=torch.int32, device=dev)
+    _need(logits, "logits", dt, (B, BLOCK, V))
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, BLOCK - 1))
+    a = HeadArgs()
+    a.dtype, a.B, a.V = _dtype_code(y), B, V
+    a.y, a.w_head, a.temperature = y.data_ptr(), w_head.data_ptr(), temperature.data_ptr()
+    a.seed, a.offset = int(seed), int(offset)
+    a.logits, a.draft_tokens = logits.data_ptr(), draft_tokens.data_ptr()
+    nbytes = ctypes.c_size_t()
+    _check(lib.dflash_draft_head_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
+    ws, wsb = _workspace(nbytes.value, workspace, dev)
+    prep = Prepared(lib.dflash_draft_head, a, ws, wsb, (y, w_head, temperature, logits, draft_tokens))
+    prep.outputs = (logits, draft_tokens)
+    return prep
+
+
+def draft_head(*args, stream=None, **kw):
+    prep = prepare_draft_head(*args, **kw)
+    prep(stream)
+    return prep.outputs

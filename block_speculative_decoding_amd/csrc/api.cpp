@@ -110,6 +110,15 @@ int validate_mlp_sizes(const char* fn, const dflash_mlp_args* a) {
     return validate_draft_b(fn, a->dtype, a->B);
 }
 
+int validate_head_sizes(const char* fn, const dflash_head_args* a) {
+    if (!a) return fail(DFLASH_EINVAL, "%s: null args", fn);
+    int rc = validate_draft_b(fn, a->dtype, a->B);
+    if (rc) return rc;
+    if (a->V < 128 || a->V > (1 << 21) || a->V % 128)
+        return fail(DFLASH_EINVAL, "%s: V %lld must be a multiple of 128 in [128, 2^21]", fn, (long long)a->V);
+    return DFLASH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -127,6 +136,7 @@ size_t dflash_args_size(int kind) {
         case 4: return sizeof(dflash_qkv_args);
         case 5: return sizeof(dflash_mlp_args);
         case 6: return sizeof(dflash_ring_args);
+        case 7: return sizeof(dflash_head_args);
         default: return 0;
     }
 }
@@ -173,6 +183,15 @@ int dflash_draft_mlp_workspace_size(const dflash_mlp_args* a, size_t* bytes) {
     int rc = validate_mlp_sizes(fn, a);
     if (rc) return rc;
     *bytes = dflash::draft_mlp_plan(*a).ws_bytes;
+    return ok();
+}
+
+int dflash_draft_head_workspace_size(const dflash_head_args* a, size_t* bytes) {
+    const char* fn = "dflash_draft_head_workspace_size";
+    if (!bytes) return fail(DFLASH_EINVAL, "%s: null output", fn);
+    int rc = validate_head_sizes(fn, a);
+    if (rc) return rc;
+    *bytes = dflash::head_workspace_bytes(a->B, a->V);
     return ok();
 }
 
@@ -317,6 +336,20 @@ int dflash_ring_append(const dflash_ring_args* a, void* stream) {
     if (!a->ring || !a->ctx_len || !a->n_new || !a->slot || !a->pos)
         return fail(DFLASH_EINVAL, "%s: null pointer", fn);
     return launched(fn, dflash::launch_ring_append(*a, static_cast<hipStream_t>(stream)));
+}
+
+int dflash_draft_head(const dflash_head_args* a, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "dflash_draft_head";
+    int rc = validate_head_sizes(fn, a);
+    if (rc) return rc;
+    REQUIRE_PTR(a->y);
+    REQUIRE_PTR(a->w_head);
+    REQUIRE_PTR(a->temperature);
+    REQUIRE_PTR(a->logits);
+    REQUIRE_PTR(a->draft_tokens);
+    rc = check_ws(fn, dflash::head_workspace_bytes(a->B, a->V), ws, ws_bytes);
+    if (rc) return rc;
+    return launched(fn, dflash::launch_head(*a, ws, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

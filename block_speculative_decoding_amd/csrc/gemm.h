@@ -23,6 +23,8 @@ struct GemmParams {
     int M, N, K;
     int ks, kt_per_split;
     float* part;          // [ks][M][N]
+    uint16_t* out_bf16;   // bf16 path with ks == 1: if set, the product rounded to bf16
+                          // goes here ([M][N]) instead of part
 };
 
 // Tile id for this workgroup: XCD-contiguous ranges, then 8-row M groups.

@@ -148,6 +148,19 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
     wait_lgkm<0>();
 
     // Lane holds column lr of each 32x32 block, rows 8*(r/4) + 4*lh + (r%4).
+    if (p.out_bf16) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int gm = m0 + wr + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    const int gn = n0 + wc + 32 * j + lr;
+                    if (gm < p.M) p.out_bf16[(int64_t)gm * p.N + gn] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
+                }
+        return;
+    }
     float* out = p.part + (int64_t)t.ks * p.M * p.N;
 #pragma unroll
     for (int i = 0; i < 2; ++i)

@@ -49,4 +49,8 @@ hipError_t launch_draft_mlp(const dflash_mlp_args& a, const DraftMlpPlan& plan, 
 // ---- sliding-window cache ----
 hipError_t launch_ring_append(const dflash_ring_args& a, hipStream_t s);
 
+// ---- shared LM head and draft proposals ----
+size_t head_workspace_bytes(int B, int64_t V);
+hipError_t launch_head(const dflash_head_args& a, void* ws, hipStream_t s);
+
 }  // namespace dflash

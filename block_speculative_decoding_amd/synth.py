@@ -110,6 +110,27 @@ def embedding(seed, V):
     return normal(seed, "emb", (V, D))
 
 
+def head_weight(seed, V, std=0.05):
+    """Shared LM head [V, 2560] ~ N(0, std^2): on unit-RMS states the logits
+    have standard deviation std * sqrt(2560) (about 2.5 at the default)."""
+    return normal(seed, "w_head", (V, D), std=std)
+
+
+def head_input(seed, B):
+    """Final-norm output of the last draft layer [B, 8, 2560] ~ N(0, 1)."""
+    return normal(seed, "y_head", (B, BLOCK, D))
+
+
+def head_temperatures(seed, B):
+    """Per-sequence temperatures: a quarter greedy (0 or -1), the rest
+    uniform on [0.3, 1.5]."""
+    g = gen(seed, "head_temperature")
+    t = g.uniform(0.3, 1.5, size=B).astype(np.float32)
+    greedy = g.permutation(B)[:max(1, B // 4)]
+    t[greedy] = np.where(np.arange(len(greedy)) % 2 == 0, 0.0, -1.0)
+    return t
+
+
 def anchors(seed, B, V):
     """Last verified token of each sequence, uniform on [0, V)."""
     return gen(seed, "anchors").integers(0, V, size=B).astype(np.int32)

@@ -19,6 +19,10 @@
  *
  *   dflash_ring_append slots and positions of a cycle's verified rows
  *
+ * and the shared LM head with the draft proposals it samples:
+ *
+ *   dflash_draft_head  block logits and the seven proposals
+ *
  * Sources (web pages; cited by title and section):
  *   [E4B] "Nemotron 3.5 Bolt E4B: Block-Parallel Speculation with DFlash"
  *   [DF2] "DFlash & DFlash2: Block-Diffusion LLM-Speedup"
@@ -92,7 +96,7 @@ extern "C" {
 #define DFLASH_MAX_LAYERS 5      /* draft layers */
 #define DFLASH_INTER      5120   /* SwiGLU width (derived from the parameter count) */
 
-#define DFLASH_VERSION 10100     /* 1.1.0 */
+#define DFLASH_VERSION 10200     /* 1.2.0 */
 
 /*
  * dflash_ctx_fuse -- context fusion and K/V injection.
@@ -318,6 +322,38 @@ typedef struct dflash_ring_args {
     int32_t* pos;             /* device [B * rows_per_seq] */
 } dflash_ring_args;
 
+/*
+ * dflash_draft_head -- the shared LM head over the eight block rows and the
+ * seven draft proposals.  [E4B] "The parameter count exposes the real cost"
+ * (the drafter's output head is a copy of the target head, [262144, 2560],
+ * since it scores the target's vocabulary) and "The released serving cycle"
+ * (one forward over the block proposes all seven future tokens); [DF2] 4.2
+ * (the target's unembedding head maps output states to vocabulary logits).
+ *   logits[b][r] = y[b][r] . w_head^T            r = 0..7, stored in dtype
+ *   draft_tokens[b][k-1], k = 1..7, from the STORED row logits[b][k]:
+ *     T_b <= 0: argmax_i logits[b][k][i]             (lowest index on ties)
+ *     T_b >  0: argmax_i logits[b][k][i] / T_b - ln(-ln u_i)
+ * with u_i = U(2, b, k, i), stream 2 of the uniform layout documented at
+ * dflash_spec_verify (streams 0 and 1 belong to verification): a Gumbel-max
+ * draw, which is an exact sample from softmax(logits[b][k] / T_b).  Row 0
+ * (the anchor) is projected and not sampled.  Rows 1..7 of logits are the
+ * draft_logits of dflash_spec_verify for the same cycle (base logits + V,
+ * d_batch_stride = 8 V, d_row_stride = V).  Use the same seed and offset as
+ * that verify call: draft and verification draws come from disjoint streams.
+ */
+typedef struct dflash_head_args {
+    int32_t dtype;            /* DFLASH_BF16 or DFLASH_F32 */
+    int32_t B;                /* sequences, 1..8192 */
+    int64_t V;                /* vocabulary, multiple of 128, 128..2^21 */
+    const void* y;            /* device [B][8][2560] final-norm output of the last draft layer */
+    const void* w_head;       /* device [V][2560] head weight (row i scores token i) */
+    const float* temperature; /* device [B]; <= 0 means greedy */
+    uint64_t seed;
+    uint64_t offset;          /* per-cycle counter word */
+    void* logits;             /* device [B][8][V] (dtype), written */
+    int32_t* draft_tokens;    /* device [B][7] proposals d_1..d_7, written */
+} dflash_head_args;
+
 /* Library version (DFLASH_VERSION of the build). */
 int dflash_version(void);
 
@@ -327,7 +363,7 @@ const char* dflash_last_error(void);
 /* sizeof of the argument structs as compiled into the library:
  * kind 0 = dflash_fuse_args, 1 = dflash_attn_args, 2 = dflash_verify_args,
  * 3 = dflash_embed_args, 4 = dflash_qkv_args, 5 = dflash_mlp_args,
- * 6 = dflash_ring_args;
+ * 6 = dflash_ring_args, 7 = dflash_head_args;
  * returns 0 for any other kind.  Lets bindings check their struct mirrors. */
 size_t dflash_args_size(int kind);
 
@@ -338,6 +374,7 @@ int dflash_attn_workspace_size(const dflash_attn_args* args, size_t* bytes);
 int dflash_verify_workspace_size(const dflash_verify_args* args, size_t* bytes);
 int dflash_draft_qkv_workspace_size(const dflash_qkv_args* args, size_t* bytes);
 int dflash_draft_mlp_workspace_size(const dflash_mlp_args* args, size_t* bytes);
+int dflash_draft_head_workspace_size(const dflash_head_args* args, size_t* bytes);
 
 /* The three operations.  `workspace` must hold at least the size returned
  * above (it may be NULL when that size is 0); its contents are scratch. */
@@ -358,6 +395,10 @@ int dflash_draft_mlp(const dflash_mlp_args* args, void* workspace,
 
 /* Sliding-window cache append (no workspace). */
 int dflash_ring_append(const dflash_ring_args* args, void* stream);
+
+/* Shared LM head and draft proposals. */
+int dflash_draft_head(const dflash_head_args* args, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

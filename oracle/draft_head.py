@@ -34,6 +34,16 @@ def head_logits_ref(y, w_head):
     return np.asarray(y, dtype=np.float64) @ np.asarray(w_head, dtype=np.float64).T
 
 
+def draft_keys(row, T, seed, offset, b, k):
+    """Keys whose first maximum is proposal k of sequence b: the logits
+    themselves when greedy (T <= 0), else z_i / T + G_i with the stream-2
+    Gumbel noise of (b, k)."""
+    row = np.asarray(row, dtype=np.float64)
+    if not T > 0:
+        return row
+    return row / T + gumbel(uniform_row(seed, offset, DRAFT_STREAM, b, k, row.shape[0]))
+
+
 def draft_sample_ref(z, temperature, seed=0, offset=0):
     """Proposals d [B, 7] int32 from stored logits z [B, 8, V] and the gap
     between the two largest keys of each draw (inf for greedy rows, where
@@ -49,7 +59,7 @@ def draft_sample_ref(z, temperature, seed=0, offset=0):
             if not T > 0:
                 d[b, k - 1] = int(np.argmax(row))     # first maximum = lowest index
                 continue
-            keys = row / T + gumbel(uniform_row(seed, offset, DRAFT_STREAM, b, k, V))
+            keys = draft_keys(row, T, seed, offset, b, k)
             i = int(np.argmax(keys))
             d[b, k - 1] = i
             gap[b, k - 1] = keys[i] - np.max(np.delete(keys, i)) if V > 1 else np.inf

@@ -37,7 +37,8 @@ def test_header_declares_every_operation():
               "dflash_fuse_workspace_size", "dflash_attn_workspace_size",
               "dflash_verify_workspace_size", "dflash_last_error", "dflash_version",
               "dflash_args_size", "dflash_draft_embed", "dflash_draft_qkv", "dflash_draft_mlp",
-              "dflash_draft_qkv_workspace_size", "dflash_draft_mlp_workspace_size", "dflash_ring_append"):
+              "dflash_draft_qkv_workspace_size", "dflash_draft_mlp_workspace_size", "dflash_ring_append",
+              "dflash_draft_head", "dflash_draft_head_workspace_size"):
         assert f in fns
 
 
@@ -53,7 +54,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_struct_sizes_and_version(lib):
     from block_speculative_decoding_amd import _lib
-    assert lib.dflash_version() == 10100
+    assert lib.dflash_version() == 10200
     for kind, st in enumerate(_lib.ARG_STRUCTS):
         assert lib.dflash_args_size(kind) == ctypes.sizeof(st)
     assert lib.dflash_args_size(len(_lib.ARG_STRUCTS)) == 0
@@ -270,3 +271,30 @@ def test_ring_append_validation(lib):
     assert f(ctypes.byref(args(n_new=None)), None) == -1
     assert b"null" in lib.dflash_last_error()
 
+
+
+def test_draft_head_validation(lib):
+    from block_speculative_decoding_amd import _lib
+
+    def args(**kw):
+        a = _lib.HeadArgs()
+        a.dtype, a.B, a.V = 0, 64, 262144
+        a.y = a.w_head = a.temperature = a.logits = a.draft_tokens = FAKE
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+    rc, n = _ws(lib, "draft_head", args())
+    # one (key, index) partial per 8192-entry chunk of each proposal row
+    assert rc == 0 and n == 64 * 7 * 32 * 8
+    assert _ws(lib, "draft_head", args(V=262144 + 64))[0] == -1      # not a multiple of 128
+    assert _ws(lib, "draft_head", args(V=0))[0] == -1
+    assert _ws(lib, "draft_head", args(V=(1 << 21) + 128))[0] == -1
+    assert _ws(lib, "draft_head", args(B=0))[0] == -1
+    assert _ws(lib, "draft_head", args(B=8193))[0] == -1
+    assert _ws(lib, "draft_head", args(dtype=3))[0] == -2
+    assert _ws(lib, "draft_head", args(V=128, B=1))[1] == 256        # one chunk, rounded to 256 bytes
+    assert _call(lib, "dflash_draft_head", args(w_head=None), FAKE, n) == -1
+    assert _call(lib, "dflash_draft_head", args(logits=FAKE + 4), FAKE, n) == -1
+    assert _call(lib, "dflash_draft_head", args(temperature=None), FAKE, n) == -1
+    assert _call(lib, "dflash_draft_head", args(), FAKE, n - 1) == -4
+    assert _call(lib, "dflash_draft_head", args(), None, 0) == -4

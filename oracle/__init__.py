@@ -31,6 +31,10 @@ Modules:
                      capacity, append slots, wrapped block table.
 * ``draft_head``  -- the shared LM head over the block rows and the draft
                      proposals (argmax, or Gumbel-max on stream 2).
+* ``dflash2``     -- DFlash2's depthwise block convolution (a residual branch
+                     between attention and the feed-forward half) and the
+                     top-m path selector (per-position candidates, entropy,
+                     top-P paths).
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test
 against values printed on the pages, closed forms, invariants, brute force
@@ -45,6 +49,7 @@ from .spec_verify import spec_verify_ref, VerifyTrace
 from .draft_layer import embed_block, qkv_ref, mlp_ref, o_proj_residual_ref, ffn_ref, silu, layer_weight_shapes
 from .window_cache import ring_pages, ring_append, ring_block_table
 from .draft_head import head_logits_ref, draft_keys, draft_sample_ref
+from .dflash2 import depthwise_conv_ref, conv_mlp_ref, row_stats_ref, top_paths_ref, path_select_ref
 
 __all__ = [
     "bf16_round", "rms_norm", "rope_rotate_half", "rope_angles",
@@ -55,4 +60,5 @@ __all__ = [
     "embed_block", "qkv_ref", "mlp_ref", "o_proj_residual_ref", "ffn_ref", "silu", "layer_weight_shapes",
     "ring_pages", "ring_append", "ring_block_table",
     "head_logits_ref", "draft_keys", "draft_sample_ref",
+    "depthwise_conv_ref", "conv_mlp_ref", "row_stats_ref", "top_paths_ref", "path_select_ref",
 ]

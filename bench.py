@@ -392,6 +392,17 @@ def draft_measurement(torch, dfl, synth, wl):
 
     f_ms = timed(torch, forward, warmup=2, reps=10)
     d_ms = timed(torch, dense_only, warmup=2, reps=10)
+    # One layer's output projection + MLP with DFlash2's block convolution
+    # (k = 5) between the halves, against the same call without it.
+    w0 = {k: d(v) for k, v in synth.draft_layer_weights(SEED, 0).items()}
+    wc, bc = (d(v) for v in synth.conv_weights(SEED, 5))
+    o0 = layers[0][1].out
+    xs = torch.empty_like(x)
+    plain = dfl.prepare_draft_mlp(x, o0, w0["w_o"], w0["g_post"], w0["w_gu"], w0["w_d"], x_out=xs)
+    conv = dfl.prepare_draft_mlp(x, o0, w0["w_o"], w0["g_post"], w0["w_gu"], w0["w_d"], x_out=xs, w_conv=wc,
+                                 b_conv=bc, workspace=plain.workspace)
+    pl_ms = timed(torch, plain, warmup=2, reps=10)
+    cv_ms = timed(torch, conv, warmup=2, reps=10)
     per_layer = (6144 * 2560 + 2560 * 4096 + 10240 * 2560 + 2560 * 5120)
     M = 8 * B
     flops = 2 * M * per_layer * LAYERS
@@ -399,9 +410,10 @@ def draft_measurement(torch, dfl, synth, wl):
     # layer input (read twice: projection and residual), Q/K/V out, the
     # attention output in and the layer output; the embedding writes M rows.
     nbytes = per_layer * 2 * LAYERS + LAYERS * M * 2 * (2 * 2560 + 6144 + 4096 + 2560) + M * 2560 * 2
-    del emb, embed, dense, layers
+    del emb, embed, dense, layers, plain, conv
     torch.cuda.empty_cache()
     return {"draft_forward_b64": {"ms": round(f_ms, 4), "layers": LAYERS, "block_rows": M},
+            "draft_mlp_block_conv_b64": {"ms": round(cv_ms, 4), "without_conv_ms": round(pl_ms, 4), "k": 5},
             "draft_dense_b64": {"ms": round(d_ms, 4), "TFLOP/s": round(flops / (d_ms * 1e-3) / 1e12, 1),
                                 "mfma_frac": round(flops / (d_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                                 "GB/s": round(nbytes / (d_ms * 1e-3) / 1e9, 1),
@@ -426,15 +438,24 @@ def head_measurement(torch, dfl, synth):
                                     draft_tokens=d, workspace=mixed.workspace)
     m_ms = timed(torch, mixed, warmup=2, reps=10)
     g_ms = timed(torch, greedy, warmup=2, reps=10)
+    # DFlash2's path selector on the head's own logits (rows 1..7): top-4
+    # candidates per position, 16 paths.
+    paths = dfl.prepare_draft_paths(logits, 4, 16, 0.2)
+    p_ms = timed(torch, paths, warmup=2, reps=10)
+    p_bytes = 7 * B * V * 2
     M = 8 * B
     flops = 2 * M * V * 2560
     # Algorithmic bytes: the head once, the block rows in, the logits out,
     # the seven proposal rows read back by the sampling pass.
     nbytes = V * 2560 * 2 + M * 2560 * 2 + M * V * 2 + 7 * B * V * 2
     n_sampled = int((temp > 0).sum().item())
-    del w, logits, mixed, greedy
+    del w, logits, mixed, greedy, paths
     torch.cuda.empty_cache()
-    return {"draft_head_b64": {"ms": round(m_ms, 4), "greedy_ms": round(g_ms, 4), "V": V, "block_rows": M,
+    return {"draft_paths_b64": {"ms": round(p_ms, 4), "m": 4, "P": 16, "V": V,
+                                "GB/s": round(p_bytes / (p_ms * 1e-3) / 1e9, 1),
+                                "hbm_frac": round(p_bytes / (p_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                "algorithmic_bytes": p_bytes},
+            "draft_head_b64": {"ms": round(m_ms, 4), "greedy_ms": round(g_ms, 4), "V": V, "block_rows": M,
                                "sampled_sequences": n_sampled,
                                "TFLOP/s": round(flops / (m_ms * 1e-3) / 1e12, 1),
                                "mfma_frac": round(flops / (m_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),

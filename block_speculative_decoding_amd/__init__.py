@@ -9,10 +9,12 @@ from ._lib import (DFlashError, load, ctx_fuse, block_attn, spec_verify,
                    prepare_ctx_fuse, prepare_block_attn, prepare_spec_verify,
                    draft_embed, draft_qkv, draft_mlp,
                    prepare_draft_embed, prepare_draft_qkv, prepare_draft_mlp,
-                   ring_append, prepare_ring_append, draft_head, prepare_draft_head, EXPORTS)
+                   ring_append, prepare_ring_append, draft_head, prepare_draft_head,
+                   draft_paths, prepare_draft_paths, EXPORTS)
 
 __all__ = ["DFlashError", "load", "ctx_fuse", "block_attn", "spec_verify",
            "prepare_ctx_fuse", "prepare_block_attn", "prepare_spec_verify",
            "draft_embed", "draft_qkv", "draft_mlp",
            "prepare_draft_embed", "prepare_draft_qkv", "prepare_draft_mlp",
-           "ring_append", "prepare_ring_append", "draft_head", "prepare_draft_head", "EXPORTS"]
+           "ring_append", "prepare_ring_append", "draft_head", "prepare_draft_head",
+           "draft_paths", "prepare_draft_paths", "EXPORTS"]

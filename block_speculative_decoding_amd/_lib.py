@@ -70,7 +70,8 @@ class QkvArgs(ctypes.Structure):
 class MlpArgs(ctypes.Structure):
     _fields_ = [("dtype", _I32), ("B", _I32),
                 ("x", _P), ("o", _P), ("w_o", _P), ("g_post", _P), ("w_gu", _P), ("w_d", _P),
-                ("g_final", _P), ("eps", _F32), ("x_out", _P), ("y_out", _P), ("h_out", _P)]
+                ("g_final", _P), ("eps", _F32), ("x_out", _P), ("y_out", _P), ("h_out", _P),
+                ("conv_k", _I32), ("w_conv", _P), ("b_conv", _P)]
 
 
 class RingArgs(ctypes.Structure):
@@ -83,15 +84,21 @@ class HeadArgs(ctypes.Structure):
                 ("seed", _U64), ("offset", _U64), ("logits", _P), ("draft_tokens", _P)]
 
 
-ARG_STRUCTS = (FuseArgs, AttnArgs, VerifyArgs, EmbedArgs, QkvArgs, MlpArgs, RingArgs, HeadArgs)
+class PathsArgs(ctypes.Structure):
+    _fields_ = [("dtype", _I32), ("B", _I32), ("V", _I64), ("logits", _P), ("batch_stride", _I64),
+                ("row_stride", _I64), ("m", _I32), ("P", _I32), ("lam", _F32), ("cand_ids", _P),
+                ("cand_logp", _P), ("entropy", _P), ("paths", _P), ("scores", _P)]
+
+
+ARG_STRUCTS = (FuseArgs, AttnArgs, VerifyArgs, EmbedArgs, QkvArgs, MlpArgs, RingArgs, HeadArgs, PathsArgs)
 
 EXPORTS = ["dflash_version", "dflash_last_error", "dflash_args_size",
            "dflash_fuse_workspace_size", "dflash_attn_workspace_size", "dflash_verify_workspace_size",
            "dflash_draft_qkv_workspace_size", "dflash_draft_mlp_workspace_size",
-           "dflash_draft_head_workspace_size",
+           "dflash_draft_head_workspace_size", "dflash_draft_paths_workspace_size",
            "dflash_ctx_fuse", "dflash_block_attn", "dflash_spec_verify",
            "dflash_draft_embed", "dflash_draft_qkv", "dflash_draft_mlp", "dflash_ring_append",
-           "dflash_draft_head"]
+           "dflash_draft_head", "dflash_draft_paths"]
 
 _lib = None
 
@@ -109,13 +116,15 @@ def load():
     lib.dflash_args_size.restype = ctypes.c_size_t
     lib.dflash_args_size.argtypes = [ctypes.c_int]
     for name, st in (("fuse", FuseArgs), ("attn", AttnArgs), ("verify", VerifyArgs),
-                     ("draft_qkv", QkvArgs), ("draft_mlp", MlpArgs), ("draft_head", HeadArgs)):
+                     ("draft_qkv", QkvArgs), ("draft_mlp", MlpArgs), ("draft_head", HeadArgs),
+                     ("draft_paths", PathsArgs)):
         f = getattr(lib, f"dflash_{name}_workspace_size")
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.POINTER(st), ctypes.POINTER(ctypes.c_size_t)]
     for name, st in (("dflash_ctx_fuse", FuseArgs), ("dflash_block_attn", AttnArgs),
                      ("dflash_spec_verify", VerifyArgs), ("dflash_draft_qkv", QkvArgs),
-                     ("dflash_draft_mlp", MlpArgs), ("dflash_draft_head", HeadArgs)):
+                     ("dflash_draft_mlp", MlpArgs), ("dflash_draft_head", HeadArgs),
+                     ("dflash_draft_paths", PathsArgs)):
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.POINTER(st), _P, ctypes.c_size_t, _P]
@@ -440,14 +449,16 @@ def draft_qkv(*args, stream=None, **kw):
 
 
 def prepare_draft_mlp(x, o, w_o, g_post, w_gu, w_d, g_final=None, x_out=None, y_out=None, h_out=None, eps=1e-6,
-                      workspace=None):
+                      workspace=None, w_conv=None, b_conv=None):
     """Output projection + residual, RMSNorm, SwiGLU MLP + residual and the
     optional final RMSNorm (include/dflash.h, dflash_draft_mlp).
 
     x [B, 8, 2560] layer input; o [B, 32, 8, 128] attention output;
     w_o [2560, 4096]; g_post [2560]; w_gu [10240, 2560]; w_d [2560, 5120];
     g_final [2560] or None.  Outputs x_out (may be x), with g_final y_out,
-    and the stored residual h in h_out when that is given.
+    and the stored residual h in h_out when that is given.  With w_conv
+    [k, 2560] and b_conv [2560], DFlash2's block convolution h' = h +
+    conv(h) runs between the two halves (h_out then holds h').
     """
     lib = load()
     dt = x.dtype
@@ -469,6 +480,11 @@ def prepare_draft_mlp(x, o, w_o, g_post, w_gu, w_d, g_final=None, x_out=None, y_
         _need(y_out, "y_out", dt, (B, BLOCK, D))
     if h_out is not None:
         _need(h_out, "h_out", dt, (B, BLOCK, D))
+    if (w_conv is None) != (b_conv is None):
+        raise DFlashError(-1, "w_conv and b_conv go together")
+    if w_conv is not None:
+        _need(w_conv, "w_conv", dt, (w_conv.shape[0], D))
+        _need(b_conv, "b_conv", dt, (D,))
     a = MlpArgs()
     a.dtype, a.B = _dtype_code(x), B
     a.x, a.o, a.w_o, a.g_post = x.data_ptr(), o.data_ptr(), w_o.data_ptr(), g_post.data_ptr()
@@ -478,11 +494,13 @@ def prepare_draft_mlp(x, o, w_o, g_post, w_gu, w_d, g_final=None, x_out=None, y_
     a.x_out = x_out.data_ptr()
     a.y_out = None if y_out is None else y_out.data_ptr()
     a.h_out = None if h_out is None else h_out.data_ptr()
+    if w_conv is not None:
+        a.conv_k, a.w_conv, a.b_conv = w_conv.shape[0], w_conv.data_ptr(), b_conv.data_ptr()
     nbytes = ctypes.c_size_t()
     _check(lib.dflash_draft_mlp_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
     ws, wsb = _workspace(nbytes.value, workspace, dev)
     prep = Prepared(lib.dflash_draft_mlp, a, ws, wsb,
-                    (x, o, w_o, g_post, w_gu, w_d, g_final, x_out, y_out, h_out))
+                    (x, o, w_o, g_post, w_gu, w_d, g_final, x_out, y_out, h_out, w_conv, b_conv))
     prep.outputs = (x_out, y_out, h_out)
     return prep
 
@@ -579,5 +597,49 @@ def prepare_draft_head(y, w_head, temperature, seed=0, offset=0, logits=None, dr
 
 def draft_head(*args, stream=None, **kw):
     prep = prepare_draft_head(*args, **kw)
+    prep(stream)
+    return prep.outputs
+
+
+# ---------------------------------------------------------------- DFlash2 paths
+def prepare_draft_paths(logits, m, P, lam=0.0, cand_ids=None, cand_logp=None, entropy=None, paths=None,
+                        scores=None, workspace=None):
+    """DFlash2's top-m candidate path selector (include/dflash.h,
+    dflash_draft_paths).
+
+    logits [B, 8, V] (rows 1..7 read; last dim contiguous, any 16-byte
+    aligned row / batch strides).  Outputs cand_ids int32 [B, 7, m],
+    cand_logp float32 [B, 7, m], entropy float32 [B, 7], paths int32
+    [B, P, 7] and scores float32 [B, P] (allocated if None).
+    """
+    lib = load()
+    B, R, V = logits.shape
+    if R != BLOCK or not logits.is_cuda or logits.stride(2) != 1:
+        raise DFlashError(-1, "logits must be a device tensor [B, 8, V] with a contiguous last dim")
+    dev = logits.device
+    J = BLOCK - 1
+    outs = {"cand_ids": (cand_ids, torch.int32, (B, J, m)), "cand_logp": (cand_logp, torch.float32, (B, J, m)),
+            "entropy": (entropy, torch.float32, (B, J)), "paths": (paths, torch.int32, (B, P, J)),
+            "scores": (scores, torch.float32, (B, P))}
+    t = {}
+    for name, (x, dt, shape) in outs.items():
+        t[name] = torch.empty(shape, dtype=dt, device=dev) if x is None else x
+        _need(t[name], name, dt, shape)
+    a = PathsArgs()
+    a.dtype, a.B, a.V = _dtype_code(logits), B, V
+    a.logits, a.batch_stride, a.row_stride = logits.data_ptr(), logits.stride(0), logits.stride(1)
+    a.m, a.P, a.lam = m, P, lam
+    for name in outs:
+        setattr(a, name, t[name].data_ptr())
+    nbytes = ctypes.c_size_t()
+    _check(lib.dflash_draft_paths_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
+    ws, wsb = _workspace(nbytes.value, workspace, dev)
+    prep = Prepared(lib.dflash_draft_paths, a, ws, wsb, (logits,) + tuple(t.values()))
+    prep.outputs = tuple(t[n] for n in outs)
+    return prep
+
+
+def draft_paths(*args, stream=None, **kw):
+    prep = prepare_draft_paths(*args, **kw)
     prep(stream)
     return prep.outputs

@@ -119,6 +119,25 @@ int validate_head_sizes(const char* fn, const dflash_head_args* a) {
     return DFLASH_OK;
 }
 
+int validate_paths_sizes(const char* fn, const dflash_paths_args* a) {
+    if (!a) return fail(DFLASH_EINVAL, "%s: null args", fn);
+    int rc = validate_draft_b(fn, a->dtype, a->B);
+    if (rc) return rc;
+    if (a->m < 1 || a->m > 8) return fail(DFLASH_EINVAL, "%s: m %d outside [1, 8]", fn, a->m);
+    int64_t paths = 1;
+    for (int k = 0; k < 7 && paths <= 64; ++k) paths *= a->m;
+    if (a->P < 1 || a->P > 64 || a->P > paths)
+        return fail(DFLASH_EINVAL, "%s: P %d outside [1, min(64, m^7)]", fn, a->P);
+    if (a->V < a->m || a->V > (1 << 24) || a->V % 8)
+        return fail(DFLASH_EINVAL, "%s: V %lld must be a multiple of 8 in [m, 2^24]", fn, (long long)a->V);
+    if (a->row_stride < a->V || a->row_stride % 8)
+        return fail(DFLASH_EINVAL, "%s: row_stride %lld must be a multiple of 8, >= V", fn, (long long)a->row_stride);
+    if (a->batch_stride < 8 * a->row_stride || a->batch_stride % 8)
+        return fail(DFLASH_EINVAL, "%s: batch_stride %lld must be a multiple of 8, >= 8 * row_stride", fn,
+                    (long long)a->batch_stride);
+    return DFLASH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -137,6 +156,7 @@ size_t dflash_args_size(int kind) {
         case 5: return sizeof(dflash_mlp_args);
         case 6: return sizeof(dflash_ring_args);
         case 7: return sizeof(dflash_head_args);
+        case 8: return sizeof(dflash_paths_args);
         default: return 0;
     }
 }
@@ -192,6 +212,15 @@ int dflash_draft_head_workspace_size(const dflash_head_args* a, size_t* bytes) {
     int rc = validate_head_sizes(fn, a);
     if (rc) return rc;
     *bytes = dflash::head_workspace_bytes(a->B, a->V);
+    return ok();
+}
+
+int dflash_draft_paths_workspace_size(const dflash_paths_args* a, size_t* bytes) {
+    const char* fn = "dflash_draft_paths_workspace_size";
+    if (!bytes) return fail(DFLASH_EINVAL, "%s: null output", fn);
+    int rc = validate_paths_sizes(fn, a);
+    if (rc) return rc;
+    *bytes = dflash::paths_workspace_bytes(a->B, a->V);
     return ok();
 }
 
@@ -319,6 +348,11 @@ int dflash_draft_mlp(const dflash_mlp_args* a, void* ws, size_t ws_bytes, void* 
         REQUIRE_PTR(a->y_out);
     }
     if (a->h_out && !aligned16(a->h_out)) return fail(DFLASH_EINVAL, "%s: h_out is not 16-byte aligned", fn);
+    if (a->conv_k < 0 || a->conv_k > 8) return fail(DFLASH_EINVAL, "%s: conv_k %d outside [0, 8]", fn, a->conv_k);
+    if (a->conv_k > 0) {
+        REQUIRE_PTR(a->w_conv);
+        REQUIRE_PTR(a->b_conv);
+    }
     if (!(a->eps > 0.f)) return fail(DFLASH_EINVAL, "%s: eps must be > 0", fn);
     const dflash::DraftMlpPlan pl = dflash::draft_mlp_plan(*a);
     rc = check_ws(fn, pl.ws_bytes, ws, ws_bytes);
@@ -350,6 +384,18 @@ int dflash_draft_head(const dflash_head_args* a, void* ws, size_t ws_bytes, void
     rc = check_ws(fn, dflash::head_workspace_bytes(a->B, a->V), ws, ws_bytes);
     if (rc) return rc;
     return launched(fn, dflash::launch_head(*a, ws, static_cast<hipStream_t>(stream)));
+}
+
+int dflash_draft_paths(const dflash_paths_args* a, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "dflash_draft_paths";
+    int rc = validate_paths_sizes(fn, a);
+    if (rc) return rc;
+    REQUIRE_PTR(a->logits);
+    if (!a->cand_ids || !a->cand_logp || !a->entropy || !a->paths || !a->scores)
+        return fail(DFLASH_EINVAL, "%s: null output pointer", fn);
+    rc = check_ws(fn, dflash::paths_workspace_bytes(a->B, a->V), ws, ws_bytes);
+    if (rc) return rc;
+    return launched(fn, dflash::launch_paths(*a, ws, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -19,7 +19,8 @@
 //
 // Launch sequence of dflash_draft_qkv:  norm -> gemm (N = 6144) -> scatter
 // Launch sequence of dflash_draft_mlp:  transpose -> gemm (N = 2560, K = 4096)
-//   -> residual + norm -> gemm (N = 10240) -> swiglu -> gemm (N = 2560,
+//   -> residual + norm (with DFlash2's block convolution: residual + conv +
+//   norm per sequence) -> gemm (N = 10240) -> swiglu -> gemm (N = 2560,
 //   K = 5120) -> residual (+ final norm)
 #include "device_common.h"
 #include "gemm.h"
@@ -211,6 +212,81 @@ __global__ __launch_bounds__(kRowThreads) void residual_kernel(const float* __re
     V8<T>::store(norm_out + row + c, r);
 }
 
+// DFlash2's block convolution fused with the post-attention residual: one
+// workgroup per sequence (8 block rows, 8 columns per thread).
+//   h[t]  = x[t] + sum of the W_O partials           (stored as T)
+//   h'[t] = h[t] + b + sum_{j < k, t - j >= 0} w[j] * h[t - j]   (from the
+//           stored h; stored as T into hc, the feed-forward residual)
+//   c[t]  = g * h'[t] / sqrt(mean(h'[t]^2) + eps)     (from the stored h')
+// k <= 8 (the block length).
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void residual_conv_kernel(const float* __restrict__ part, int ks, int M,
+                                                                     const T* __restrict__ x,
+                                                                     const T* __restrict__ w_conv, int k,
+                                                                     const T* __restrict__ b_conv,
+                                                                     T* __restrict__ hc, const T* __restrict__ g,
+                                                                     float eps, T* __restrict__ c_out) {
+    __shared__ float red[8][kRowThreads / 64];
+    const int64_t row0 = (int64_t)blockIdx.x * 8 * kD;
+    const int c = threadIdx.x * 8;
+    float h[8][8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) V8<T>::load(x + row0 + t * kD + c, h[t]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) add_parts8(part, ks, (int64_t)M * kD, row0 + t * kD + c, h[t]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[t][e] = round_as<T>(h[t][e]);
+    float bv[8];
+    V8<T>::load(b_conv + c, bv);
+    float y[8][8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[t][e] = bv[e];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {          // unrolled to the block length: static register indices
+        if (j >= k) break;
+        float wv[8];
+        V8<T>::load(w_conv + (int64_t)j * kD + c, wv);
+#pragma unroll
+        for (int t = j; t < 8; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[t][e] += wv[e] * h[t - j][e];
+    }
+    float ss[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        ss[t] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            y[t][e] = h[t][e] + y[t][e];
+        }
+        V8<T>::store(hc + row0 + t * kD + c, y[t]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            y[t][e] = round_as<T>(y[t][e]);
+            ss[t] += y[t][e] * y[t][e];
+        }
+        ss[t] = wave_sum(ss[t]);
+    }
+    if ((threadIdx.x & 63) == 0)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) red[t][threadIdx.x >> 6] = ss[t];
+    __syncthreads();
+    float gv[8];
+    V8<T>::load(g + c, gv);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const float tot = red[t][0] + red[t][1] + red[t][2] + red[t][3] + red[t][4];
+        const float rinv = 1.0f / sqrtf(tot * (1.0f / kD) + eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[t][e] = gv[e] * y[t][e] * rinv;
+        V8<T>::store(c_out + row0 + t * kD + c, y[t]);
+    }
+}
+
 // s = silu(gate) * up from the [gate | up] partials (5120 + 5120 columns).
 // 640 groups of 8 columns per row, 2 per thread.
 template <typename T>
@@ -269,7 +345,8 @@ hipError_t run_mlp(const dflash_mlp_args& a, const DraftMlpPlan& pl, char* ws, h
     const int M = 8 * a.B;
     T* ao = reinterpret_cast<T*>(ws + pl.off_ao);
     float* part = reinterpret_cast<float*>(ws + pl.off_part);
-    // The stored h lives in h_out when the caller wants a copy, else in the workspace.
+    // The feed-forward residual (h, or h' with the convolution) lives in h_out
+    // when the caller wants a copy, else in the workspace.
     T* h = a.h_out ? static_cast<T*>(a.h_out) : reinterpret_cast<T*>(ws + pl.off_h);
     T* c = reinterpret_cast<T*>(ws + pl.off_c);
     T* sw = reinterpret_cast<T*>(ws + pl.off_s);
@@ -278,8 +355,14 @@ hipError_t run_mlp(const dflash_mlp_args& a, const DraftMlpPlan& pl, char* ws, h
     heads_to_rows_kernel<T><<<M, kThreads, 0, s>>>(static_cast<const T*>(a.o), ao);
     const GemmParams g1 = gemm_params(ao, kQN, a.w_o, M, kD, kQN, pl.ks_o, a.dtype, part);
     if ((e = launch_gemm(g1, a.dtype, s)) != hipSuccess) return e;
-    residual_kernel<T><<<M, kRowThreads, 0, s>>>(part, g1.ks, M, static_cast<const T*>(a.x), h,
-                                               static_cast<const T*>(a.g_post), a.eps, c);
+    if (a.conv_k > 0)
+        residual_conv_kernel<T><<<a.B, kRowThreads, 0, s>>>(part, g1.ks, M, static_cast<const T*>(a.x),
+                                                          static_cast<const T*>(a.w_conv), a.conv_k,
+                                                          static_cast<const T*>(a.b_conv), h,
+                                                          static_cast<const T*>(a.g_post), a.eps, c);
+    else
+        residual_kernel<T><<<M, kRowThreads, 0, s>>>(part, g1.ks, M, static_cast<const T*>(a.x), h,
+                                                   static_cast<const T*>(a.g_post), a.eps, c);
 
     const GemmParams g2 = gemm_params(c, kD, a.w_gu, M, 2 * kInter, kD, pl.ks_gu, a.dtype, part);
     if ((e = launch_gemm(g2, a.dtype, s)) != hipSuccess) return e;

@@ -53,4 +53,8 @@ hipError_t launch_ring_append(const dflash_ring_args& a, hipStream_t s);
 size_t head_workspace_bytes(int B, int64_t V);
 hipError_t launch_head(const dflash_head_args& a, void* ws, hipStream_t s);
 
+// ---- DFlash2 path selector ----
+size_t paths_workspace_bytes(int B, int64_t V);
+hipError_t launch_paths(const dflash_paths_args& a, void* ws, hipStream_t s);
+
 }  // namespace dflash

@@ -100,6 +100,12 @@ def draft_layer_weights(seed, layer=0):
     }
 
 
+def conv_weights(seed, k):
+    """DFlash2 block convolution: taps [k, 2560] ~ N(0, 0.2^2) and bias
+    [2560] ~ N(0, 0.02^2)."""
+    return normal(seed, f"w_conv{k}", (k, D), std=0.2), normal(seed, f"b_conv{k}", (D,), std=0.02)
+
+
 def final_norm(seed):
     """Final RMSNorm gain [2560] after the last draft layer."""
     return normal(seed, "g_final", (D,), std=0.1, mean=1.0)

@@ -23,6 +23,11 @@
  *
  *   dflash_draft_head  block logits and the seven proposals
  *
+ * and DFlash2's candidate path selector (its block convolution is an option
+ * of dflash_draft_mlp):
+ *
+ *   dflash_draft_paths top-m candidates per position, entropies, top-P paths
+ *
  * Sources (web pages; cited by title and section):
  *   [E4B] "Nemotron 3.5 Bolt E4B: Block-Parallel Speculation with DFlash"
  *   [DF2] "DFlash & DFlash2: Block-Diffusion LLM-Speedup"
@@ -276,6 +281,15 @@ typedef struct dflash_qkv_args {
  * Every "stored" value is rounded to dtype once and the next step reads the
  * rounded value.  x_out may be x itself (in place); y_out and h_out must not
  * overlap x, o, x_out or each other.
+ *
+ * With conv_k > 0, DFlash2's depthwise block convolution ([DF2] "DFlash2",
+ * item 1: kernel width 3 or 5 between the attention and feed-forward
+ * sublayers) is applied to the stored h as a residual branch, causal over
+ * the eight block positions t = 0..7 of each sequence (nothing before the
+ * anchor):
+ *   h'[t] = h[t] + b_conv + sum_{j < conv_k, t - j >= 0} w_conv[j] * h[t - j]   (stored)
+ * and the rest of the layer reads h' in place of h (c, and the residual of
+ * x_out); h_out then receives h'.
  */
 typedef struct dflash_mlp_args {
     int32_t dtype;            /* DFLASH_BF16 or DFLASH_F32 */
@@ -290,7 +304,10 @@ typedef struct dflash_mlp_args {
     float eps;                /* RMSNorm epsilon (> 0) */
     void* x_out;              /* device [B][8][2560] layer output */
     void* y_out;              /* device [B][8][2560] final-norm output; required iff g_final != NULL */
-    void* h_out;              /* optional device [B][8][2560] copy of h (dtype); NULL = not written */
+    void* h_out;              /* optional device [B][8][2560] copy of h (h' with the convolution) (dtype); NULL = not written */
+    int32_t conv_k;           /* 0 = no convolution; else the kernel width, 1..8 */
+    const void* w_conv;       /* device [conv_k][2560] per-channel taps (tap j multiplies h[t - j]); required iff conv_k > 0 */
+    const void* b_conv;       /* device [2560] bias; required iff conv_k > 0 */
 } dflash_mlp_args;
 
 /*
@@ -354,6 +371,43 @@ typedef struct dflash_head_args {
     int32_t* draft_tokens;    /* device [B][7] proposals d_1..d_7, written */
 } dflash_head_args;
 
+/*
+ * dflash_draft_paths -- DFlash2's top-m candidate path selector.  [DF2]
+ * "DFlash2", item 2: the head yields the top-m candidates of every block
+ * position, a path (one candidate per position) is scored by the sum of its
+ * draft log-probabilities plus lambda times the positions' entropies, and
+ * the best paths are handed to the target.  For proposal positions
+ * k = 1..7 (rows 1..7 of each sequence's logits), with P_k = softmax of the
+ * stored row and H_k its entropy:
+ *   cand_ids[b][k-1][r]  = the r-th largest logit's id (r < m; ties to the lower id)
+ *   cand_logp[b][k-1][r] = log P_k(cand_ids[b][k-1][r]),   entropy[b][k-1] = H_k
+ *   paths[b][0..P)       = the P best rank tuples (r_1..r_7) by
+ *                          score = sum_k cand_logp[b][k-1][r_k] + lambda * sum_k H_k,
+ *                          best first, equal scores by the lexicographically
+ *                          smaller tuple; written as token ids
+ * The drafter proposes the block in one forward, so P_k does not depend on
+ * the candidates chosen before k: the score separates per position, and a
+ * beam of width P keeps exactly the top P.  Scores are accumulated in fp32.
+ * Rows 1..7 of dflash_draft_head's logits are the natural input
+ * (batch_stride = 8 V, row_stride = V).
+ */
+typedef struct dflash_paths_args {
+    int32_t dtype;            /* DFLASH_BF16 or DFLASH_F32 logits */
+    int32_t B;                /* sequences, 1..8192 */
+    int64_t V;                /* vocabulary, multiple of 8, m..2^24 */
+    const void* logits;       /* device; row r (0..7) of sequence b at b*batch_stride + r*row_stride; rows 1..7 read */
+    int64_t batch_stride;     /* elements, multiple of 8, >= 8 * row_stride */
+    int64_t row_stride;       /* elements, multiple of 8, >= V */
+    int32_t m;                /* candidates per position, 1..8 */
+    int32_t P;                /* paths, 1..64 and <= m^7 */
+    float lambda;             /* entropy weight */
+    int32_t* cand_ids;        /* device [B][7][m] */
+    float* cand_logp;         /* device [B][7][m] */
+    float* entropy;           /* device [B][7] */
+    int32_t* paths;           /* device [B][P][7] token ids, best path first */
+    float* scores;            /* device [B][P] */
+} dflash_paths_args;
+
 /* Library version (DFLASH_VERSION of the build). */
 int dflash_version(void);
 
@@ -363,7 +417,7 @@ const char* dflash_last_error(void);
 /* sizeof of the argument structs as compiled into the library:
  * kind 0 = dflash_fuse_args, 1 = dflash_attn_args, 2 = dflash_verify_args,
  * 3 = dflash_embed_args, 4 = dflash_qkv_args, 5 = dflash_mlp_args,
- * 6 = dflash_ring_args, 7 = dflash_head_args;
+ * 6 = dflash_ring_args, 7 = dflash_head_args, 8 = dflash_paths_args;
  * returns 0 for any other kind.  Lets bindings check their struct mirrors. */
 size_t dflash_args_size(int kind);
 
@@ -375,6 +429,7 @@ int dflash_verify_workspace_size(const dflash_verify_args* args, size_t* bytes);
 int dflash_draft_qkv_workspace_size(const dflash_qkv_args* args, size_t* bytes);
 int dflash_draft_mlp_workspace_size(const dflash_mlp_args* args, size_t* bytes);
 int dflash_draft_head_workspace_size(const dflash_head_args* args, size_t* bytes);
+int dflash_draft_paths_workspace_size(const dflash_paths_args* args, size_t* bytes);
 
 /* The three operations.  `workspace` must hold at least the size returned
  * above (it may be NULL when that size is 0); its contents are scratch. */
@@ -399,6 +454,10 @@ int dflash_ring_append(const dflash_ring_args* args, void* stream);
 /* Shared LM head and draft proposals. */
 int dflash_draft_head(const dflash_head_args* args, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* DFlash2 candidate path selector. */
+int dflash_draft_paths(const dflash_paths_args* args, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -38,7 +38,8 @@ def test_header_declares_every_operation():
               "dflash_verify_workspace_size", "dflash_last_error", "dflash_version",
               "dflash_args_size", "dflash_draft_embed", "dflash_draft_qkv", "dflash_draft_mlp",
               "dflash_draft_qkv_workspace_size", "dflash_draft_mlp_workspace_size", "dflash_ring_append",
-              "dflash_draft_head", "dflash_draft_head_workspace_size"):
+              "dflash_draft_head", "dflash_draft_head_workspace_size", "dflash_draft_paths",
+              "dflash_draft_paths_workspace_size"):
         assert f in fns
 
 
@@ -298,3 +299,40 @@ def test_draft_head_validation(lib):
     assert _call(lib, "dflash_draft_head", args(temperature=None), FAKE, n) == -1
     assert _call(lib, "dflash_draft_head", args(), FAKE, n - 1) == -4
     assert _call(lib, "dflash_draft_head", args(), None, 0) == -4
+
+
+def test_draft_paths_validation(lib):
+    from block_speculative_decoding_amd import _lib
+
+    def args(**kw):
+        a = _lib.PathsArgs()
+        a.dtype, a.B, a.V, a.m, a.P = 0, 64, 262144, 4, 16
+        a.batch_stride, a.row_stride = 8 * 262144, 262144
+        a.logits = a.cand_ids = a.cand_logp = a.entropy = a.paths = a.scores = FAKE
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+    rc, n = _ws(lib, "draft_paths", args())
+    assert rc == 0 and n == 64 * 7 * 16 * 80          # one 80-byte partial per 16384-entry chunk of a row
+    assert _ws(lib, "draft_paths", args(m=0))[0] == -1
+    assert _ws(lib, "draft_paths", args(m=9))[0] == -1
+    assert _ws(lib, "draft_paths", args(P=65))[0] == -1
+    assert _ws(lib, "draft_paths", args(m=1, P=2))[0] == -1      # only one path exists
+    assert _ws(lib, "draft_paths", args(m=2, P=64))[0] == 0      # 128 paths exist
+    assert _ws(lib, "draft_paths", args(V=262140))[0] == -1
+    assert _ws(lib, "draft_paths", args(V=3, row_stride=8, batch_stride=64))[0] == -1  # V < m
+    assert _ws(lib, "draft_paths", args(row_stride=262136))[0] == -1
+    assert _ws(lib, "draft_paths", args(batch_stride=7 * 262144))[0] == -1
+    assert _ws(lib, "draft_paths", args(dtype=4))[0] == -2
+    assert _call(lib, "dflash_draft_paths", args(paths=None), FAKE, n) == -1
+    assert _call(lib, "dflash_draft_paths", args(logits=FAKE + 2), FAKE, n) == -1
+    assert _call(lib, "dflash_draft_paths", args(), FAKE, n - 1) == -4
+
+
+def test_draft_mlp_conv_validation(lib):
+    rc, m = _ws(lib, "draft_mlp", _mlp_args())
+    assert _call(lib, "dflash_draft_mlp", _mlp_args(conv_k=9, w_conv=FAKE, b_conv=FAKE), FAKE, m) == -1
+    assert _call(lib, "dflash_draft_mlp", _mlp_args(conv_k=-1), FAKE, m) == -1
+    assert _call(lib, "dflash_draft_mlp", _mlp_args(conv_k=3, w_conv=FAKE), FAKE, m) == -1   # b_conv missing
+    assert b"b_conv" in lib.dflash_last_error()
+    assert _call(lib, "dflash_draft_mlp", _mlp_args(conv_k=3, b_conv=FAKE, w_conv=FAKE + 8), FAKE, m) == -1

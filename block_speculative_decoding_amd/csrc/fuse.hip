@@ -193,6 +193,19 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
     wait_lgkm<0>();
 
     // Lane holds column lr of each 32x32 block, rows 8*(r/4) + 4*lh + (r%4).
+    if (!KV && p.out_bf16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int gm = m0 + wr + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    const int gn = n0 + wc + kBstep * j + lr;
+                    if (gm < p.M) p.out_bf16[(int64_t)gm * p.N + gn] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
+                }
+        return;
+    }
     if (!KV) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -499,6 +512,12 @@ FusePlan fuse_plan(const dflash_fuse_args& a) {
     pl.ws_bytes = pl.off_part2 + (pl.big ? align256((size_t)M * 64 * sizeof(float2))
                                          : align256((size_t)pl.ks2 * M * N2 * 4));
     return pl;
+}
+
+hipError_t launch_gemm_big(const GemmParams& g, hipStream_t s) {
+    const int tiles = ((g.M + BMB - 1) / BMB) * (g.N / BNB);
+    gemm_bf16_big_kernel<false><<<(tiles + kXcds - 1) / kXcds * kXcds, kBigThreads, 0, s>>>(g, KvEpilogue{});
+    return hipGetLastError();
 }
 
 hipError_t launch_fuse(const dflash_fuse_args& a, const FusePlan& pl, void* ws, hipStream_t s) {

@@ -9,8 +9,9 @@
 //
 // Launch sequence:
 //   gemm    -- logits [8B][V] = y [8B][2560] . W_head^T, written in the
-//              storage type (the split-K kernel with one split and a direct
-//              bf16 output, or the fp32 kernel)
+//              storage type (bf16: the 256 x 256-tile kernel from 256 rows
+//              on, else the 128 x 128 kernel with one split; both with a
+//              direct bf16 output; or the fp32 kernel)
 //   sample  -- vocab-parallel over rows k = 1..7 of each sequence: greedy rows
 //              keep (max, lowest argmax); sampled rows the Gumbel-max key
 //              z / T - ln(-ln u) with u from stream 2 of the uniform layout,
@@ -142,7 +143,10 @@ hipError_t launch_head(const dflash_head_args& a, void* ws, hipStream_t s) {
     gemm_set_split(g, a.dtype, 1);
     if (a.dtype == DFLASH_BF16) g.out_bf16 = static_cast<uint16_t*>(a.logits);
     else g.part = static_cast<float*>(a.logits);
-    hipError_t e = launch_gemm(g, a.dtype, s);
+    // 256 x 256 tiles once there are 256 rows: half the operand traffic per
+    // flop of the 128 x 128 kernel.
+    const bool big = a.dtype == DFLASH_BF16 && M >= 256 && a.V % 256 == 0;
+    hipError_t e = big ? launch_gemm_big(g, s) : launch_gemm(g, a.dtype, s);
     if (e != hipSuccess) return e;
 
     HeadParams p;

@@ -65,9 +65,11 @@ def _run(y_t, w_t, temp, dtype):
     return logits.double().cpu().numpy(), d.cpu().numpy()
 
 
-@pytest.mark.parametrize("dtype,B,V", [(BF16, 5, 3 * 8192 + 384), (F32, 3, 8192 + 128), (BF16, 1, 128)])
+@pytest.mark.parametrize("dtype,B,V", [(BF16, 5, 3 * 8192 + 384), (F32, 3, 8192 + 128), (BF16, 1, 128),
+                                        (BF16, 40, 8192 + 256)])
 def test_head_logits_and_proposals(dtype, B, V):
-    # Several 128-row and 8192-entry chunks with ragged tails (M = 8B rows).
+    # Several 128-row and 8192-entry chunks with ragged tails (M = 8B rows);
+    # B = 40 (M = 320) takes the 256 x 256-tile projection with a ragged tile.
     y_t, y = _stored(synth.head_input(SEED, B), dtype)
     w_t, w = _stored(synth.head_weight(SEED, V), dtype)
     temp = synth.head_temperatures(SEED, B)

@@ -85,7 +85,7 @@ def log(msg):
 class Workload:
     """Serving-batch inputs on the device."""
 
-    def __init__(self, torch, dfl, synth):
+    def __init__(self, torch, dfl, synth, ctx=None, split_tokens=0):
         self.torch = torch
         dev = torch.device("cuda:0")
         bf = torch.bfloat16
@@ -94,9 +94,10 @@ class Workload:
         def d(x, dt=bf):
             return torch.from_numpy(np.ascontiguousarray(x)).to(dt).to(dev)
 
-        # Paged caches: ctx 8192 + up to 8 new rows per sequence, shuffled pages.
+        # Paged caches: ctx 8192 (or the given lengths) + up to 8 new rows per
+        # sequence, shuffled pages.
         self.n_new = synth.new_rows(SEED, B)
-        self.ctx = np.full(B, S_CTX, dtype=np.int32)
+        self.ctx = np.full(B, S_CTX, dtype=np.int32) if ctx is None else np.asarray(ctx, dtype=np.int32)
         self.lens = (self.ctx + self.n_new).astype(np.int32)
         table, npages = synth.page_table(SEED, self.ctx + 8)
         self.table_np = table
@@ -129,7 +130,8 @@ class Workload:
         for l in range(LAYERS):
             bl = {k: d(v) for k, v in self.blk_np[l].items()}
             p = dfl.prepare_block_attn(bl["q"], bl["k_blk"], bl["v_blk"], bl["gq"], bl["gk"], self.kc[l],
-                                       self.vc[l], self.block_table, self.ctx_len, workspace=ws)
+                                       self.vc[l], self.block_table, self.ctx_len, split_tokens=split_tokens,
+                                       workspace=ws)
             ws = p.workspace  # one workspace shared by the five layers (same stream)
             self.attn.append(p)
         # Logits: N(0, 4^2) target, draft = target + N(0, 1); half greedy, half T = 0.7.
@@ -421,6 +423,32 @@ def draft_measurement(torch, dfl, synth, wl):
                                 "weight_bytes": per_layer * 2 * LAYERS}}
 
 
+def ragged_measurement(torch, dfl, synth):
+    """The serving batch with ragged cached contexts, uniform on [1024, 8192]
+    (mean ~4.6k) on shuffled pages: whole cycles (fusion of the new rows, 5
+    attention layers, verification) eagerly, and attention per layer; once
+    with the automatic split (one split per sequence: the batch alone fills
+    the chip, and the host does not see the lengths) and once with 2048-token
+    splits (a caller that knows its lengths; splits past a sequence's end
+    exit at once)."""
+    ctx = synth.ragged_lengths(SEED + 5, B, 1024, 8192)
+    out = {}
+    for split in (0, 2048):
+        wl = Workload(torch, dfl, synth, ctx=ctx, split_tokens=split)
+        step_ms = timed(torch, lambda: wl.step(0), warmup=2, reps=10)
+        a_ms = timed(torch, lambda: [a() for a in wl.attn], warmup=2, reps=10) / LAYERS
+        a_bytes = attn_bytes(wl.lens)
+        out["serving_ragged_b64" + ("_split2048" if split else "")] = {
+            "cycles/s_eager": round(1000.0 / step_ms, 1), "ms_per_step_eager": round(step_ms, 4),
+            "mean_ctx": round(float(np.mean(wl.lens)), 1), "attn_ms": round(a_ms, 4),
+            "attn_GB/s": round(a_bytes / (a_ms * 1e-3) / 1e9, 1),
+            "attn_hbm_frac": round(a_bytes / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "split_tokens": split if split else "auto (one split per sequence)"}
+        del wl
+        torch.cuda.empty_cache()
+    return out
+
+
 def head_measurement(torch, dfl, synth):
     """The shared LM head over the serving batch's block rows (B = 64, 8 rows
     each, V = 262144) and the seven proposals per sequence, once with the
@@ -585,6 +613,8 @@ def main():
         res["kernels"].update(window_measurement(torch, dfl, wl))
         log("[bench] draft forward around attention: B=64, 5 layers")
         res["kernels"].update(draft_measurement(torch, dfl, synth, wl))
+        log("[bench] serving batch with ragged contexts in [1024, 8192]")
+        res["kernels"].update(ragged_measurement(torch, dfl, synth))
         log("[bench] shared LM head and draft proposals: B=64, V=262144")
         res["kernels"].update(head_measurement(torch, dfl, synth))
     if not args.no_cpu_baseline:

@@ -13,6 +13,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Natural log through the hardware log2 (v_log_f32, about 1 ulp for normal
+// inputs): x must be a positive normal float.
+__device__ __forceinline__ float fast_ln(float x) { return __builtin_amdgcn_logf(x) * kLn2; }
+
 // bfloat16 is stored as raw uint16 bits; widening is exact.
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);

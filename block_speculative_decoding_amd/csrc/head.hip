@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void draft_sample_kernel(HeadParams p) {
             const int j = (int)((i0 + e) & 7);
             const uint64_t wd = words[j >> 1];
             const float u = (j & 1) ? word_to_uniform_lo(wd) : word_to_uniform(wd);
-            better(best, bi, f[e] * invT - logf(-logf(u)), (int)(i0 + e));
+            better(best, bi, f[e] * invT - fast_ln(-fast_ln(u)), (int)(i0 + e));
         }
     }
 #pragma unroll

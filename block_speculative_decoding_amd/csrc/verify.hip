@@ -24,7 +24,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRows = 15;            // 8 target rows + 7 draft rows per sequence
 constexpr int64_t kStatsChunk = 32768;
-constexpr int64_t kSampleChunk = 8192;
+constexpr int64_t kSampleChunk = 2048;   // the draw touches few rows: small chunks spread them over the chip
 
 struct StatPart { float m; float s; int idx; int pad; };
 struct SamplePart { float key; int idx; float keyp; int idxp; };
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(Params p) {
                 const float pv = __builtin_amdgcn_exp2f(xt) * ds.inv_st;
                 const float qv = __builtin_amdgcn_exp2f(scaled(zq[e] - ds.mq, sc)) * ds.inv_sq;
                 const float rr = pv - qv;
-                w[it][e] = rr > 0.f ? logf(rr) : -INFINITY;
+                w[it][e] = rr > 0.f ? fast_ln(rr) : -INFINITY;
                 wp[it][e] = xt * kLn2;
             } else {
                 w[it][e] = zt[e] * invT;
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(Params p) {
             const int j = (int)((i0 + e) & 7);
             const uint64_t wd = words[j >> 1];
             const float u = (j & 1) ? word_to_uniform_lo(wd) : word_to_uniform(wd);
-            const float key = wv - logf(-logf(u));
+            const float key = wv - fast_ln(-fast_ln(u));
             if (use_resid) combine_arg(best, bi, key, (int)(i0 + e));
             else combine_arg(bestp, bip, key, (int)(i0 + e));
         }

@@ -79,12 +79,21 @@ __global__ __launch_bounds__(kThreads) void draft_sample_kernel(HeadParams p) {
     const uint64_t ctr1 = 8ull * (uint64_t)b + (uint64_t)k;
     float best = -INFINITY;
     int bi = 0x7FFFFFFF;
-    for (int64_t i0 = c0 + (int64_t)threadIdx.x * N; i0 < c1; i0 += (int64_t)kThreads * N) {
-        float f[N];
-        Vec<T>::load(z + i0, f);
+    // Every load of the thread is issued before any is used.
+    constexpr int kIt = kChunk / (kThreads * N);
+    float f[kIt][N];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+        const int64_t i0 = c0 + ((int64_t)it * kThreads + threadIdx.x) * N;
+        if (i0 < c1) Vec<T>::load(z + i0, f[it]);
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+        const int64_t i0 = c0 + ((int64_t)it * kThreads + threadIdx.x) * N;
+        if (i0 >= c1) continue;
         if (greedy) {
 #pragma unroll
-            for (int e = 0; e < N; ++e) better(best, bi, f[e], (int)(i0 + e));
+            for (int e = 0; e < N; ++e) better(best, bi, f[it][e], (int)(i0 + e));
             continue;
         }
         // Entry j of an 8-entry group uses half j % 2 of word j / 2 of the
@@ -97,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void draft_sample_kernel(HeadParams p) {
             const int j = (int)((i0 + e) & 7);
             const uint64_t wd = words[j >> 1];
             const float u = (j & 1) ? word_to_uniform_lo(wd) : word_to_uniform(wd);
-            better(best, bi, f[e] * invT - fast_ln(-fast_ln(u)), (int)(i0 + e));
+            better(best, bi, f[it][e] * invT - fast_ln(-fast_ln(u)), (int)(i0 + e));
         }
     }
 #pragma unroll

@@ -46,7 +46,8 @@ struct PathParams {
     int64_t bstride, rstride, V;
     int B, m, P;
     float lam;
-    int nch;
+    int nch;               // stats workgroups per row (kChunk entries each)
+    int nsub;              // partials per row (one per wave: kChunk / 4 entries each)
     ChunkPart* part;
     int32_t* cand_ids;
     float* cand_logp;
@@ -102,52 +103,138 @@ __device__ __forceinline__ Stat stat_merge(Stat a, Stat b) {
     return r;
 }
 
-// Wave-wide first entry in (value, index) order; every lane gets it.
-__device__ __forceinline__ void wave_first(float& v, int& i) {
+// Cross-lane moves through DPP (no LDS round trip): lanes a row mask leaves
+// out, or whose source lane does not exist, receive the identity `id`.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_f(float x, float id) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, id), __builtin_bit_cast(int, x),
+                                                                 CTRL, ROWS, 0xf, false));
+}
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ int dpp_i(int x, int id) {
+    return __builtin_amdgcn_update_dpp(id, x, CTRL, ROWS, 0xf, false);
+}
+// The reduction order: swap within pairs, within quads, mirror within
+// half-rows and rows (every lane of a 16-lane row then holds the row's
+// result), then row 1 <- lane 15 and row 3 <- lane 47 (row_bcast:15, rows 1
+// and 3), row 3 <- lane 31 (row_bcast:31, rows 2 and 3): lane 63 ends with
+// the wave's result, read back as a uniform value.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ void first_step(float& v, int& i) {
+    const float v2 = dpp_f<CTRL, ROWS>(v, -INFINITY);
+    const int i2 = dpp_i<CTRL, ROWS>(i, 0x7FFFFFFF);
+    if (before(v2, i2, v, i)) { v = v2; i = i2; }
+}
+
+// Lists of a compile-time length L, in order: insertion as one
+// compare-and-select pass (no branches, so no copies of the list around
+// them); an entry that comes after all L drops out.
+template <int L>
+__device__ __forceinline__ void insert_n(float* lv, int* li, float v, int i) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float v2 = __shfl_xor(v, o);
-        const int i2 = __shfl_xor(i, o);
-        if (before(v2, i2, v, i)) { v = v2; i = i2; }
+    for (int s = 0; s < L; ++s) {
+        const bool b = before(v, i, lv[s], li[s]);
+        const float ov = lv[s];
+        const int oi = li[s];
+        lv[s] = b ? v : ov;
+        li[s] = b ? i : oi;
+        v = b ? ov : v;
+        i = b ? oi : i;
     }
 }
 
-__device__ __forceinline__ Stat wave_stat(Stat s) {
+template <int L>
+__device__ __forceinline__ void pop_n(float* lv, int* li) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        Stat t;
-        t.m = __shfl_xor(s.m, o);
-        t.s0 = __shfl_xor(s.s0, o);
-        t.s1 = __shfl_xor(s.s1, o);
-        s = stat_merge(s, t);
+    for (int s = 0; s < L - 1; ++s) {
+        lv[s] = lv[s + 1];
+        li[s] = li[s + 1];
     }
+    lv[L - 1] = -INFINITY;
+    li[L - 1] = 0x7FFFFFFF;
+}
+
+// Wave-wide first entry in (value, index) order; every lane gets it.
+__device__ __forceinline__ void wave_first(float& v, int& i) {
+    first_step<kDppXor1>(v, i);
+    first_step<kDppXor2>(v, i);
+    first_step<kDppHalfMirror>(v, i);
+    first_step<kDppMirror>(v, i);
+    first_step<kDppBcast15, 0xA>(v, i);
+    first_step<kDppBcast31, 0xC>(v, i);
+    v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+    i = __builtin_amdgcn_readlane(i, 63);
+}
+
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ void stat_step(Stat& s) {
+    Stat t;
+    t.m = dpp_f<CTRL, ROWS>(s.m, -INFINITY);
+    t.s0 = dpp_f<CTRL, ROWS>(s.s0, 0.f);
+    t.s1 = dpp_f<CTRL, ROWS>(s.s1, 0.f);
+    s = stat_merge(s, t);
+}
+
+__device__ __forceinline__ Stat wave_stat(Stat s) {
+    stat_step<kDppXor1>(s);
+    stat_step<kDppXor2>(s);
+    stat_step<kDppHalfMirror>(s);
+    stat_step<kDppMirror>(s);
+    stat_step<kDppBcast15, 0xA>(s);
+    stat_step<kDppBcast31, 0xC>(s);
+    s.m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s.m), 63));
+    s.s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s.s0), 63));
+    s.s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s.s1), 63));
     return s;
+}
+
+// Loaded vectors stay in their storage form (bf16: 8 values in 4 registers)
+// and are unpacked in each pass: half the registers of fp32 copies, so
+// more waves share a SIMD to cover the loads' latency.
+// Wave-wide max / sum of one float, uniform result.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float max_step(float x) { return fmaxf(x, dpp_f<CTRL, ROWS>(x, -INFINITY)); }
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float sum_step(float x) { return x + dpp_f<CTRL, ROWS>(x, 0.f); }
+__device__ __forceinline__ float wave_max_dpp(float x) {
+    x = max_step<kDppXor1>(x); x = max_step<kDppXor2>(x); x = max_step<kDppHalfMirror>(x);
+    x = max_step<kDppMirror>(x); x = max_step<kDppBcast15, 0xA>(x); x = max_step<kDppBcast31, 0xC>(x);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+    x = sum_step<kDppXor1>(x); x = sum_step<kDppXor2>(x); x = sum_step<kDppHalfMirror>(x);
+    x = sum_step<kDppMirror>(x); x = sum_step<kDppBcast15, 0xA>(x); x = sum_step<kDppBcast31, 0xC>(x);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
 template <typename T> struct Vec;
 template <> struct Vec<uint16_t> {
     static constexpr int N = 8;
-    static __device__ __forceinline__ void load(const uint16_t* p, float* f) {
-        const uint4 w = *reinterpret_cast<const uint4*>(p);
+    using Raw = uint4;
+    static __device__ __forceinline__ Raw load(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+    static __device__ __forceinline__ Raw neg_inf() { return make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u); }
+    static __device__ __forceinline__ void unpack(const Raw& w, float* f) {
         f[0] = lo_bf16(w.x); f[1] = hi_bf16(w.x); f[2] = lo_bf16(w.y); f[3] = hi_bf16(w.y);
         f[4] = lo_bf16(w.z); f[5] = hi_bf16(w.z); f[6] = lo_bf16(w.w); f[7] = hi_bf16(w.w);
     }
 };
 template <> struct Vec<float> {
     static constexpr int N = 4;
-    static __device__ __forceinline__ void load(const float* p, float* f) {
-        const float4 w = *reinterpret_cast<const float4*>(p);
-        f[0] = w.x; f[1] = w.y; f[2] = w.z; f[3] = w.w;
-    }
+    using Raw = float4;
+    static __device__ __forceinline__ Raw load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+    static __device__ __forceinline__ Raw neg_inf() { return make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY); }
+    static __device__ __forceinline__ void unpack(const Raw& w, float* f) { f[0] = w.x; f[1] = w.y; f[2] = w.z; f[3] = w.w; }
 };
 
-template <typename T>
+template <typename T, int M>     // M = m, the candidates kept
 __global__ __launch_bounds__(kThreads) void path_stats_kernel(PathParams p) {
+    // Each wave is independent: it covers kSub entries of a row and writes its
+    // own partial (no LDS, no barrier); the select kernel merges them.
     constexpr int kWaves = kThreads / 64;
-    __shared__ float s_v[kWaves][kList];
-    __shared__ int s_i[kWaves][kList];
-    __shared__ float s_st[kWaves][3];
-    const int chunk = blockIdx.x % p.nch;
+    const int chunk = blockIdx.x % p.nch;        // p.nch: workgroup chunks per row
     const int row = blockIdx.x / p.nch;          // b * 7 + (k - 1)
     const int b = row / kRows, k = row % kRows + 1;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -156,40 +243,37 @@ __global__ __launch_bounds__(kThreads) void path_stats_kernel(PathParams p) {
     constexpr int kSub = kChunk / kWaves;        // entries per wave
     constexpr int kIt = kSub / (64 * N);
     // V <= 2^24: entry indices fit in int.
-    const int c1 = (int)min(p.V, (int64_t)chunk * kChunk + kChunk);
     const int w0 = chunk * kChunk + wave * kSub;
-    float f[kIt][N];
+    if (w0 >= p.V) return;                       // past the row (the last chunk only)
+    const int c1 = (int)min(p.V, (int64_t)w0 + kSub);
+    typename Vec<T>::Raw raw[kIt];
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
         const int i0 = w0 + (it * 64 + lane) * N;
-        if (i0 < c1) Vec<T>::load(z + i0, f[it]);
-        else
-#pragma unroll
-            for (int e = 0; e < N; ++e) f[it][e] = -INFINITY;
+        raw[it] = i0 < c1 ? Vec<T>::load(z + i0) : Vec<T>::neg_inf();
     }
-    // Lane maximum, then the threshold: the m-th largest of the 64 lane
-    // maxima.  Those m values are entries of the wave's range, so its m best
-    // entries all have values >= the threshold (equal values are ordered by
-    // index inside the lists).
     float vm[kIt];                           // maximum of each loaded vector
     float mx = -INFINITY;
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
-        vm[it] = f[it][0];
+        float f[N];
+        Vec<T>::unpack(raw[it], f);
+        vm[it] = f[0];
 #pragma unroll
-        for (int e = 1; e < N; ++e) vm[it] = fmaxf(vm[it], f[it][e]);
+        for (int e = 1; e < N; ++e) vm[it] = fmaxf(vm[it], f[e]);
         mx = fmaxf(mx, vm[it]);
     }
+    // Threshold: after M rounds that each take the largest remaining lane
+    // maximum (every lane holding it), tv is at most the M-th largest lane
+    // maximum.  At least M entries of the wave's range are >= tv, so its M
+    // best entries all are.
     float tv = mx;
     {
         float ov = mx;
-        int ol = lane;
-        for (int r = 0; r < p.m; ++r) {
-            float v = ov;
-            int l = ol;
-            wave_first(v, l);
-            tv = v;
-            if (l == lane) ov = -INFINITY;   // this lane's maximum is taken
+#pragma unroll
+        for (int r = 0; r < M; ++r) {
+            tv = wave_max_dpp(ov);
+            if (ov == tv) ov = -INFINITY;
         }
     }
     // Softmax sums relative to the lane maximum on the hardware exp2
@@ -197,71 +281,66 @@ __global__ __launch_bounds__(kThreads) void path_stats_kernel(PathParams p) {
     // logits give exactly 0).
     constexpr float kLog2e = 1.4426950408889634f;
     const float ref = mx == -INFINITY ? 0.f : mx * kLog2e;
-    float s0 = 0.f, s1 = 0.f;
+    // Opaque to the compiler: the unpacked copies of the maximum pass are not
+    // kept alive until here (they would double the registers).
 #pragma unroll
     for (int it = 0; it < kIt; ++it)
+        asm volatile("" : "+v"(raw[it].x), "+v"(raw[it].y), "+v"(raw[it].z), "+v"(raw[it].w));
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+        float f[N];
+        Vec<T>::unpack(raw[it], f);
 #pragma unroll
         for (int e = 0; e < N; ++e) {
-            const float d2 = fmaxf(fmaf(f[it][e], kLog2e, -ref), -200.f);
+            const float d2 = fmaxf(fmaf(f[e], kLog2e, -ref), -200.f);
             const float ex = __builtin_amdgcn_exp2f(d2);
             s0 += ex;
             s1 = fmaf(ex, d2, s1);
         }
-    Stat st = {mx, s0, s1 * (1.0f / kLog2e)};
+    }
+    // The wave's statistics: rescale every lane's sums to the wave maximum,
+    // then add them up.
+    const float wm = wave_max_dpp(mx);
+    {
+        const float dm = mx == -INFINITY ? 0.f : (mx - wm) * kLog2e;   // <= 0, in log2 units
+        const float sc = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(dm);
+        s1 = (s1 + dm * s0) * sc;                                       // still in log2 units
+        s0 *= sc;
+    }
+    s0 = wave_sum_dpp(s0);
+    s1 = wave_sum_dpp(s1);
     // Few vectors hold an entry that passes the threshold: re-read those (the
-    // row is in L2) and insert their passing entries, so that the insertion
-    // code appears N times rather than once per entry.  Padding past V is
+    // row is in L2) and insert their passing entries.  Padding past V is
     // never admitted.
     uint32_t vmask = 0;
 #pragma unroll
     for (int it = 0; it < kIt; ++it)
         if (vm[it] >= tv) vmask |= 1u << it;
-    float lv[kList];
-    int li[kList];
+    float lv[M];
+    int li[M];
 #pragma unroll
-    for (int s = 0; s < kList; ++s) { lv[s] = -INFINITY; li[s] = 0x7FFFFFFF; }
+    for (int s = 0; s < M; ++s) { lv[s] = -INFINITY; li[s] = 0x7FFFFFFF; }
     while (vmask) {
         const int it = __builtin_ctz(vmask);
         vmask &= vmask - 1;
         const int i0 = w0 + (it * 64 + lane) * N;
         if (i0 >= c1) continue;
         float g[N];
-        Vec<T>::load(z + i0, g);
+        Vec<T>::unpack(Vec<T>::load(z + i0), g);
 #pragma unroll
-        for (int e = 0; e < N; ++e)
-            if (g[e] >= tv) list_insert(lv, li, g[e], i0 + e);
+        for (int e = 0; e < N; ++e) insert_n<M>(lv, li, g[e] >= tv ? g[e] : -INFINITY, g[e] >= tv ? i0 + e : 0x7FFFFFFF);
     }
-    st = wave_stat(st);
-    for (int r = 0; r < p.m; ++r) {
+    ChunkPart* out = p.part + (int64_t)row * p.nsub + chunk * kWaves + wave;
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
         float v = lv[0];
         int i = li[0];
         wave_first(v, i);
-        if (li[0] == i && lv[0] == v) list_pop(lv, li);
-        if (lane == 0) { s_v[wave][r] = v; s_i[wave][r] = i; }
+        if (li[0] == i && lv[0] == v) pop_n<M>(lv, li);
+        if (lane == 0) { out->val[r] = v; out->idx[r] = i; }
     }
-    if (lane == 0) { s_st[wave][0] = st.m; s_st[wave][1] = st.s0; s_st[wave][2] = st.s1; }
-    __syncthreads();
-    if (wave != 0) return;
-    // Wave 0 merges the four waves' lists and statistics.
-    float v = -INFINITY;
-    int i = 0x7FFFFFFF;
-    if (lane < kWaves * p.m) { v = s_v[lane / p.m][lane % p.m]; i = s_i[lane / p.m][lane % p.m]; }
-    ChunkPart* out = p.part + (int64_t)row * p.nch + chunk;
-    for (int r = 0; r < p.m; ++r) {
-        float fv = v;
-        int fi = i;
-        wave_first(fv, fi);
-        if (i == fi && v == fv) { v = -INFINITY; i = 0x7FFFFFFF; }
-        if (lane == 0) { out->val[r] = fv; out->idx[r] = fi; }
-    }
-    if (lane == 0) {
-        Stat t = {s_st[0][0], s_st[0][1], s_st[0][2]};
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) t = stat_merge(t, Stat{s_st[w][0], s_st[w][1], s_st[w][2]});
-        out->mx = t.m;
-        out->s0 = t.s0;
-        out->s1 = t.s1;
-    }
+    if (lane == 0) { out->mx = wm; out->s0 = s0; out->s1 = s1 * (1.0f / kLog2e); }
 }
 
 constexpr int kSelThreads = 512;   // wave k < 7 merges row k; all take part in the beam
@@ -279,13 +358,13 @@ __global__ __launch_bounds__(kSelThreads) void path_select_kernel(PathParams p) 
     const int m = p.m;
     if (wave < kRows) {
         const int k = wave;
-        const ChunkPart* part = p.part + ((int64_t)b * kRows + k) * p.nch;
+        const ChunkPart* part = p.part + ((int64_t)b * kRows + k) * p.nsub;
         Stat st = {-INFINITY, 0.f, 0.f};
         float lv[kList];
         int li[kList];
 #pragma unroll
         for (int s = 0; s < kList; ++s) { lv[s] = -INFINITY; li[s] = 0x7FFFFFFF; }
-        for (int c = lane; c < p.nch; c += 64) {
+        for (int c = lane; c < p.nsub; c += 64) {
             st = stat_merge(st, Stat{part[c].mx, part[c].s0, part[c].s1});
             for (int r = 0; r < m; ++r) list_insert(lv, li, part[c].val[r], part[c].idx[r]);
         }
@@ -363,9 +442,11 @@ __global__ __launch_bounds__(kSelThreads) void path_select_kernel(PathParams p) 
 
 }  // namespace
 
+constexpr int kSubEntries = kChunk / (kThreads / 64);
+
 size_t paths_workspace_bytes(int B, int64_t V) {
-    const int64_t nch = (V + kChunk - 1) / kChunk;
-    return ((size_t)B * kRows * nch * sizeof(ChunkPart) + 255) & ~(size_t)255;
+    const int64_t nsub = (V + kSubEntries - 1) / kSubEntries;
+    return ((size_t)B * kRows * nsub * sizeof(ChunkPart) + 255) & ~(size_t)255;
 }
 
 hipError_t launch_paths(const dflash_paths_args& a, void* ws, hipStream_t s) {
@@ -377,6 +458,7 @@ hipError_t launch_paths(const dflash_paths_args& a, void* ws, hipStream_t s) {
     p.B = a.B; p.m = a.m; p.P = a.P;
     p.lam = a.lambda;
     p.nch = (int)((a.V + kChunk - 1) / kChunk);
+    p.nsub = (int)((a.V + kSubEntries - 1) / kSubEntries);
     p.part = static_cast<ChunkPart*>(ws);
     p.cand_ids = a.cand_ids;
     p.cand_logp = a.cand_logp;
@@ -384,8 +466,18 @@ hipError_t launch_paths(const dflash_paths_args& a, void* ws, hipStream_t s) {
     p.paths = a.paths;
     p.scores = a.scores;
     const int grid = a.B * kRows * p.nch;
-    if (a.dtype == DFLASH_BF16) path_stats_kernel<uint16_t><<<grid, kThreads, 0, s>>>(p);
-    else path_stats_kernel<float><<<grid, kThreads, 0, s>>>(p);
+    const bool bf = a.dtype == DFLASH_BF16;
+    switch (a.m) {
+#define DFLASH_PATHS_M(MM)                                                                     \
+    case MM:                                                                                   \
+        if (bf) path_stats_kernel<uint16_t, MM><<<grid, kThreads, 0, s>>>(p);                  \
+        else path_stats_kernel<float, MM><<<grid, kThreads, 0, s>>>(p);                        \
+        break;
+        DFLASH_PATHS_M(1) DFLASH_PATHS_M(2) DFLASH_PATHS_M(3) DFLASH_PATHS_M(4)
+        DFLASH_PATHS_M(5) DFLASH_PATHS_M(6) DFLASH_PATHS_M(7) DFLASH_PATHS_M(8)
+#undef DFLASH_PATHS_M
+        default: return hipErrorInvalidValue;
+    }
     path_select_kernel<<<a.B, kSelThreads, 0, s>>>(p);
     return hipGetLastError();
 }

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void draft_pick_kernel(HeadParams p) {
                                                      p.part[(int64_t)row * p.nch + c].idx);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) better(best, bi, __shfl_xor(best, o), __shfl_xor(bi, o));
-    if (lane == 0) p.d[row] = bi;
+    if (lane == 0) p.d[row] = bi == 0x7FFFFFFF ? -1 : bi;   // no finite key (non-finite logits): -1
 }
 
 }  // namespace

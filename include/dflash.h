@@ -368,7 +368,8 @@ typedef struct dflash_head_args {
     uint64_t seed;
     uint64_t offset;          /* per-cycle counter word */
     void* logits;             /* device [B][8][V] (dtype), written */
-    int32_t* draft_tokens;    /* device [B][7] proposals d_1..d_7, written */
+    int32_t* draft_tokens;    /* device [B][7] proposals d_1..d_7, written (-1 if a row has no finite key,
+                                 which only non-finite inputs cause; dflash_spec_verify rejects it) */
 } dflash_head_args;
 
 /*

@@ -1,6 +1,6 @@
 """GPU parity of DFlash2's variants against the oracle.
 
-Block convolution (dflash_draft_mlp with conv_k = 3 or 5): x_out, y and the
+Block convolution (dflash_draft_mlp with conv_k = 3, 5 and the extremes 1, 8): x_out, y and the
 stored h' against the oracle's chain from the same synthetic inputs.  bf16
 bounds are those of the plain layer, plus one term: the stored h may be one
 bf16 step from the oracle's.  A worst-case step in each of the k rows a
@@ -39,7 +39,7 @@ def _conv_extra(h_ref, w_conv, B):
     return e.reshape(B * 8, -1)
 
 
-@pytest.mark.parametrize("B,k", [(3, 3), (40, 5), (1, 5)])
+@pytest.mark.parametrize("B,k", [(3, 3), (40, 5), (1, 5), (2, 1), (2, 8)])
 def test_conv_layer_bf16(B, k):
     import block_speculative_decoding_amd as dfl
     seed = 40 + k

@@ -111,4 +111,23 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Cross-lane moves through DPP (no LDS round trip): lanes a row mask leaves
+// out, or whose source lane does not exist, receive the identity `id`.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_f(float x, float id) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, id), __builtin_bit_cast(int, x),
+                                                                 CTRL, ROWS, 0xf, false));
+}
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ int dpp_i(int x, int id) {
+    return __builtin_amdgcn_update_dpp(id, x, CTRL, ROWS, 0xf, false);
+}
+// The reduction order: swap within pairs, within quads, mirror within
+// half-rows and rows (every lane of a 16-lane row then holds the row's
+// result), then row 1 <- lane 15 and row 3 <- lane 47 (row_bcast:15, rows 1
+// and 3), row 3 <- lane 31 (row_bcast:31, rows 2 and 3): lane 63 ends with
+// the wave's result, read back as a uniform value.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
 }  // namespace dflash

@@ -26,6 +26,7 @@
 
 #include "device_common.h"
 #include "gemm.h"
+#include "head_sample.h"
 #include "kernels.h"
 
 namespace dflash {
@@ -74,8 +75,12 @@ struct KvEpilogue {
     void* vc[5];
 };
 
-template <bool KV>
-__global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParams p, KvEpilogue ep) {
+// MODE 0: fp32 partials to p.part (the fusion GEMM); 1: the K/V epilogue
+// (ep); 2: the shared head's epilogue (hp): bf16 logits through LDS and the
+// draft keys of its rows.
+template <int MODE>
+__global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParams p, KvEpilogue ep, HeadEpilogue hp) {
+    constexpr bool KV = MODE == 1;
     const int tiles_m = (p.M + BMB - 1) / BMB, tiles_n = p.N / BNB;
     const TileId t = tile_id(p, tiles_m, tiles_n);
     if (!t.valid) return;
@@ -193,17 +198,63 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
     wait_lgkm<0>();
 
     // Lane holds column lr of each 32x32 block, rows 8*(r/4) + 4*lh + (r%4).
-    if (!KV && p.out_bf16) {
+    if (MODE == 2) {
+        // Round the tile to bf16 into LDS ([256 rows][256 columns]; 16-byte
+        // chunk c of row r at c ^ (r % 32)), then read it back in 16-byte
+        // chunks: each is stored to the logits and its 8 keys
+        // (head_sample.h) are folded into one (key, index) per row of the
+        // tile.
+        // The temperatures of the tile's 32 sequences, read once (after the
+        // operand stages, in the 4 KiB the K/V epilogue uses for row sums).
+        float* s_temp = reinterpret_cast<float*>(lds + 2 * kBigStageBytes / 16);
+        if (tid < BMB / 8) {
+            const int bq = (m0 >> 3) + tid;
+            s_temp[tid] = bq < (p.M >> 3) ? hp.temp[bq] : 0.f;
+        }
+        __syncthreads();  // every wave is done with the operand stages
+        uint16_t* st = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int gm = m0 + wr + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    const int gn = n0 + wc + kBstep * j + lr;
-                    if (gm < p.M) p.out_bf16[(int64_t)gm * p.N + gn] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
+                    const int row = wr + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    const int col = wc + kBstep * j + lr;
+                    st[row * 256 + 8 * ((col >> 3) ^ (row & 31)) + (col & 7)] =
+                        (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
                 }
+        __syncthreads();
+        // Four threads per row, 64 columns (eight chunks) each; two passes of
+        // 128 rows.  The row's four threads are a quad: two DPP swaps reduce it.
+        const int q = tid & 3;
+        for (int pass = 0; pass < 2; ++pass) {
+            const int row = pass * (BMB / 2) + (tid >> 2);
+            const int gm = m0 + row;
+            const int b = gm >> 3, k = gm & 7;
+            const bool active = gm < p.M && k != 0;   // the same for the row's four threads
+            const float Tb = s_temp[row >> 3];
+            const bool greedy = !(Tb > 0.f);
+            const float invT = greedy ? 1.f : 1.0f / Tb;
+            float best = -INFINITY;
+            int bi = 0x7FFFFFFF;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int cg = 8 * q + c;
+                const int64_t i0 = (int64_t)n0 + 8 * cg;
+                const uint4 w = *reinterpret_cast<const uint4*>(st + row * 256 + 8 * (cg ^ (row & 31)));
+                if (gm < p.M) *reinterpret_cast<uint4*>(p.out_bf16 + (int64_t)gm * p.N + i0) = w;
+                if (active) {
+                    float f[8];
+                    f[0] = lo_bf16(w.x); f[1] = hi_bf16(w.x); f[2] = lo_bf16(w.y); f[3] = hi_bf16(w.y);
+                    f[4] = lo_bf16(w.z); f[5] = hi_bf16(w.z); f[6] = lo_bf16(w.w); f[7] = hi_bf16(w.w);
+                    draft_best8(f, i0, greedy, invT, 8ull * (uint64_t)b + (uint64_t)k, hp.seed, hp.offset, best, bi);
+                }
+            }
+            better_step<kDppXor1>(best, bi);
+            better_step<kDppXor2>(best, bi);
+            if (active && q == 0) hp.part[((int64_t)b * 7 + k - 1) * hp.nparts + t.tn] = {best, bi};
+        }
         return;
     }
     if (!KV) {
@@ -514,9 +565,9 @@ FusePlan fuse_plan(const dflash_fuse_args& a) {
     return pl;
 }
 
-hipError_t launch_gemm_big(const GemmParams& g, hipStream_t s) {
+hipError_t launch_gemm_big_head(const GemmParams& g, const HeadEpilogue& hp, hipStream_t s) {
     const int tiles = ((g.M + BMB - 1) / BMB) * (g.N / BNB);
-    gemm_bf16_big_kernel<false><<<(tiles + kXcds - 1) / kXcds * kXcds, kBigThreads, 0, s>>>(g, KvEpilogue{});
+    gemm_bf16_big_kernel<2><<<(tiles + kXcds - 1) / kXcds * kXcds, kBigThreads, 0, s>>>(g, KvEpilogue{}, hp);
     return hipGetLastError();
 }
 
@@ -541,7 +592,7 @@ hipError_t launch_fuse(const dflash_fuse_args& a, const FusePlan& pl, void* ws, 
     KvEpilogue ep = {};
     if (pl.big) {
         const int tiles = ((M + BMB - 1) / BMB) * (DFLASH_D / BNB);
-        gemm_bf16_big_kernel<false><<<(tiles + kXcds - 1) / kXcds * kXcds, kBigThreads, 0, s>>>(g1, ep);
+        gemm_bf16_big_kernel<0><<<(tiles + kXcds - 1) / kXcds * kXcds, kBigThreads, 0, s>>>(g1, ep, HeadEpilogue{});
     } else {
         hipError_t e = launch_gemm(g1, a.dtype, s);
         if (e != hipSuccess) return e;
@@ -579,7 +630,7 @@ hipError_t launch_fuse(const dflash_fuse_args& a, const FusePlan& pl, void* ws, 
         ep.gk = a.gk; ep.eps = a.eps; ep.slot = a.slot; ep.num_pages = a.num_pages;
         for (int i = 0; i < 5; ++i) { ep.kc[i] = a.k_cache[i]; ep.vc[i] = a.v_cache[i]; }
         const int tiles = ((M + BMB - 1) / BMB) * (N2 / BNB);
-        gemm_bf16_big_kernel<true><<<(tiles + kXcds - 1) / kXcds * kXcds, kBigThreads, 0, s>>>(g2, ep);
+        gemm_bf16_big_kernel<1><<<(tiles + kXcds - 1) / kXcds * kXcds, kBigThreads, 0, s>>>(g2, ep, HeadEpilogue{});
         return hipGetLastError();
     }
     hipError_t e = launch_gemm(g2, a.dtype, s);

@@ -99,9 +99,5 @@ void gemm_set_split(GemmParams& g, int dtype, int ks);
 // aligned rows, a_stride < 2^23; fp32: 64x64 tiles, N % 64 == 0, K and
 // seg_w multiples of 16.
 hipError_t launch_gemm(const GemmParams& g, int dtype, hipStream_t s);
-// bf16 only, large M: 256x256 tiles, one workgroup of 8 waves per CU, no
-// split (g.ks must be 1); N % 256 == 0, K and seg_w multiples of 64.  Writes
-// out_bf16 when set, else part.  (Defined with the fusion kernels.)
-hipError_t launch_gemm_big(const GemmParams& g, hipStream_t s);
 
 }  // namespace dflash

@@ -7,30 +7,30 @@
 // tokens); "DFlash & DFlash2", section 4.2 (the target's unembedding head
 // maps the output states to vocabulary logits).
 //
-// Launch sequence:
-//   gemm    -- logits [8B][V] = y [8B][2560] . W_head^T, written in the
-//              storage type (bf16: the 256 x 256-tile kernel from 256 rows
-//              on, else the 128 x 128 kernel with one split; both with a
-//              direct bf16 output; or the fp32 kernel)
-//   sample  -- vocab-parallel over rows k = 1..7 of each sequence: greedy rows
-//              keep (max, lowest argmax); sampled rows the Gumbel-max key
-//              z / T - ln(-ln u) with u from stream 2 of the uniform layout,
-//              one Philox4x64-10 block per 8 entries
-//   pick    -- one wave per row: merge the chunk partials into d_k
-// Sampling reads the stored logits, so the proposals are those of the values
-// verification will read.
+// Launch sequence (keys: head_sample.h):
+//   bf16 with 256 rows or more and V % 256 == 0 (fused):
+//     gemm+sample -- the 256 x 256-tile projection; its epilogue rounds the
+//                    tile to bf16, stores it as 16-byte chunks and folds the
+//                    keys of rows k = 1..7 into one (key, index) per row and
+//                    tile
+//   otherwise:
+//     gemm        -- the 128 x 128 kernel with one split and a direct bf16
+//                    output (or the fp32 kernel)
+//     sample      -- vocabulary-parallel over rows k = 1..7, one (key, index)
+//                    per row and 8192-entry chunk
+//   pick          -- one wave per row: the best partial is d_k
+// Keys are computed from the stored (rounded) logits, so the proposals are
+// those of the values verification will read.
 #include "device_common.h"
 #include "gemm.h"
+#include "head_sample.h"
 #include "kernels.h"
 
 namespace dflash {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int64_t kChunk = 8192;       // vocabulary entries per sampling workgroup
-constexpr uint64_t kDraftStream = 2;   // uniform stream of draft sampling
-
-struct KeyPart { float key; int idx; };
+constexpr int64_t kChunk = 8192;       // vocabulary entries per sampling workgroup (separate pass)
 
 struct HeadParams {
     const void* logits;   // [B][8][V]
@@ -38,33 +38,30 @@ struct HeadParams {
     int B;
     int64_t V;
     uint64_t seed, offset;
-    int nch;
-    KeyPart* part;        // [B][7][nch]
+    int nch;              // partials per proposal row
+    KeyIdx* part;         // [B][7][nch]
     int32_t* d;           // [B][7]
 };
 
-template <typename T> struct Vec;
-template <> struct Vec<uint16_t> {
-    static constexpr int N = 8;
+// Eight consecutive stored logits as fp32 (one 16-byte load for bf16, two
+// for fp32); offsets are multiples of 8.
+template <typename T> struct Group8;
+template <> struct Group8<uint16_t> {
     static __device__ __forceinline__ void load(const uint16_t* p, float* f) {
         const uint4 w = *reinterpret_cast<const uint4*>(p);
         f[0] = lo_bf16(w.x); f[1] = hi_bf16(w.x); f[2] = lo_bf16(w.y); f[3] = hi_bf16(w.y);
         f[4] = lo_bf16(w.z); f[5] = hi_bf16(w.z); f[6] = lo_bf16(w.w); f[7] = hi_bf16(w.w);
     }
 };
-template <> struct Vec<float> {
-    static constexpr int N = 4;
+template <> struct Group8<float> {
     static __device__ __forceinline__ void load(const float* p, float* f) {
-        const float4 w = *reinterpret_cast<const float4*>(p);
-        f[0] = w.x; f[1] = w.y; f[2] = w.z; f[3] = w.w;
+        const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
     }
 };
 
-// Larger key wins; equal keys go to the lower index.
-__device__ __forceinline__ void better(float& v, int& i, float v2, int i2) {
-    if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
-}
-
+// Separate sampling pass (rows below 256, or V not a multiple of 256):
+// vocabulary-parallel over rows k = 1..7, one workgroup per 8192-entry chunk.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void draft_sample_kernel(HeadParams p) {
     const int chunk = blockIdx.x % p.nch;
@@ -74,44 +71,26 @@ __global__ __launch_bounds__(kThreads) void draft_sample_kernel(HeadParams p) {
     const bool greedy = !(Tb > 0.f);
     const float invT = greedy ? 1.f : 1.0f / Tb;
     const T* z = static_cast<const T*>(p.logits) + ((int64_t)b * 8 + k) * p.V;
-    constexpr int N = Vec<T>::N;
     const int64_t c0 = (int64_t)chunk * kChunk, c1 = min(p.V, c0 + kChunk);
     const uint64_t ctr1 = 8ull * (uint64_t)b + (uint64_t)k;
     float best = -INFINITY;
     int bi = 0x7FFFFFFF;
     // Every load of the thread is issued before any is used.
-    constexpr int kIt = kChunk / (kThreads * N);
-    float f[kIt][N];
+    constexpr int kIt = kChunk / (kThreads * 8);
+    float f[kIt][8];
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
-        const int64_t i0 = c0 + ((int64_t)it * kThreads + threadIdx.x) * N;
-        if (i0 < c1) Vec<T>::load(z + i0, f[it]);
+        const int64_t i0 = c0 + ((int64_t)it * kThreads + threadIdx.x) * 8;
+        if (i0 < c1) Group8<T>::load(z + i0, f[it]);
     }
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
-        const int64_t i0 = c0 + ((int64_t)it * kThreads + threadIdx.x) * N;
-        if (i0 >= c1) continue;
-        if (greedy) {
-#pragma unroll
-            for (int e = 0; e < N; ++e) better(best, bi, f[it][e], (int)(i0 + e));
-            continue;
-        }
-        // Entry j of an 8-entry group uses half j % 2 of word j / 2 of the
-        // group's Philox block (counter (i / 8, 8b + k, 2, offset)).
-        const U64x4 c = {(uint64_t)(i0 >> 3), ctr1, kDraftStream, p.offset};
-        const U64x4 r = philox4x64_10(c, p.seed, 0ull);
-        const uint64_t words[4] = {r.x0, r.x1, r.x2, r.x3};
-#pragma unroll
-        for (int e = 0; e < N; ++e) {
-            const int j = (int)((i0 + e) & 7);
-            const uint64_t wd = words[j >> 1];
-            const float u = (j & 1) ? word_to_uniform_lo(wd) : word_to_uniform(wd);
-            better(best, bi, f[it][e] * invT - fast_ln(-fast_ln(u)), (int)(i0 + e));
-        }
+        const int64_t i0 = c0 + ((int64_t)it * kThreads + threadIdx.x) * 8;
+        if (i0 < c1) draft_best8(f[it], i0, greedy, invT, ctr1, p.seed, p.offset, best, bi);
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) better(best, bi, __shfl_xor(best, o), __shfl_xor(bi, o));
-    __shared__ KeyPart sw[kThreads / 64];
+    __shared__ KeyIdx sw[kThreads / 64];
     if ((threadIdx.x & 63) == 0) sw[threadIdx.x >> 6] = {best, bi};
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -120,25 +99,31 @@ __global__ __launch_bounds__(kThreads) void draft_sample_kernel(HeadParams p) {
     }
 }
 
-// One wave per (sequence, proposal): the chunk partials' best key.
+// One wave per (sequence, proposal): the best of the row's partials.
 __global__ __launch_bounds__(kThreads) void draft_pick_kernel(HeadParams p) {
     const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= p.B * 7) return;
     float best = -INFINITY;
     int bi = 0x7FFFFFFF;
-    for (int c = lane; c < p.nch; c += 64) better(best, bi, p.part[(int64_t)row * p.nch + c].key,
-                                                     p.part[(int64_t)row * p.nch + c].idx);
+    for (int c = lane; c < p.nch; c += 64) {
+        const KeyIdx kp = p.part[(int64_t)row * p.nch + c];
+        better(best, bi, kp.key, kp.idx);
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) better(best, bi, __shfl_xor(best, o), __shfl_xor(bi, o));
     if (lane == 0) p.d[row] = bi == 0x7FFFFFFF ? -1 : bi;   // no finite key (non-finite logits): -1
 }
 
+bool fused_path(const dflash_head_args& a) { return a.dtype == DFLASH_BF16 && 8 * a.B >= 256 && a.V % 256 == 0; }
+
 }  // namespace
 
 size_t head_workspace_bytes(int B, int64_t V) {
-    const int64_t nch = (V + kChunk - 1) / kChunk;
-    return ((size_t)B * 7 * nch * sizeof(KeyPart) + 255) & ~(size_t)255;
+    // The fused path keeps one partial per row and 256-column tile, the
+    // separate pass one per 8192-entry chunk: size for the larger.
+    const int64_t n = (V + 255) / 256;
+    return ((size_t)B * 7 * n * sizeof(KeyIdx) + 255) & ~(size_t)255;
 }
 
 hipError_t launch_head(const dflash_head_args& a, void* ws, hipStream_t s) {
@@ -152,21 +137,29 @@ hipError_t launch_head(const dflash_head_args& a, void* ws, hipStream_t s) {
     gemm_set_split(g, a.dtype, 1);
     if (a.dtype == DFLASH_BF16) g.out_bf16 = static_cast<uint16_t*>(a.logits);
     else g.part = static_cast<float*>(a.logits);
-    // 256 x 256 tiles once there are 256 rows: half the operand traffic per
-    // flop of the 128 x 128 kernel.
-    const bool big = a.dtype == DFLASH_BF16 && M >= 256 && a.V % 256 == 0;
-    hipError_t e = big ? launch_gemm_big(g, s) : launch_gemm(g, a.dtype, s);
-    if (e != hipSuccess) return e;
 
     HeadParams p;
     p.logits = a.logits; p.temp = a.temperature; p.B = a.B; p.V = a.V;
     p.seed = a.seed; p.offset = a.offset;
-    p.nch = (int)((a.V + kChunk - 1) / kChunk);
-    p.part = static_cast<KeyPart*>(ws);
+    p.part = static_cast<KeyIdx*>(ws);
     p.d = a.draft_tokens;
     const int rows = a.B * 7;
-    if (a.dtype == DFLASH_BF16) draft_sample_kernel<uint16_t><<<rows * p.nch, kThreads, 0, s>>>(p);
-    else draft_sample_kernel<float><<<rows * p.nch, kThreads, 0, s>>>(p);
+    hipError_t e;
+    if (fused_path(a)) {
+        // 256 x 256 tiles (half the operand bytes per flop of 128 x 128),
+        // keys computed in the epilogue from the rounded logits.
+        HeadEpilogue ep;
+        ep.temp = a.temperature; ep.seed = a.seed; ep.offset = a.offset;
+        ep.part = p.part;
+        ep.nparts = (int)(a.V / 256);
+        if ((e = launch_gemm_big_head(g, ep, s)) != hipSuccess) return e;
+        p.nch = ep.nparts;
+    } else {
+        if ((e = launch_gemm(g, a.dtype, s)) != hipSuccess) return e;
+        p.nch = (int)((a.V + kChunk - 1) / kChunk);
+        if (a.dtype == DFLASH_BF16) draft_sample_kernel<uint16_t><<<rows * p.nch, kThreads, 0, s>>>(p);
+        else draft_sample_kernel<float><<<rows * p.nch, kThreads, 0, s>>>(p);
+    }
     draft_pick_kernel<<<(rows + 3) / 4, kThreads, 0, s>>>(p);
     return hipGetLastError();
 }

@@ -103,25 +103,6 @@ __device__ __forceinline__ Stat stat_merge(Stat a, Stat b) {
     return r;
 }
 
-// Cross-lane moves through DPP (no LDS round trip): lanes a row mask leaves
-// out, or whose source lane does not exist, receive the identity `id`.
-template <int CTRL, int ROWS = 0xf>
-__device__ __forceinline__ float dpp_f(float x, float id) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, id), __builtin_bit_cast(int, x),
-                                                                 CTRL, ROWS, 0xf, false));
-}
-template <int CTRL, int ROWS = 0xf>
-__device__ __forceinline__ int dpp_i(int x, int id) {
-    return __builtin_amdgcn_update_dpp(id, x, CTRL, ROWS, 0xf, false);
-}
-// The reduction order: swap within pairs, within quads, mirror within
-// half-rows and rows (every lane of a 16-lane row then holds the row's
-// result), then row 1 <- lane 15 and row 3 <- lane 47 (row_bcast:15, rows 1
-// and 3), row 3 <- lane 31 (row_bcast:31, rows 2 and 3): lane 63 ends with
-// the wave's result, read back as a uniform value.
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
-constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
-
 template <int CTRL, int ROWS = 0xf>
 __device__ __forceinline__ void first_step(float& v, int& i) {
     const float v2 = dpp_f<CTRL, ROWS>(v, -INFINITY);
@@ -279,7 +260,6 @@ __global__ __launch_bounds__(kThreads) void path_stats_kernel(PathParams p) {
     // Softmax sums relative to the lane maximum on the hardware exp2
     // (differences scaled by log2 e, clamped so that padding and masked
     // logits give exactly 0).
-    constexpr float kLog2e = 1.4426950408889634f;
     const float ref = mx == -INFINITY ? 0.f : mx * kLog2e;
     // Opaque to the compiler: the unpacked copies of the maximum pass are not
     // kept alive until here (they would double the registers).

@@ -285,8 +285,8 @@ def test_draft_head_validation(lib):
             setattr(a, k, v)
         return a
     rc, n = _ws(lib, "draft_head", args())
-    # one (key, index) partial per 8192-entry chunk of each proposal row
-    assert rc == 0 and n == 64 * 7 * 32 * 8
+    # one (key, index) partial per 256-column tile of each proposal row
+    assert rc == 0 and n == 64 * 7 * 1024 * 8
     assert _ws(lib, "draft_head", args(V=262144 + 64))[0] == -1      # not a multiple of 128
     assert _ws(lib, "draft_head", args(V=0))[0] == -1
     assert _ws(lib, "draft_head", args(V=(1 << 21) + 128))[0] == -1

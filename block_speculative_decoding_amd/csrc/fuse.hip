@@ -105,23 +105,35 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
         voa[j] = (uint32_t)(r * (int)p.a_stride + 8 * c) * 2u;
         vob[j] = (uint32_t)(r * p.K + 8 * c) * 2u;
     }
-    auto load_part = [&](int kt, int slot, int part) {
+    // Both operands' buffer descriptors for k-tile kt, computed once per
+    // k-tile at the top of the loop: the loads themselves sit between matrix
+    // instructions, where a segment select (a division and a five-way pointer
+    // choice per load) would hold up the next one.
+    struct StageSrc { i32x4 a, b; };
+    auto stage_src = [&](int kt) {
         const int kg = kt * BKB;
-        uint4* sb = lds + slot * (kBigStageBytes / 16) + wave * 64;
+        // The K/V projection's A operand (H_t) and the head's (y) are one segment.
+        const int seg = MODE != 0 ? 0 : kg / p.seg_w;
+        const int kc = kg - seg * p.seg_w;
+        const void* av = seg == 0 ? aseg0 : seg == 1 ? aseg1 : seg == 2 ? aseg2 : seg == 3 ? aseg3 : aseg4;
+        const uint16_t* a = static_cast<const uint16_t*>(av) + (int64_t)m0 * p.a_stride + kc;
+        StageSrc s;
+        s.a = buffer_rsrc(a, arows * (uint32_t)p.a_stride * 2u - (uint32_t)kc * 2u);
+        s.b = buffer_rsrc(bmat + kg, (uint32_t)BNB * (uint32_t)p.K * 2u - (uint32_t)kg * 2u);
+        return s;
+    };
+    // The wave index read as wave-uniform, so that each load's LDS base (M0)
+    // is scalar arithmetic.
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    auto load_part = [&](const StageSrc& src, int slot, int part) {
+        uint4* sb = lds + slot * (kBigStageBytes / 16) + wave_s * 64;
         if (part < kBigPartsA) {
-            // The K/V projection's A operand (H_t) is one segment.
-            const int seg = KV ? 0 : kg / p.seg_w;
-            const int kc = kg - seg * p.seg_w;
-            const void* av = seg == 0 ? aseg0 : seg == 1 ? aseg1 : seg == 2 ? aseg2 : seg == 3 ? aseg3 : aseg4;
-            const uint16_t* a = static_cast<const uint16_t*>(av) + (int64_t)m0 * p.a_stride + kc;
-            const i32x4 rs = buffer_rsrc(a, arows * (uint32_t)p.a_stride * 2u - (uint32_t)kc * 2u);
-            llvm_amdgcn_raw_buffer_load_lds(rs, (__attribute__((address_space(3))) uint32_t*)(sb + part * kBigThreads), 16,
-                                            (int)voa[part], 0, 0, 0);
+            llvm_amdgcn_raw_buffer_load_lds(src.a, (__attribute__((address_space(3))) uint32_t*)(sb + part * kBigThreads),
+                                            16, (int)voa[part], 0, 0, 0);
         } else {
             const int j = part - kBigPartsA;
-            const i32x4 rs = buffer_rsrc(bmat + kg, (uint32_t)BNB * (uint32_t)p.K * 2u - (uint32_t)kg * 2u);
             llvm_amdgcn_raw_buffer_load_lds(
-                rs, (__attribute__((address_space(3))) uint32_t*)(sb + BMB * 8 + j * kBigThreads), 16, (int)vob[j], 0, 0, 0);
+                src.b, (__attribute__((address_space(3))) uint32_t*)(sb + BMB * 8 + j * kBigThreads), 16, (int)vob[j], 0, 0, 0);
         }
     };
 
@@ -161,15 +173,18 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
 
     bf16x8 fa[2][4], fb[2][2];
 #pragma unroll
-    for (int s0 = 0; s0 < 2; ++s0)
+    for (int s0 = 0; s0 < 2; ++s0) {
+        const StageSrc src = stage_src(min(s0, nk - 1));
 #pragma unroll
-        for (int t2 = 0; t2 < 2 * kBigPartsA; ++t2) load_part(min(s0, nk - 1), s0, t2);
+        for (int t2 = 0; t2 < 2 * kBigPartsA; ++t2) load_part(src, s0, t2);
+    }
     wait_vm<2 * kBigPartsA>();  // stage 0 landed
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     rd(0, 0, fa[0], fb[0]);
     for (int i = 0; i < nk; ++i) {
         const int slot = i & 1;
+        const StageSrc nsrc = stage_src(min(i + 2, nk - 1));
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
             rd(slot, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
@@ -184,13 +199,12 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
         asm volatile("" ::: "memory");
         rd(slot ^ 1, 0, fa[0], fb[0]);
         __builtin_amdgcn_sched_barrier(0);
-        const int kn = min(i + 2, nk - 1);
 #pragma unroll
         for (int t2 = 0; t2 < 8; ++t2) {
             acc[t2 >> 1][t2 & 1] =
                 __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][t2 >> 1], fb[1][t2 & 1], acc[t2 >> 1][t2 & 1], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
-            load_part(kn, slot, t2);  // stage i+2 into the slot stage i used
+            load_part(nsrc, slot, t2);  // stage i+2 into the slot stage i used
             __builtin_amdgcn_sched_barrier(0);
         }
     }

@@ -62,6 +62,10 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (5 times), the known-size "
                          "reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
+    ap.add_argument("--gemm-probe", action="store_true",
+                    help="only run the prefill fusion at M=32768 (2 warm-up + 5 timed calls) and, as a "
+                         "reference on the same two GEMM shapes, torch's bf16 matmul (2 + 5 each): the "
+                         "run behind the GEMM counter passes")
     return ap.parse_args()
 
 
@@ -76,6 +80,43 @@ def copy_probe():
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "repeats": 5}))
+
+
+def gemm_probe():
+    """The prefill fusion (first GEMM [32768,12800] x [12800,2560], the K/V
+    GEMM [32768,2560] x [2560,10240] with its epilogue) and torch's bf16
+    matmul on the same two shapes, for counter passes that compare the
+    matrix pipes' busy fraction, the shader clock and the L2 traffic."""
+    import torch
+    import block_speculative_decoding_amd as dfl
+    from block_speculative_decoding_amd import synth
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev).manual_seed(SEED + 1)
+    M = 32768
+    hs = [torch.randn((M, 2560), generator=g, device=dev, dtype=torch.float32).to(bf) for _ in range(5)]
+    w = {k: torch.from_numpy(np.ascontiguousarray(v)).to(bf).to(dev) for k, v in synth.fuse_weights(SEED, LAYERS).items()}
+    npages = M // 16
+    kc = [torch.zeros((npages, 8, 2048), dtype=bf, device=dev) for _ in range(LAYERS)]
+    vc = [torch.zeros((npages, 8, 2048), dtype=bf, device=dev) for _ in range(LAYERS)]
+    pos = torch.arange(M, dtype=torch.int32, device=dev)
+    slot = torch.arange(M, dtype=torch.int64, device=dev)
+    fuse = dfl.prepare_ctx_fuse(hs, w["wc"], w["gc"], w["wkv"], w["gk"], pos, slot, kc, vc)
+    f_ms = timed(torch, fuse)
+    flops, _ = fuse_flops_bytes(M)
+    del hs, kc, vc, fuse
+    torch.cuda.empty_cache()
+    a1 = torch.randn((M, 12800), generator=g, device=dev, dtype=torch.float32).to(bf)
+    h = torch.randn((M, 2560), generator=g, device=dev, dtype=torch.float32).to(bf)
+    wc_t = w["wc"].t().contiguous()
+    wkv_t = w["wkv"].t().contiguous()
+    t1 = timed(torch, lambda: torch.matmul(a1, wc_t))
+    t2 = timed(torch, lambda: torch.matmul(h, wkv_t))
+    f1, f2 = 2 * M * 12800 * 2560, 2 * M * 2560 * LAYERS * 2048
+    print(json.dumps({"gemm_probe": {
+        "ctx_fuse_m32768_ms": round(f_ms, 4), "ctx_fuse_TFLOP/s": round(flops / (f_ms * 1e-3) / 1e12, 1),
+        "torch_matmul_fuse_gemm_ms": round(t1, 4), "torch_matmul_fuse_gemm_TFLOP/s": round(f1 / (t1 * 1e-3) / 1e12, 1),
+        "torch_matmul_kv_gemm_ms": round(t2, 4), "torch_matmul_kv_gemm_TFLOP/s": round(f2 / (t2 * 1e-3) / 1e12, 1)}}))
 
 
 def log(msg):
@@ -495,6 +536,9 @@ def main():
     args = parse()
     if args.copy_probe:
         copy_probe()
+        return
+    if args.gemm_probe:
+        gemm_probe()
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",

@@ -357,16 +357,25 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
         g[0] = bf16_bits_to_f32(gk[d0]);
         g[1] = bf16_bits_to_f32(gk[d0 + 64]);
     }
-    // Per-row partial sums of squares of this wave's 64 columns.
+    // Per-row partial sums of squares of this wave's 64 columns: each half
+    // wave (the 32 columns lr of one row set) is reduced with DPP (pairs,
+    // quads, half-row and row mirrors give every lane its 16-lane row sum,
+    // then row_bcast:15 adds row 0's into row 1 and row 2's into row 3) and
+    // read back from lane 31 (lanes 0-31) or 63 (lanes 32-63).
     float ssp[4][16];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float ss = acc[i][0][r] * acc[i][0][r] + acc[i][1][r] * acc[i][1][r];
-#pragma unroll
-            for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o);
-            ssp[i][r] = ss;
+            ss += dpp_f<kDppXor1>(ss, 0.f);
+            ss += dpp_f<kDppXor2>(ss, 0.f);
+            ss += dpp_f<kDppHalfMirror>(ss, 0.f);
+            ss += dpp_f<kDppMirror>(ss, 0.f);
+            ss += dpp_f<kDppBcast15, 0xA>(ss, 0.f);
+            const int bits = __builtin_bit_cast(int, ss);
+            const int lo = __builtin_amdgcn_readlane(bits, 31), hi = __builtin_amdgcn_readlane(bits, 63);
+            ssp[i][r] = __builtin_bit_cast(float, lh ? hi : lo);
         }
     __syncthreads();  // every wave is done with the operand stages in LDS
     float* sums = reinterpret_cast<float*>(lds + 2 * kBigStageBytes / 16);  // [8 waves][128 rows]
@@ -385,7 +394,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
         for (int r = 0; r < 16; ++r) {
             const int rl = 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);  // row within the wave's 128
             const float ss = ssp[i][r] + sums[(wave ^ 1) * 128 + rl];
-            const float rinv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + ep.eps);
+            const float rinv = __builtin_amdgcn_rsqf(ss * (1.0f / 128.0f) + ep.eps);
             const int row = wr + rl;
             const int gm = min(m0 + row, p.M - 1);
             const float2 cs = ep.cs[(int64_t)gm * 64 + d0];
@@ -396,16 +405,22 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
         }
     }
     __syncthreads();
-    // 256 rows x 2 heads x 16 chunks = 8192 chunks, 16 per thread.
+    // 256 rows x 2 heads x 16 chunks = 8192 chunks, 16 per thread: rows
+    // 16 it + (tid % 16), it = 0..15, chunk (tid / 16) % 16.  The 16 slots are
+    // loaded before any store depends on them.
     const int hs = tid >> 8;                       // head of the pair this thread stores
     const int headst = ((n0 >> 7) + hs) & 7;
-#pragma unroll 4
+    const int tk = tid & 15, c = (tid >> 4) & 15;
+    int64_t slots[16];
+#pragma unroll
     for (int it = 0; it < 16; ++it) {
-        const int q = it * 256 + (tid & 255);
-        const int tk = q & 15, c = (q >> 4) & 15, row = 16 * (q >> 8) + tk;
-        const int gm = m0 + row;
-        if (gm >= p.M) continue;
-        const int64_t slot = ep.slot[gm];
+        const int gm = m0 + 16 * it + tk;
+        slots[it] = gm < p.M ? ep.slot[gm] : -1;
+    }
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int row = 16 * it + tk;
+        const int64_t slot = slots[it];
         if (slot < 0 || slot >= nslots) continue;
         const uint4 w = *reinterpret_cast<const uint4*>(st16 + row * 256 + 128 * hs + 8 * (c ^ (row & 15)));
         uint16_t* blk = cache + ((slot >> 4) * 8 + headst) * 2048;

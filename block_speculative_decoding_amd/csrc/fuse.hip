@@ -300,12 +300,18 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
         // values a lane keeps for rows 8*(r/4) + 4*lh + r%4, r = 0..7 (8..15),
         // are exactly the granule of page 0 (page 1) for half lh: one 16-byte
         // store each.  Otherwise every element is stored on its own.
+        // The slots every block tests, loaded before the first test.
+        int64_t s0v[4], smv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row0 = rbase + 32 * i;
-            const int myrow = row0 + lr;
-            const int64_t s0 = row0 < p.M ? ep.slot[row0] : -1;
-            const int64_t sm = myrow < p.M ? ep.slot[myrow] : -1;
+            s0v[i] = row0 < p.M ? ep.slot[row0] : -1;
+            smv[i] = row0 + lr < p.M ? ep.slot[row0 + lr] : -1;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row0 = rbase + 32 * i;
+            const int64_t s0 = s0v[i], sm = smv[i];
             const bool ok = (s0 & 15) == 0 && s0 >= 0 && s0 + 32 <= nslots && sm == s0 + lr;
             if (__ballot(ok) == ~0ull) {
 #pragma unroll

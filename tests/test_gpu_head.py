@@ -66,12 +66,15 @@ def _run(y_t, w_t, temp, dtype):
 
 
 @pytest.mark.parametrize("dtype,B,V", [(BF16, 5, 3 * 8192 + 384), (F32, 3, 8192 + 128), (BF16, 1, 128),
-                                        (BF16, 40, 8192 + 256), (BF16, 40, 8192 + 128)])
+                                        (BF16, 40, 8192 + 256), (BF16, 40, 8192 + 128),
+                                        (BF16, 32, 8192 + 256), (BF16, 31, 8192 + 256)])
 def test_head_logits_and_proposals(dtype, B, V):
     # Several 128-row and 8192-entry chunks with ragged tails (M = 8B rows).
     # B = 40 (M = 320) with V % 256 == 0 takes the 256 x 256-tile projection
     # with its sampling epilogue (a ragged row tile); with V % 256 == 128 the
-    # 128 x 128 projection and the separate sampling pass.
+    # 128 x 128 projection and the separate sampling pass.  B = 32 (M = 256)
+    # is the smallest call on the 256 x 256 path (one full row tile), B = 31
+    # (M = 248) the largest below it.
     y_t, y = _stored(synth.head_input(SEED, B), dtype)
     w_t, w = _stored(synth.head_weight(SEED, V), dtype)
     temp = synth.head_temperatures(SEED, B)

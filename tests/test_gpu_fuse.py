@@ -129,6 +129,23 @@ def test_fuse_large_ragged_rows_scattered_slots():
     assert ht_err <= TOL[BF16] and kv_err <= TOL[BF16]
 
 
+@pytest.mark.parametrize("M", [8191, 8192])
+def test_fuse_path_boundary(M):
+    """M = 8191 is the largest fusion on the split-K kernels, 8192 the
+    smallest on the 256x256 kernel with the K/V epilogue (32 full row tiles);
+    one layer, shuffled slots, sampled rows checked."""
+    L = 1
+    npages = (M + 15) // 16 + 3
+    rng = np.random.default_rng(M)
+    slots = rng.permutation(npages * 16)[:M].astype(np.int64)
+    pos = rng.integers(0, 65536, M).astype(np.int32)
+    rows = np.sort(rng.choice(M, 32, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    ht_err, kv_err, _, _ = _run(M, L, BF16, 8, npages, slots, pos, rows=rows)
+    note(f"fuse path boundary M={M}: H_t err {ht_err:.3e}, K/V err {kv_err:.3e}")
+    assert ht_err <= TOL[BF16] and kv_err <= TOL[BF16]
+
+
 @pytest.mark.parametrize("shift", [16, 8])
 def test_fuse_large_contiguous_slots_page_offsets(shift):
     """Large-M path with slots in order starting at `shift`: with 16 every full

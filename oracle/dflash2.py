@@ -29,10 +29,18 @@ Readings (listed in the design notes as well):
   chosen before it and a path's score separates per position.  The top-P
   paths of a separable score are then exactly what a beam of width P keeps
   position by position (a full path in the top P has its prefix in the top
-  P of its length).  Ties order by the candidate ranks, first position
-  first (the lexicographically smaller rank tuple wins); candidates of a
-  position order by logit, ties to the lower token id.
+  P of its length).  log P(x) = z(x) - lse of the position, and the lse
+  terms and lambda * entropy shift every path by the same amount, so paths
+  are ranked by the exact sum of their stored candidate logits; equal sums
+  order by the candidate ranks, first position first (the lexicographically
+  smaller rank tuple wins).  Exactness matters: stored bf16 logits lie on a
+  coarse grid, different candidate combinations often have equal sums, and
+  any rounding of a per-path score would decide those ties instead of the
+  rule.  Candidates of a position order by logit, ties to the lower token
+  id.
 """
+
+from fractions import Fraction
 
 import numpy as np
 
@@ -83,32 +91,64 @@ def row_stats_ref(z, m):
     Z = np.sum(e, axis=-1, keepdims=True)
     p = e / Z
     logp_all = (z - zmax) - np.log(Z)
-    ent = -np.sum(np.where(p > 0, p * logp_all, 0.0), axis=-1)
+    with np.errstate(invalid="ignore"):
+        ent = -np.sum(np.where(p > 0, p * logp_all, 0.0), axis=-1)
     # stable sort of -z: equal logits keep increasing id order
     ids = np.argsort(-z, axis=-1, kind="stable")[..., :m]
     logp = np.take_along_axis(logp_all, ids, axis=-1)
     return ids.astype(np.int32), logp, ent
 
 
-def top_paths_ref(ids, logp, entropy, P, lam):
+def log_normaliser_ref(z):
+    """lse = log sum_i e^(z_i) per row of z [..., V] (float64)."""
+    z = np.asarray(z, dtype=np.float64)
+    zmax = np.max(z, axis=-1)
+    return zmax + np.log(np.sum(np.exp(z - zmax[..., None]), axis=-1))
+
+
+def _path_order(n_neg_inf, total, ranks):
+    """Sort key of a (partial) path: fewer -inf candidates first, then the
+    larger exact sum of its finite candidate logits, then the
+    lexicographically smaller rank tuple."""
+    return (n_neg_inf, -total, ranks)
+
+
+def top_paths_ref(ids, vals, entropy, P, lam, lse=None):
     """Top-P paths of one sequence through its positions.
 
-    ids, logp: [J, m] candidates per position (rank order); entropy: [J].
-    Score of the path with candidate ranks (r_1..r_J) is
-    sum_j logp[j, r_j] + lam * sum_j entropy[j].  Returns (tokens int32
-    [P, J], scores [P], ranks int32 [P, J]) best first, ties to the
-    lexicographically smaller rank tuple, via a beam of width P."""
+    ids, vals: [J, m] candidates per position in rank order (token ids and
+    their stored logits); entropy: [J]; lse: [J] log-normalisers of the
+    positions (default 0).  log P of candidate r at position j is
+    vals[j, r] - lse[j], so the score of the path with ranks (r_1..r_J),
+    sum_j (vals[j, r_j] - lse[j]) + lam * sum_j entropy[j], differs between
+    paths only by sum_j vals[j, r_j]: paths are ordered by that sum, taken
+    EXACTLY (Fractions of the stored values, so that equal real sums are
+    equal here), best first, equal sums by the lexicographically smaller
+    rank tuple.  A -inf logit makes a path's sum -inf; such paths come after
+    every finite one, ordered by their number of -inf candidates and then by
+    the sum of their finite ones (the refinement keeps the order additive
+    over positions, which is what makes the beam exact).  +inf and NaN
+    logits are outside the domain.  Returns (tokens int32 [P, J], scores
+    [P], ranks int32 [P, J]) via a beam of width P."""
     ids = np.asarray(ids)
-    logp = np.asarray(logp, dtype=np.float64)
-    J, m = logp.shape
-    beam = [((), 0.0)]                      # (rank tuple, sum of log-probabilities)
+    vals = np.asarray(vals, dtype=np.float64)
+    J, m = vals.shape
+    if np.any(np.isnan(vals)) or np.any(vals == np.inf):
+        raise ValueError("candidate logits must be finite or -inf")
+    lse = np.zeros(J) if lse is None else np.asarray(lse, dtype=np.float64)
+    exact = [[None if v == -np.inf else Fraction(float(v)) for v in row] for row in vals]
+    beam = [((), 0, Fraction(0))]            # (rank tuple, -inf count, exact finite sum)
     for j in range(J):
-        ext = [(r + (c,), s + logp[j, c]) for r, s in beam for c in range(m)]
-        ext.sort(key=lambda e: (-e[1], e[0]))
+        ext = []
+        for r, n, s in beam:
+            for c in range(m):
+                v = exact[j][c]
+                ext.append((r + (c,), n + 1, s) if v is None else (r + (c,), n, s + v))
+        ext.sort(key=lambda e: _path_order(e[1], e[2], e[0]))
         beam = ext[:P]
-    shift = lam * float(np.sum(entropy))
-    ranks = np.array([r for r, _ in beam], dtype=np.int32).reshape(len(beam), J)
-    scores = np.array([s for _, s in beam]) + shift
+    shift = lam * float(np.sum(entropy)) - float(np.sum(lse))
+    ranks = np.array([r for r, _, _ in beam], dtype=np.int32).reshape(len(beam), J)
+    scores = np.array([-np.inf if n else float(s) + shift for _, n, s in beam])
     tokens = np.take_along_axis(ids[None, :, :].repeat(len(beam), 0), ranks[:, :, None], axis=2)[:, :, 0]
     return tokens.astype(np.int32), scores, ranks
 
@@ -120,10 +160,12 @@ def path_select_ref(z, m, P, lam):
     (tokens [B, P, 7], scores [B, P], ranks [B, P, 7])."""
     z = np.asarray(z, dtype=np.float64)
     ids, logp, ent = row_stats_ref(z[:, 1:], m)
+    vals = np.take_along_axis(z[:, 1:], ids.astype(np.int64), axis=-1)
+    lse = log_normaliser_ref(z[:, 1:])
     B = z.shape[0]
     toks, scores, ranks = [], [], []
     for b in range(B):
-        t, s, r = top_paths_ref(ids[b], logp[b], ent[b], P, lam)
+        t, s, r = top_paths_ref(ids[b], vals[b], ent[b], P, lam, lse[b])
         toks.append(t)
         scores.append(s)
         ranks.append(r)

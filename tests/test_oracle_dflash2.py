@@ -3,7 +3,9 @@ convolution per channel and a one-step shift kernel fixes its direction and
 zero padding; with a zero kernel the layer is the plain draft layer; row
 statistics match scipy's entropy and log-softmax and a stable sort (ties to
 the lower id); the beam's top-P paths equal brute-force enumeration of every
-path, the single best path is the per-position argmax, and lambda shifts
+path (continuous log-probabilities, and bf16-grid logits with many exactly
+tied sums, compared as integers), -inf candidates order after finite ones,
+the single best path is the per-position argmax, and lambda shifts
 every score by lambda times the summed entropy without reordering."""
 
 import itertools
@@ -102,6 +104,77 @@ def test_beam_equals_brute_force(m, P):
     assert ranks.tolist() == [list(r) for _, r in best]
     np.testing.assert_allclose(scores, [-s for s, _ in best], rtol=0, atol=1e-12)
     assert np.array_equal(toks, ids[np.arange(J)[None, :], ranks])
+
+
+def _bf16_grid(rng, shape, scale):
+    """Values on the bf16 grid of N(0, scale^2) draws (8 significant bits)."""
+    x = scale * rng.standard_normal(shape)
+    e = np.floor(np.log2(np.abs(x)))
+    q = 2.0 ** (e - 7)
+    return np.round(x / q) * q
+
+
+def _brute_force_ranks(vals, P):
+    """Every rank tuple, ordered by the integer sum of its candidates (values
+    scaled to integers: exact), larger first, ties by the tuple."""
+    J, m = vals.shape
+    unit = 2.0 ** -40                            # every value in these tests is a multiple of it
+    iv = [[int(round(v / unit)) for v in row] for row in vals]
+    assert all(float(a) * unit == v for row, vrow in zip(iv, vals) for a, v in zip(row, vrow))
+    allp = sorted(itertools.product(range(m), repeat=J), key=lambda r: (-sum(iv[j][r[j]] for j in range(J)), r))
+    return [list(r) for r in allp[:P]]
+
+
+def test_paths_on_tied_bf16_logits_equal_brute_force():
+    # Stored bf16 logits: distinct candidate combinations often have equal
+    # sums.  The order must follow the exact sums and the rank tuples; a
+    # score rounded in floating point (the sum of fp64 log-probabilities
+    # z - zmax - log Z) lets rounding decide those ties, and does so wrongly
+    # on a good share of these cases -- the check below makes sure the
+    # inputs contain such cases.
+    rng = np.random.default_rng(17)
+    J, m, P = 7, 3, 30
+    naive_wrong = 0
+    for case in range(60):
+        z = _bf16_grid(rng, (J, 40), 2.0)
+        ids, logp, ent = row_stats_ref(z, m)
+        vals = np.take_along_axis(z, ids.astype(np.int64), axis=-1)
+        lse = oracle.dflash2.log_normaliser_ref(z)
+        toks, scores, ranks = top_paths_ref(ids, vals, ent, P, 0.4, lse)
+        assert ranks.tolist() == _brute_force_ranks(vals, P), case
+        own = vals[np.arange(J)[None, :], ranks].sum(axis=1) - lse.sum() + 0.4 * ent.sum()
+        np.testing.assert_allclose(scores, own, rtol=0, atol=1e-9)
+        naive = sorted(itertools.product(range(m), repeat=J),
+                       key=lambda r: (-sum(logp[j, r[j]] for j in range(J)), r))[:P]
+        naive_wrong += [list(r) for r in naive] != ranks.tolist()
+    assert naive_wrong >= 5
+
+
+def test_paths_with_neg_inf_candidates():
+    # Rows with fewer finite logits than candidates: paths through a -inf
+    # candidate come after every finite path, by their number of -inf
+    # candidates, then by the exact sum of the finite ones, then by tuple.
+    rng = np.random.default_rng(23)
+    J, m, P = 7, 3, 600                          # 2 * 3^5 = 486 finite paths, then -inf ones
+    z = _bf16_grid(rng, (J, 16), 1.5)
+    z[1, 2:] = -np.inf                           # two finite entries: rank 2 is -inf
+    z[4, 1:] = -np.inf                           # one finite entry
+    ids, logp, ent = row_stats_ref(z, m)
+    vals = np.take_along_axis(z, ids.astype(np.int64), axis=-1)
+    toks, scores, ranks = top_paths_ref(ids, vals, ent, P, 0.0)
+    unit = 2.0 ** -40
+    allp = []
+    for r in itertools.product(range(m), repeat=J):
+        v = [vals[j, r[j]] for j in range(J)]
+        n_inf = sum(x == -np.inf for x in v)
+        allp.append(((n_inf, -sum(int(round(x / unit)) for x in v if x != -np.inf), r), r))
+    allp.sort()
+    assert ranks.tolist() == [list(r) for _, r in allp[:P]]
+    finite = np.isfinite(scores)
+    assert finite.sum() == 2 * 3 ** 5 and np.all(finite[:2 * 3 ** 5])
+    assert np.all(scores[~finite] == -np.inf)
+    with pytest.raises(ValueError):
+        top_paths_ref(ids, np.where(vals == -np.inf, np.inf, vals), ent, P, 0.0)
 
 
 def test_single_path_is_argmax_and_lambda_shifts():

@@ -20,9 +20,12 @@
 //                  partials into M, Z = sum e^(z - M), the entropy
 //                  log Z - S1 / Z and the top-m candidates with
 //                  log p = z - M - log Z; then the beam over the seven
-//                  positions, each step ranking the P x m extensions by
-//                  counting (score first, then the candidate ranks as a
-//                  base-8 code, first position most significant)
+//                  positions.  log p = z - lse per position, so paths differ
+//                  only by the sum of their stored candidate logits: each
+//                  step ranks the P x m extensions by counting, on that sum
+//                  taken exactly (128-bit fixed point, see PathKey), then
+//                  the candidate ranks as a base-8 code, first position most
+//                  significant
 #include "device_common.h"
 #include "kernels.h"
 
@@ -325,13 +328,62 @@ __global__ __launch_bounds__(kThreads) void path_stats_kernel(PathParams p) {
 
 constexpr int kSelThreads = 512;   // wave k < 7 merges row k; all take part in the beam
 
+// Exact order of (partial) paths.  A stored logit v = Mv * 2^ev with Mv an
+// integer; at a per-sequence unit 2^e0 (the finest lowest set bit among the
+// sequence's finite candidates) every candidate is the integer Mv << (ev - e0)
+// and a path's sum of candidates is an exact 128-bit integer, as long as the
+// candidates span at most 2^123 (largest magnitude over finest unit; beyond
+// that e0 is raised and the finest bits are dropped, rounding toward -inf).
+// A -inf candidate is counted instead of summed: paths order by fewer -inf
+// candidates, then the larger sum, then the smaller rank code -- an order
+// that stays additive over positions, so the beam keeps the exact top P.
+struct PathKey {
+    __int128 sum;
+    int ninf;
+    int code;
+    int pad[2];
+};
+
+__device__ __forceinline__ bool key_before(const PathKey& a, const PathKey& b) {
+    if (a.ninf != b.ninf) return a.ninf < b.ninf;
+    if (a.sum != b.sum) return a.sum > b.sum;
+    return a.code < b.code;
+}
+
+// |v| = mag * 2^e with mag odd (or 0).  +inf and NaN fall outside the
+// supported domain; they decompose to some finite pair (no fault).
+__device__ __forceinline__ void split_float(float v, uint32_t& mag, int& e, bool& neg) {
+    const uint32_t u = __float_as_uint(v);
+    const int ex = (int)((u >> 23) & 0xFFu);
+    mag = u & 0x7FFFFFu;
+    e = -149;
+    if (ex != 0) { mag |= 0x800000u; e = ex - 150; }
+    neg = (u >> 31) != 0;
+    if (mag != 0) {
+        const int tz = __builtin_ctz(mag);
+        mag >>= tz;
+        e += tz;
+    }
+}
+
+__device__ __forceinline__ double i128_to_double(__int128 x) {
+    const bool neg = x < 0;
+    const unsigned __int128 ux = neg ? (unsigned __int128)0 - (unsigned __int128)x : (unsigned __int128)x;
+    const double d = (double)(uint64_t)(ux >> 64) * 18446744073709551616.0 + (double)(uint64_t)ux;
+    return neg ? -d : d;
+}
+
 __global__ __launch_bounds__(kSelThreads) void path_select_kernel(PathParams p) {
     __shared__ float s_lp[kRows][kList];
+    __shared__ float s_v[kRows][kList];
     __shared__ int s_id[kRows][kList];
     __shared__ float s_h[kRows];
-    __shared__ float ps[kSortMax];
-    __shared__ int pc[kSortMax];
-    __shared__ float2 xe[kSortMax];
+    __shared__ float s_lse[kRows];
+    __shared__ __int128 s_key[kRows][kList];
+    __shared__ int s_inf[kRows][kList];
+    __shared__ int s_e0;
+    __shared__ PathKey ps[64];
+    __shared__ PathKey xe[kSortMax];
     __shared__ int rank[kSortMax];
     const int b = blockIdx.x;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -357,66 +409,117 @@ __global__ __launch_bounds__(kSelThreads) void path_select_kernel(PathParams p) 
             if (li[0] == i && lv[0] == v) list_pop(lv, li);
             if (lane == 0) {
                 s_lp[k][r] = v - st.m - logz;
+                s_v[k][r] = v;
                 s_id[k][r] = i;
             }
         }
-        if (lane == 0) s_h[k] = logz - st.s1 / st.s0;
+        if (lane == 0) {
+            s_h[k] = logz - st.s1 / st.s0;
+            s_lse[k] = st.m + logz;
+        }
     }
-    if (threadIdx.x == 0) { ps[0] = 0.f; pc[0] = 0; }
+    __syncthreads();
+    // The sequence's unit: finest lowest set bit, raised if the candidates
+    // would need more than 126 bits for a sum of seven.
+    if (wave == 0) {
+        int lo = 0x7FFFFFFF, hi = -0x7FFFFFFF;
+        if (lane < kRows * m) {
+            const float v = s_v[lane / m][lane % m];
+            uint32_t mag;
+            int e;
+            bool neg;
+            split_float(v, mag, e, neg);
+            if (v != -INFINITY && mag != 0) {
+                lo = e;
+                hi = e + 32 - __builtin_clz(mag);    // 2^hi > |v|
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            lo = min(lo, __shfl_xor(lo, o));
+            hi = max(hi, __shfl_xor(hi, o));
+        }
+        if (lane == 0) s_e0 = hi == -0x7FFFFFFF ? 0 : max(lo, hi + 3 - 126);
+    }
     __syncthreads();
     if (threadIdx.x < kRows * m) {
         const int k = threadIdx.x / m, r = threadIdx.x % m;
+        const float v = s_v[k][r];
+        uint32_t mag;
+        int e;
+        bool neg;
+        split_float(v, mag, e, neg);
+        const int sh = e - s_e0;
+        __int128 key = 0;
+        if (mag != 0) {
+            if (sh >= 0) key = (__int128)mag << sh;
+            else if (sh > -32) key = (__int128)(mag >> -sh);
+            if (neg) key = -key;
+            if (neg && sh < 0 && (sh <= -32 || (mag & ((1u << -sh) - 1u)) != 0)) key -= 1;   // toward -inf
+        }
+        s_key[k][r] = key;
+        s_inf[k][r] = v == -INFINITY;
         p.cand_ids[((int64_t)b * kRows + k) * m + r] = s_id[k][r];
         p.cand_logp[((int64_t)b * kRows + k) * m + r] = s_lp[k][r];
     }
     if (threadIdx.x < kRows) p.entropy[(int64_t)b * kRows + threadIdx.x] = s_h[threadIdx.x];
+    if (threadIdx.x == 0) {
+        PathKey z;
+        z.sum = 0; z.ninf = 0; z.code = 0; z.pad[0] = z.pad[1] = 0;
+        ps[0] = z;
+    }
+    __syncthreads();
 
-    // Beam: the np prefixes live in ps / pc.  Each step builds the np x m
-    // extensions in xe (score, code), gives each its rank among them by
-    // counting the entries that come first (scores descending, then the rank
-    // code ascending; codes are distinct, so ranks are too) -- the count of
-    // entry e is split over `parts` threads and summed in LDS -- and keeps
-    // ranks < P.
+    // Beam: the np prefixes live in ps.  Each step builds the np x m
+    // extensions in xe, gives each its rank among them by counting the
+    // entries that come first (codes are distinct, so ranks are too) -- the
+    // count of entry e is split over `parts` threads and summed in LDS -- and
+    // keeps ranks < P.
     int np = 1;
     for (int k = 0; k < kRows; ++k) {
         const int n = np * m;                  // <= 512 = kSelThreads
         const int parts = kSelThreads / n;
         if (threadIdx.x < n) {
             const int q = threadIdx.x / m, r = threadIdx.x % m;
-            xe[threadIdx.x] = make_float2(ps[q] + s_lp[k][r], __int_as_float((pc[q] << 3) | r));
+            PathKey x;
+            x.sum = ps[q].sum + s_key[k][r];
+            x.ninf = ps[q].ninf + s_inf[k][r];
+            x.code = (ps[q].code << 3) | r;
+            x.pad[0] = x.pad[1] = 0;
+            xe[threadIdx.x] = x;
             rank[threadIdx.x] = 0;
         }
         __syncthreads();
         if (threadIdx.x < parts * n) {
             const int e = threadIdx.x % n, part = threadIdx.x / n;
-            const float2 me = xe[e];
-            const int mc = __float_as_int(me.y);
+            const PathKey me = xe[e];
             const int q0 = part * n / parts, q1 = (part + 1) * n / parts;
             int cnt = 0;
-            for (int q = q0; q < q1; ++q) {
-                const float2 o = xe[q];
-                cnt += before(o.x, __float_as_int(o.y), me.x, mc) ? 1 : 0;
-            }
+            for (int q = q0; q < q1; ++q) cnt += key_before(xe[q], me) ? 1 : 0;
             atomicAdd(&rank[e], cnt);
         }
         __syncthreads();
         const int np2 = min(p.P, n);
-        if (threadIdx.x < n && rank[threadIdx.x] < np2) {
-            const float2 me = xe[threadIdx.x];
-            ps[rank[threadIdx.x]] = me.x;
-            pc[rank[threadIdx.x]] = __float_as_int(me.y);
-        }
+        if (threadIdx.x < n && rank[threadIdx.x] < np2) ps[rank[threadIdx.x]] = xe[threadIdx.x];
         np = np2;
         __syncthreads();
     }
+    // score = sum of candidates - sum of lse + lambda * sum of entropies
+    double shift = 0.0;
     float hsum = 0.f;
 #pragma unroll
-    for (int k = 0; k < kRows; ++k) hsum += s_h[k];
+    for (int k = 0; k < kRows; ++k) {
+        shift -= (double)s_lse[k];
+        hsum += s_h[k];
+    }
+    shift += (double)p.lam * (double)hsum;
     for (int e = threadIdx.x; e < p.P; e += kSelThreads) {
-        p.scores[(int64_t)b * p.P + e] = ps[e] + p.lam * hsum;
+        const PathKey x = ps[e];
+        p.scores[(int64_t)b * p.P + e] =
+            x.ninf ? -INFINITY : (float)(ldexp(i128_to_double(x.sum), s_e0) + shift);
 #pragma unroll
         for (int k = 0; k < kRows; ++k)
-            p.paths[((int64_t)b * p.P + e) * kRows + k] = s_id[k][(pc[e] >> (3 * (kRows - 1 - k))) & 7];
+            p.paths[((int64_t)b * p.P + e) * kRows + k] = s_id[k][(x.code >> (3 * (kRows - 1 - k))) & 7];
     }
 }
 

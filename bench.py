@@ -281,12 +281,15 @@ def cpu_baseline(wl):
             t_attn += time.perf_counter() - t1
     vb_sel = list(range(B))
     t_ver = 0.0
+    traces = []
     for b in vb_sel:
         zt = wl.zt[b:b + 1].float().cpu().numpy()
         zd = wl.zd[b:b + 1].float().cpu().numpy()
         t1 = time.perf_counter()
-        oracle.spec_verify_ref(zt, zd, wl.d_np[b:b + 1], wl.temp_np[b:b + 1], SEED, 0, batch_offset=b)
+        traces.append(oracle.spec_verify_ref(zt, zd, wl.d_np[b:b + 1], wl.temp_np[b:b + 1], SEED, 0,
+                                             batch_offset=b))
         t_ver += time.perf_counter() - t1
+    wl.verify_traces = traces
     cycle = t_fuse + t_attn * (B / len(sample_b)) + t_ver * (B / len(vb_sel))
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {
@@ -648,6 +651,10 @@ def main():
                          "GB/s": round(f_bytes / (f_ms * 1e-3) / 1e9, 1)},
         },
     }
+    calls = args.warmup + K * (1 if args.eager else 3)
+    res["kernels"]["spec_verify"]["near_ties"] = {
+        "count": int(wl.verify.outputs[2].item()), "verify_calls": calls,
+        "rule": "acceptance decisions with |u - p/q| < 1e-6, counted by the kernel"}
     if not args.no_prefill:
         log("[bench] prefill workload: ctx_fuse M=32768, verify B=256")
         res["kernels"].update(prefill_measurements(torch, dfl, synth))
@@ -664,7 +671,26 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(wl)
+        res["kernels"]["spec_verify"]["parity_vs_oracle"] = verify_parity(wl)
     print(json.dumps(res), flush=True)
+
+
+def verify_parity(wl):
+    """The serving batch's verification at offset 0 on the GPU against the
+    oracle's traces of the CPU baseline, sequence by sequence, under the
+    parity rule of the tests (bit-exact; an acceptance decision within 1e-6
+    of its uniform, or a final draw inside its fp32 key bound, is excluded
+    and counted)."""
+    from tests.gpu_util import compare_verify
+    torch = wl.torch
+    wl.verify.args.offset = 0
+    wl.verify()
+    torch.cuda.synchronize()
+    toks = wl.verify.outputs[0].cpu().numpy()
+    lens = wl.verify.outputs[1].cpu().numpy()
+    excluded = sum(compare_verify(toks[b:b + 1], lens[b:b + 1], tr) for b, tr in enumerate(wl.verify_traces))
+    return {"sequences": len(wl.verify_traces), "bit_exact": len(wl.verify_traces) - excluded,
+            "excluded": excluded, "oracle_near_ties": int(sum(tr.near_ties for tr in wl.verify_traces))}
 
 
 if __name__ == "__main__":

@@ -42,6 +42,13 @@ from .philox import uniforms, gumbel
 BLOCK = 8
 N_PROP = BLOCK - 1
 NEAR_TIE = 1e-6
+DRAW_TOP = 8
+# Exact terms of a draw's key, per entry: p, q and r = max(0, p - q) (residual
+# draws; bonus draws give p = q = r = nan), x_t = (z_t - max z_t) / T,
+# x_q = (z_q - max z_q) / T (nan for bonus draws), the Gumbel noise G, and the
+# log-weight w (key = w + G): ln r, or ln p in the zero-residual fallback, or
+# z / T for the bonus.
+DRAW_TERMS = ("p", "q", "r", "x_t", "x_q", "g", "w")
 
 
 @dataclass
@@ -55,6 +62,17 @@ class VerifyTrace:
     near_tie_k: np.ndarray   # [B] first k with |u - rho| < 1e-6 (0 = none)
     near_ties: int           # number of such decisions taken
     sample_gap: np.ndarray   # [B] top-2 key gap of the final draw (inf if greedy)
+    # The final Gumbel-max draw of a sampled sequence, for checking a draw
+    # computed in lower precision: its DRAW_TOP entries with the largest keys
+    # (best first; -1 where unused or greedy), their keys and the exact terms
+    # behind each key (DRAW_TERMS columns), whether the residual was
+    # identically zero (the draw then used p), and the means of |x| under p
+    # and q, x = (z - max z) / T, of the two rows a residual draw compares.
+    draw_idx: np.ndarray = None    # [B, DRAW_TOP] int64
+    draw_key: np.ndarray = None    # [B, DRAW_TOP]
+    draw_terms: np.ndarray = None  # [B, DRAW_TOP, len(DRAW_TERMS)]
+    draw_fallback: np.ndarray = None  # [B] bool
+    draw_mean_abs_x: np.ndarray = None  # [B, 2] E_p|x_t|, E_q|x_q| (residual draws)
 
 
 def _softmax(z):
@@ -70,6 +88,18 @@ def _top2(keys):
     rest = np.delete(keys, i)
     second = np.max(rest) if rest.size else -np.inf
     return i, float(best - second)
+
+
+def _record_draw(tr, b, keys, terms, fallback=False, mean_abs_x=(np.nan, np.nan)):
+    """Keep the DRAW_TOP largest keys of a draw (ties to the lower index) and
+    the exact terms of those entries."""
+    order = np.argsort(-keys, kind="stable")[:DRAW_TOP]
+    n = len(order)
+    tr.draw_idx[b, :n] = order
+    tr.draw_key[b, :n] = keys[order]
+    tr.draw_terms[b, :n] = np.stack([terms[name][order] for name in DRAW_TERMS], axis=-1)
+    tr.draw_fallback[b] = fallback
+    tr.draw_mean_abs_x[b] = mean_abs_x
 
 
 def spec_verify_ref(zt, zd, d, temperature, seed=0, offset=0, seq_block=4, batch_offset=0):
@@ -95,6 +125,11 @@ def spec_verify_ref(zt, zd, d, temperature, seed=0, offset=0, seq_block=4, batch
         near_tie_k=np.zeros(B, dtype=np.int32),
         near_ties=0,
         sample_gap=np.full(B, np.inf),
+        draw_idx=np.full((B, DRAW_TOP), -1, dtype=np.int64),
+        draw_key=np.full((B, DRAW_TOP), -np.inf),
+        draw_terms=np.full((B, DRAW_TOP, len(DRAW_TERMS)), np.nan),
+        draw_fallback=np.zeros(B, dtype=bool),
+        draw_mean_abs_x=np.full((B, 2), np.nan),
     )
     # Acceptance uniforms U(0, b, k, 0) for every sequence and k = 1..7.
     bb, kk = np.meshgrid(batch_offset + np.arange(B), np.arange(1, BLOCK), indexing="ij")
@@ -148,24 +183,34 @@ def _verify_one(b, gb, zt, zd, d, T, seed, offset, u_b, tr):
                 n += 1
                 continue
             r = np.maximum(0.0, p - q)
-            if not np.any(r > 0):
+            fallback = not np.any(r > 0)
+            if fallback:
                 r = p
             g = gumbel(uniforms(seed, offset, 1, gb, k, np.arange(V)))
             with np.errstate(divide="ignore"):
-                keys = np.where(r > 0, np.log(r) + g, -np.inf)
+                w = np.where(r > 0, np.log(r), -np.inf)
+            keys = w + g
             x_new, gap = _top2(keys)
             emitted.append(x_new)
             tr.sample_gap[b] = gap
             tr.kind[b] = 1
+            xt = (zt[k - 1] - np.max(zt[k - 1])) / T
+            xq = (zd[k - 1] - np.max(zd[k - 1])) / T
+            _record_draw(tr, b, keys, {"p": p, "q": q, "r": r, "x_t": xt, "x_q": xq, "g": g, "w": w},
+                         fallback, (float(np.sum(p * np.abs(xt))), float(np.sum(q * np.abs(xq)))))
             done = True
             break
         if not done:
             g = gumbel(uniforms(seed, offset, 1, gb, BLOCK, np.arange(V)))
-            keys = zt[BLOCK - 1] / T + g
+            w = zt[BLOCK - 1] / T
+            keys = w + g
             x_new, gap = _top2(keys)
             emitted.append(x_new)
             tr.sample_gap[b] = gap
             tr.kind[b] = 2
+            nan = np.full(V, np.nan)
+            _record_draw(tr, b, keys, {"p": nan, "q": nan, "r": nan, "x_t": (zt[BLOCK - 1] - np.max(zt[BLOCK - 1])) / T,
+                                       "x_q": nan, "g": g, "w": w})
     tr.n_acc[b] = n
     tr.out_len[b] = len(emitted)
     tr.out_tokens[b, :len(emitted)] = emitted

@@ -198,9 +198,19 @@ typedef struct dflash_attn_args {
  *   all accepted: greedy emits argmax target[b][7]; sampled emits
  *       argmax_i target[b][7][i]/T + G_i  with G from k = 8
  *   G_i = -ln(-ln U(1, b, k, i)).
- * U(s, b, k, i) = ((w >> 41) + 0.5) * 2^-23 where w is word (i mod 4) of
- * Philox4x64-10 (Salmon et al., SC'11) with key (seed, 0) and counter
- * (i / 4, 8b + k, s, offset).
+ * Uniforms: U(s, b, k, i) for stream s, sequence b, position k, entry i.
+ * One Philox4x64-10 block (Salmon et al., SC'11: 10 rounds, multipliers
+ * 0xD2E7470EE14C6C93 and 0xCA5A826395121157, key increments
+ * 0x9E3779B97F4A7C15 and 0xBB67AE8584CAA73B) with key (seed, 0) and counter
+ * (floor(i / 8), 8b + k, s, offset) gives four 64-bit words w0..w3 and
+ * serves the eight entries 8 floor(i / 8) .. + 7:
+ *   w    = word floor(i / 2) mod 4 of the block
+ *   bits = (w >> 41) & 0x7FFFFF   when i is even (bits 41..63)
+ *          (w >> 9)  & 0x7FFFFF   when i is odd  (bits 9..31)
+ *   U    = (bits + 0.5) * 2^-23   (exact in fp32, strictly inside (0, 1))
+ * Stream 0 holds the acceptance uniforms (i = 0), stream 1 the Gumbel noise
+ * of the correction / bonus draw, stream 2 the draft proposals
+ * (dflash_draft_head).
  * Proposal ids outside [0, V) are never accepted.  Decisions with
  * |u - p/q| < 1e-6 are counted into *near_ties (atomically added).
  */
@@ -225,8 +235,8 @@ typedef struct dflash_verify_args {
 
 /*
  * dflash_draft_embed -- block input of the first draft layer.
- * [E4B] "The released serving cycle" (the block is one real anchor followed
- * by seven mask tokens) and [DF2] 4.2 (input representations come from the
+ * [E4B] "The released serving cycle" (a block of eight: the anchor, then
+ * seven mask positions) and [DF2] 4.2 (input representations come from the
  * target's embedding table, shared with the drafter).
  *   x[b][0] = emb[anchor[b]],  x[b][j] = emb[mask_id] for j = 1..7
  * An anchor id outside [0, V) gives a zero row.
@@ -351,7 +361,9 @@ typedef struct dflash_ring_args {
  *     T_b <= 0: argmax_i logits[b][k][i]             (lowest index on ties)
  *     T_b >  0: argmax_i logits[b][k][i] / T_b - ln(-ln u_i)
  * with u_i = U(2, b, k, i), stream 2 of the uniform layout documented at
- * dflash_spec_verify (streams 0 and 1 belong to verification): a Gumbel-max
+ * dflash_spec_verify (counter (floor(i / 8), 8b + k, 2, offset), entry i in
+ * half i mod 2 of word floor(i / 2) mod 4; streams 0 and 1 belong to
+ * verification): a Gumbel-max
  * draw, which is an exact sample from softmax(logits[b][k] / T_b).  Row 0
  * (the anchor) is projected and not sampled.  Rows 1..7 of logits are the
  * draft_logits of dflash_spec_verify for the same cycle (base logits + V,
@@ -386,9 +398,17 @@ typedef struct dflash_head_args {
  *                          score = sum_k cand_logp[b][k-1][r_k] + lambda * sum_k H_k,
  *                          best first, equal scores by the lexicographically
  *                          smaller tuple; written as token ids
- * The drafter proposes the block in one forward, so P_k does not depend on
- * the candidates chosen before k: the score separates per position, and a
- * beam of width P keeps exactly the top P.  Scores are accumulated in fp32.
+ *   scores[b][p]         = that score of path p (fp32; -inf if it holds a -inf logit)
+ * log P_k(x) = z_k(x) - lse_k, and lse_k and lambda * H_k are the same for
+ * every path, so paths are ranked by the EXACT sum of their stored candidate
+ * logits (a 128-bit fixed-point sum at the finest unit among the sequence's
+ * candidates; exact while they span at most 2^123 in magnitude); equal sums
+ * go to the smaller rank tuple.  A path through a -inf logit comes after
+ * every finite one (fewer -inf candidates first, then the sum of its finite
+ * ones).  +inf and NaN logits are outside the supported domain.  The drafter
+ * proposes the block in one forward, so P_k does not depend on the
+ * candidates chosen before k: the score separates per position, and a beam
+ * of width P keeps exactly the top P.
  * Rows 1..7 of dflash_draft_head's logits are the natural input
  * (batch_stride = 8 V, row_stride = V).
  */

@@ -3,9 +3,9 @@
 Test infrastructure only (see the package docstring).
 
 What the pages fix:
-* [E4B] "The released serving cycle": the drafter forms an eight-position
-  block, one real anchor followed by seven mask tokens, and runs one
-  non-causal five-layer forward over it.
+* [E4B] "The released serving cycle": the drafter's block has eight
+  positions (the anchor, then seven mask positions) and one non-causal
+  five-layer forward covers all of them.
 * [DF2] 4.2 "Geteilte Embeddings & LM-Head": the anchor's input
   representation comes from the target's (shared, frozen) embedding table.
 * [DF2] 4.1: Q_i = W_i^Q H_d and the block half of K_i / V_i is W_i^K H_d /

@@ -186,6 +186,21 @@ def _workspace(nbytes, workspace, device):
     return workspace, workspace.numel() * workspace.element_size()
 
 
+def _record(stream, objs):
+    """Tell torch's caching allocator that every tensor the call reads or
+    writes is in use on `stream` when that is not the current stream: the
+    workspace and outputs allocated here live on the current stream, and the
+    one-shot wrappers drop them as soon as the call is enqueued, so without
+    this their memory could be handed out again while the kernels still run."""
+    if stream is None or stream == torch.cuda.current_stream(stream.device):
+        return
+    for o in objs:
+        if isinstance(o, (list, tuple)):
+            _record(stream, o)
+        elif isinstance(o, torch.Tensor):
+            o.record_stream(stream)
+
+
 class Prepared:
     """A validated argument struct plus its workspace: call it to enqueue."""
 
@@ -195,6 +210,7 @@ class Prepared:
 
     def __call__(self, stream=None):
         _check(self._fn(ctypes.byref(self.args), _ptr(self.workspace), self.ws_bytes, _stream(stream)))
+        _record(stream, (self.workspace, self._keep))
 
 
 # ---------------------------------------------------------------- ctx_fuse
@@ -377,6 +393,7 @@ class PreparedEmbed:
 
     def __call__(self, stream=None):
         _check(load().dflash_draft_embed(ctypes.byref(self.args), _stream(stream)))
+        _record(stream, self._keep)
 
 
 def prepare_draft_embed(emb, anchor, mask_id, x=None):
@@ -520,6 +537,7 @@ class PreparedRing:
 
     def __call__(self, stream=None):
         _check(load().dflash_ring_append(ctypes.byref(self.args), _stream(stream)))
+        _record(stream, self._keep)
 
 
 def prepare_ring_append(ring, ctx_len, n_new, rows_per_seq=8, slot=None, pos=None):

@@ -7,6 +7,7 @@ DFlashError if it has not been built.
 
 from ._lib import (DFlashError, load, ctx_fuse, block_attn, spec_verify,
                    prepare_ctx_fuse, prepare_block_attn, prepare_spec_verify,
+                   spec_verify_noalloc, prepare_spec_verify_noalloc, verify_scratch_bytes,
                    draft_embed, draft_qkv, draft_mlp,
                    prepare_draft_embed, prepare_draft_qkv, prepare_draft_mlp,
                    ring_append, prepare_ring_append, draft_head, prepare_draft_head,
@@ -14,6 +15,7 @@ from ._lib import (DFlashError, load, ctx_fuse, block_attn, spec_verify,
 
 __all__ = ["DFlashError", "load", "ctx_fuse", "block_attn", "spec_verify",
            "prepare_ctx_fuse", "prepare_block_attn", "prepare_spec_verify",
+           "spec_verify_noalloc", "prepare_spec_verify_noalloc", "verify_scratch_bytes",
            "draft_embed", "draft_qkv", "draft_mlp",
            "prepare_draft_embed", "prepare_draft_qkv", "prepare_draft_mlp",
            "ring_append", "prepare_ring_append", "draft_head", "prepare_draft_head",

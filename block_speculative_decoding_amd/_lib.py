@@ -97,6 +97,7 @@ EXPORTS = ["dflash_version", "dflash_last_error", "dflash_args_size",
            "dflash_draft_qkv_workspace_size", "dflash_draft_mlp_workspace_size",
            "dflash_draft_head_workspace_size", "dflash_draft_paths_workspace_size",
            "dflash_ctx_fuse", "dflash_block_attn", "dflash_spec_verify",
+           "dflash_spec_verify_noalloc", "dflash_verify_scratch_bytes",
            "dflash_draft_embed", "dflash_draft_qkv", "dflash_draft_mlp", "dflash_ring_append",
            "dflash_draft_head", "dflash_draft_paths"]
 
@@ -128,6 +129,10 @@ def load():
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.POINTER(st), _P, ctypes.c_size_t, _P]
+    lib.dflash_spec_verify_noalloc.restype = ctypes.c_int
+    lib.dflash_spec_verify_noalloc.argtypes = [ctypes.POINTER(VerifyArgs), _P]
+    lib.dflash_verify_scratch_bytes.restype = ctypes.c_int
+    lib.dflash_verify_scratch_bytes.argtypes = [ctypes.POINTER(ctypes.c_size_t)]
     lib.dflash_draft_embed.restype = ctypes.c_int
     lib.dflash_draft_embed.argtypes = [ctypes.POINTER(EmbedArgs), _P]
     lib.dflash_ring_append.restype = ctypes.c_int
@@ -176,8 +181,11 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+_NO_WORKSPACE = object()   # sizes the call but allocates no workspace (allocation-free entry point)
+
+
 def _workspace(nbytes, workspace, device):
-    if nbytes == 0:
+    if nbytes == 0 or workspace is _NO_WORKSPACE:
         return None, 0
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -380,6 +388,45 @@ def prepare_spec_verify(target_logits, draft_logits, draft_tokens, temperature, 
 
 def spec_verify(*args, stream=None, **kw):
     prep = prepare_spec_verify(*args, **kw)
+    prep(stream)
+    return prep.outputs
+
+
+class PreparedNoAlloc:
+    """dflash_spec_verify_noalloc: the library's fixed device scratch, no workspace."""
+
+    def __init__(self, args, keep):
+        self.args, self._keep = args, keep
+
+    def __call__(self, stream=None):
+        _check(load().dflash_spec_verify_noalloc(ctypes.byref(self.args), _stream(stream)))
+        _record(stream, self._keep)
+
+
+def verify_scratch_bytes():
+    """Size of the allocation-free verification's device scratch."""
+    n = ctypes.c_size_t()
+    _check(load().dflash_verify_scratch_bytes(ctypes.byref(n)))
+    return n.value
+
+
+def prepare_spec_verify_noalloc(target_logits, draft_logits, draft_tokens, temperature, out_tokens, out_len,
+                                near_ties, seed=0, offset=0):
+    """Allocation-free verification (include/dflash.h, dflash_spec_verify_noalloc):
+    the arguments of prepare_spec_verify, with every output supplied by the
+    caller; nothing is allocated here or in the library."""
+    for n, t in (("out_tokens", out_tokens), ("out_len", out_len), ("near_ties", near_ties)):
+        if t is None:
+            raise DFlashError(-1, f"{n} must be supplied: this entry point allocates nothing")
+    prep = prepare_spec_verify(target_logits, draft_logits, draft_tokens, temperature, seed, offset,
+                               out_tokens, out_len, near_ties, workspace=_NO_WORKSPACE)
+    out = PreparedNoAlloc(prep.args, prep._keep)
+    out.outputs = prep.outputs
+    return out
+
+
+def spec_verify_noalloc(*args, stream=None, **kw):
+    prep = prepare_spec_verify_noalloc(*args, **kw)
     prep(stream)
     return prep.outputs
 

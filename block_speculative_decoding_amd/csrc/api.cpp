@@ -93,6 +93,9 @@ int validate_verify_sizes(const char* fn, const dflash_verify_args* a) {
     return DFLASH_OK;
 }
 
+// Sizes, pointers and strides of a verification call (defined below).
+int validate_verify(const char* fn, const dflash_verify_args* a);
+
 int validate_draft_b(const char* fn, int dtype, int B) {
     int rc = check_dtype(fn, dtype);
     if (rc) return rc;
@@ -280,6 +283,41 @@ int dflash_block_attn(const dflash_attn_args* a, void* ws, size_t ws_bytes, void
 
 int dflash_spec_verify(const dflash_verify_args* a, void* ws, size_t ws_bytes, void* stream) {
     const char* fn = "dflash_spec_verify";
+    int rc = validate_verify(fn, a);
+    if (rc) return rc;
+    const size_t need = dflash::verify_workspace_bytes(a->B, a->V);
+    rc = check_ws(fn, need, ws, ws_bytes);
+    if (rc) return rc;
+    return launched(fn, dflash::launch_verify(*a, ws, static_cast<hipStream_t>(stream)));
+}
+
+int dflash_spec_verify_noalloc(const dflash_verify_args* a, void* stream) {
+    const char* fn = "dflash_spec_verify_noalloc";
+    int rc = validate_verify(fn, a);
+    if (rc) return rc;
+    const size_t need = dflash::verify_workspace_bytes(a->B, a->V);
+    if (need > dflash::kVerifyScratchBytes)
+        return fail(DFLASH_EWORKSPACE,
+                    "%s: B = %d, V = %lld needs %zu bytes of scratch, above the %zu-byte device array of the "
+                    "allocation-free entry point (use dflash_spec_verify with a workspace)",
+                    fn, a->B, (long long)a->V, need, dflash::kVerifyScratchBytes);
+    void* ws = nullptr;
+    const hipError_t e = dflash::verify_scratch(&ws);
+    if (e != hipSuccess) return fail(DFLASH_EHIP, "%s: scratch address lookup failed: %s", fn, hipGetErrorString(e));
+    return launched(fn, dflash::launch_verify(*a, ws, static_cast<hipStream_t>(stream)));
+}
+
+int dflash_verify_scratch_bytes(size_t* bytes) {
+    if (!bytes) return fail(DFLASH_EINVAL, "dflash_verify_scratch_bytes: null bytes");
+    *bytes = dflash::kVerifyScratchBytes;
+    return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+int validate_verify(const char* fn, const dflash_verify_args* a) {
     int rc = validate_verify_sizes(fn, a);
     if (rc) return rc;
     REQUIRE_PTR(a->target_logits);
@@ -295,11 +333,12 @@ int dflash_spec_verify(const dflash_verify_args* a, void* ws, size_t ws_bytes, v
         return fail(DFLASH_EINVAL, "%s: negative batch stride", fn);
     if ((a->t_row_stride | a->d_row_stride | a->t_batch_stride | a->d_batch_stride) % 8 != 0)
         return fail(DFLASH_EINVAL, "%s: strides must be multiples of 8 elements", fn);
-    const size_t need = dflash::verify_workspace_bytes(a->B, a->V);
-    rc = check_ws(fn, need, ws, ws_bytes);
-    if (rc) return rc;
-    return launched(fn, dflash::launch_verify(*a, ws, static_cast<hipStream_t>(stream)));
+    return DFLASH_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int dflash_draft_embed(const dflash_embed_args* a, void* stream) {
     const char* fn = "dflash_draft_embed";

@@ -12,6 +12,10 @@ namespace dflash {
 // ---- spec_verify ----
 size_t verify_workspace_bytes(int B, int64_t V);
 hipError_t launch_verify(const dflash_verify_args& a, void* ws, hipStream_t s);
+// Size of the allocation-free entry point's device scratch, and its address
+// on the current device (looked up once per device).
+constexpr size_t kVerifyScratchBytes = size_t(4) << 20;
+hipError_t verify_scratch(void** ptr);
 
 // ---- block_attn ----
 struct AttnPlan {

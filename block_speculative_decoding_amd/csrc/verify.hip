@@ -15,6 +15,8 @@
 //   3. sample    -- vocab-parallel Gumbel-max over the one row a sampled
 //                   sequence still needs (residual max(0, p-q) or the bonus).
 //   4. finalize  -- one wave per sequence: merge the Gumbel-max partials.
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -450,7 +452,33 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Params p) {
     }
 }
 
+// Scratch of the allocation-free entry point: every GPU the library runs on
+// holds its own copy of this array until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in):
+// it uses the device address hipGetSymbolAddress returns for the current
+// device.  Every allocation-free call on a GPU shares that GPU's copy.
+static __device__ __align__(256) unsigned char scratch[kVerifyScratchBytes];
+
 }  // namespace
+
+hipError_t verify_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 size_t verify_workspace_bytes(int B, int64_t V) {
     const int64_t nch1 = (V + kStatsChunk - 1) / kStatsChunk;

@@ -461,6 +461,21 @@ int dflash_block_attn(const dflash_attn_args* args, void* workspace,
 int dflash_spec_verify(const dflash_verify_args* args, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* Allocation-free dflash_spec_verify, for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, results
+ * and errors as dflash_spec_verify; the scratch comes from a fixed device
+ * array of dflash_verify_scratch_bytes() bytes (4 MiB) that the library holds
+ * on every GPU it runs on until the process ends.  It calls no allocating
+ * routine.  Calls whose dflash_verify_workspace_size exceeds that size are
+ * rejected with DFLASH_EWORKSPACE (e.g. B = 1048 at V = 262144 still fits).
+ * Every allocation-free call on a GPU uses that GPU's one array: calls that
+ * overlap on one GPU (concurrent streams, or threads without ordering) race
+ * and must not be issued; calls ordered on one stream are fine.  The first
+ * call on a device looks up the array's device address (no allocation). */
+int dflash_spec_verify_noalloc(const dflash_verify_args* args, void* stream);
+int dflash_verify_scratch_bytes(size_t* bytes);
+
 /* The draft layer around block attention (dflash_draft_embed needs no
  * workspace). */
 int dflash_draft_embed(const dflash_embed_args* args, void* stream);

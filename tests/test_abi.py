@@ -39,7 +39,7 @@ def test_header_declares_every_operation():
               "dflash_args_size", "dflash_draft_embed", "dflash_draft_qkv", "dflash_draft_mlp",
               "dflash_draft_qkv_workspace_size", "dflash_draft_mlp_workspace_size", "dflash_ring_append",
               "dflash_draft_head", "dflash_draft_head_workspace_size", "dflash_draft_paths",
-              "dflash_draft_paths_workspace_size"):
+              "dflash_draft_paths_workspace_size", "dflash_spec_verify_noalloc", "dflash_verify_scratch_bytes"):
         assert f in fns
 
 
@@ -137,6 +137,32 @@ def test_verify_validation(lib):
     # workspace grows with B and V
     assert _ws(lib, "verify", _verify_args(B=8))[1] > n
     assert _ws(lib, "verify", _verify_args(V=262144))[1] > n
+
+
+def test_verify_noalloc_validation(lib):
+    # The allocation-free entry point validates like dflash_spec_verify and
+    # rejects calls whose workspace would exceed its fixed device scratch;
+    # none of these calls reaches the GPU.
+    n = ctypes.c_size_t()
+    assert lib.dflash_verify_scratch_bytes(ctypes.byref(n)) == 0 and n.value == 4 << 20
+    cap = n.value
+    assert _ws(lib, "verify", _verify_args(B=1048, V=262144))[1] <= cap
+    assert _ws(lib, "verify", _verify_args(B=1049, V=262144))[1] > cap
+
+    def call(a):
+        return lib.dflash_spec_verify_noalloc(ctypes.byref(a), None)
+
+    def big(B, V):
+        return _verify_args(B=B, V=V, t_batch_stride=8 * V, t_row_stride=V, d_batch_stride=7 * V, d_row_stride=V)
+    assert call(big(1049, 262144)) == -4
+    msg = lib.dflash_last_error().decode()
+    assert "dflash_spec_verify_noalloc" in msg and str(cap) in msg and "B = 1049" in msg
+    assert call(big(4096, 1 << 20)) == -4
+    assert call(_verify_args(target_logits=None)) == -1
+    assert call(_verify_args(V=4100)) == -1
+    assert call(_verify_args(dtype=7)) == -2
+    assert lib.dflash_spec_verify_noalloc(None, None) == -1
+    assert lib.dflash_verify_scratch_bytes(None) == -1
 
 
 def test_attn_validation(lib):

@@ -48,7 +48,7 @@ from .block_attn import block_attn_ref, attend, prep_block
 from .spec_verify import spec_verify_ref, VerifyTrace
 from .draft_layer import embed_block, qkv_ref, mlp_ref, o_proj_residual_ref, ffn_ref, silu, layer_weight_shapes
 from .window_cache import ring_pages, ring_append, ring_block_table
-from .draft_head import head_logits_ref, draft_keys, draft_sample_ref
+from .draft_head import head_logits_ref, draft_keys, draft_sample_ref, draft_stats_ref
 from .dflash2 import depthwise_conv_ref, conv_mlp_ref, row_stats_ref, top_paths_ref, path_select_ref
 
 __all__ = [
@@ -59,6 +59,6 @@ __all__ = [
     "spec_verify_ref", "VerifyTrace",
     "embed_block", "qkv_ref", "mlp_ref", "o_proj_residual_ref", "ffn_ref", "silu", "layer_weight_shapes",
     "ring_pages", "ring_append", "ring_block_table",
-    "head_logits_ref", "draft_keys", "draft_sample_ref",
+    "head_logits_ref", "draft_keys", "draft_sample_ref", "draft_stats_ref",
     "depthwise_conv_ref", "conv_mlp_ref", "row_stats_ref", "top_paths_ref", "path_select_ref",
 ]

@@ -15,6 +15,11 @@ Readings (listed in the design notes as well):
 * The head is applied to all eight block rows of the final-norm output
   (row 0, the anchor, is computed and not used); logits are stored in the
   storage type, and sampling reads the stored values.
+* The normaliser of q_k = softmax(z_k / T) (the drafter's distribution that
+  sampled verification divides by) is a statistic of the same stored row,
+  so the head can hand it to verification, which then reads no draft row
+  for it ([E4B] "Why exact verification preserves the target": the
+  acceptance ratio p / q).
 * Proposal k = 1..7 of sequence b comes from row k: greedy (T <= 0) takes
   the argmax (lowest index on ties); sampled takes the Gumbel-max draw
   argmax_i z_i / T + G_i with G_i = -ln(-ln U(2, b, k, i)) -- stream 2 of
@@ -42,6 +47,27 @@ def draft_keys(row, T, seed, offset, b, k):
     if not T > 0:
         return row
     return row / T + gumbel(uniform_row(seed, offset, DRAFT_STREAM, b, k, row.shape[0]))
+
+
+def draft_stats_ref(z, temperature):
+    """Softmax statistics of the proposal rows at each sequence's temperature,
+    the normaliser of q_k = softmax(z[b, k] / T_b) that verification needs:
+    for k = 1..7, m = max_i z[b, k, i] and s = sum_i exp((z[b, k, i] - m) / T_b),
+    from the stored logits z [B, 8, V].  Greedy sequences (T <= 0) need none:
+    (-inf, 0).  Returns float64 [B, 7, 2]."""
+    z = np.asarray(z, dtype=np.float64)
+    B = z.shape[0]
+    out = np.zeros((B, 7, 2))
+    for b in range(B):
+        T = float(temperature[b])
+        if not T > 0:
+            out[b, :, 0] = -np.inf
+            continue
+        rows = z[b, 1:]
+        m = np.max(rows, axis=-1)
+        out[b, :, 0] = m
+        out[b, :, 1] = np.sum(np.exp((rows - m[:, None]) / T), axis=-1)
+    return out
 
 
 def draft_sample_ref(z, temperature, seed=0, offset=0):

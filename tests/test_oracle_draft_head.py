@@ -2,12 +2,14 @@
 proposals are the lowest-index argmax, sampled proposals follow
 softmax(z / T) (chi-square over independent offsets), a vanishing
 temperature reduces sampling to the argmax, and draws use stream 2 (the
-verification streams give other draws)."""
+verification streams give other draws); the proposal rows' softmax statistics
+match scipy's logsumexp and closed forms."""
 
 import numpy as np
 import pytest
 from scipy import stats
 
+import oracle
 from oracle.draft_head import DRAFT_STREAM, draft_sample_ref, head_logits_ref
 from oracle.philox import gumbel, uniform_row
 
@@ -71,3 +73,33 @@ def test_draws_use_stream_two():
     # with V = 4096 the three streams' draws differ in at least one of the seven rows
     other = [[int(np.argmax(z[0, k] / T + gumbel(uniform_row(3, 11, s, 0, k, V)))) for k in range(1, 8)] for s in (0, 1)]
     assert other[0] != d[0].tolist() and other[1] != d[0].tolist()
+
+
+def test_draft_stats_closed_forms_and_library():
+    # s is the softmax normaliser at temperature T relative to the row max:
+    # log(s) + m / T = logsumexp(z / T) (scipy); constant rows give s = V;
+    # one logit far above the rest gives s = 1; greedy rows carry none.
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(12)
+    B, V = 4, 600
+    z = 3.0 * rng.standard_normal((B, 8, V))
+    temp = np.array([0.7, 0.0, 1.0, 2.5])
+    st = oracle.draft_stats_ref(z, temp)
+    for b in (0, 2, 3):
+        T = temp[b]
+        np.testing.assert_array_equal(st[b, :, 0], z[b, 1:].max(axis=-1))
+        np.testing.assert_allclose(np.log(st[b, :, 1]) + st[b, :, 0] / T, logsumexp(z[b, 1:] / T, axis=-1),
+                                   rtol=1e-13)
+        # q_k(x) = exp((z - m) / T) / s sums to one, and matches softmax(z / T)
+        q = np.exp((z[b, 1:] - st[b, :, :1]) / T) / st[b, :, 1:]
+        np.testing.assert_allclose(q.sum(axis=-1), 1.0, rtol=1e-13)
+    assert np.all(st[1, :, 0] == -np.inf) and np.all(st[1, :, 1] == 0)
+    flat = np.zeros((1, 8, V))
+    np.testing.assert_allclose(oracle.draft_stats_ref(flat, [0.8])[0, :, 1], V)
+    spike = np.zeros((1, 8, V))
+    spike[0, :, 7] = 1e4
+    np.testing.assert_allclose(oracle.draft_stats_ref(spike, [1.0])[0, :, 1], 1.0)
+    # row 0 (the anchor) is not a proposal row
+    z2 = z.copy()
+    z2[:, 0] += 100.0
+    np.testing.assert_array_equal(oracle.draft_stats_ref(z2, temp), st)

@@ -510,6 +510,31 @@ def head_measurement(torch, dfl, synth):
                                     draft_tokens=d, workspace=mixed.workspace)
     m_ms = timed(torch, mixed, warmup=2, reps=10)
     g_ms = timed(torch, greedy, warmup=2, reps=10)
+    # NEXT-2's statistics half: the head also folds the sampled proposal rows'
+    # softmax statistics, and verification takes them instead of reading the
+    # draft rows.  Timed as head + verify over the same logits, against head
+    # + verify that computes them itself (target N(0, 4^2); the head's mix).
+    stats = torch.empty((B, 7, 2), dtype=torch.float32, device=dev)
+    with_stats = dfl.prepare_draft_head(y, w, temp, seed=SEED, offset=0, logits=logits, draft_tokens=d,
+                                        workspace=mixed.workspace, draft_stats=stats)
+    s_ms = timed(torch, with_stats, warmup=2, reps=10)
+    zt = (4.0 * torch.randn((B, 8, V), generator=g, device=dev, dtype=torch.float32)).to(bf)
+    ver_plain = dfl.prepare_spec_verify(zt, logits[:, 1:], d, temp, seed=SEED, offset=0)
+    ver_stats = dfl.prepare_spec_verify(zt, logits[:, 1:], d, temp, seed=SEED, offset=0,
+                                        workspace=ver_plain.workspace, draft_stats=stats)
+    vp_ms = timed(torch, ver_plain, warmup=2, reps=10)
+    vs_ms = timed(torch, ver_stats, warmup=2, reps=10)
+
+    def pair(head, ver):
+        def run():
+            head()
+            ver()
+        return run
+    pp_ms = timed(torch, pair(mixed, ver_plain), warmup=2, reps=10)
+    ps_ms = timed(torch, pair(with_stats, ver_stats), warmup=2, reps=10)
+    n_samp = int((temp > 0).sum().item())
+    v_read_plain = (8 * (B - n_samp) + 14 * n_samp) * V * 2
+    v_read_stats = (8 * (B - n_samp) + 7 * n_samp) * V * 2
     # DFlash2's path selector on the head's own logits (rows 1..7): top-4
     # candidates per position, 16 paths.
     paths = dfl.prepare_draft_paths(logits, 4, 16, 0.2)
@@ -521,9 +546,17 @@ def head_measurement(torch, dfl, synth):
     # the seven proposal rows read back by the sampling pass.
     nbytes = V * 2560 * 2 + M * 2560 * 2 + M * V * 2 + 7 * B * V * 2
     n_sampled = int((temp > 0).sum().item())
-    del w, logits, mixed, greedy, paths
+    del w, logits, mixed, greedy, paths, with_stats, ver_plain, ver_stats, zt
     torch.cuda.empty_cache()
-    return {"draft_paths_b64": {"ms": round(p_ms, 4), "m": 4, "P": 16, "V": V,
+    return {"head_stats_into_verify_b64": {
+                "head_ms": round(m_ms, 4), "head_with_stats_ms": round(s_ms, 4),
+                "verify_ms": round(vp_ms, 4), "verify_with_stats_ms": round(vs_ms, 4),
+                "head_then_verify_ms": round(pp_ms, 4), "head_with_stats_then_verify_ms": round(ps_ms, 4),
+                "sampled_sequences": n_samp,
+                "verify_read_bytes": v_read_plain, "verify_with_stats_read_bytes": v_read_stats,
+                "verify_with_stats_GB/s": round(v_read_stats / (vs_ms * 1e-3) / 1e9, 1),
+                "verify_with_stats_hbm_frac": round(v_read_stats / (vs_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "draft_paths_b64": {"ms": round(p_ms, 4), "m": 4, "P": 16, "V": V,
                                 "GB/s": round(p_bytes / (p_ms * 1e-3) / 1e9, 1),
                                 "hbm_frac": round(p_bytes / (p_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                 "algorithmic_bytes": p_bytes},

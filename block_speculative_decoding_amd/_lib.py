@@ -53,7 +53,7 @@ class VerifyArgs(ctypes.Structure):
                 ("draft_logits", _P), ("d_batch_stride", _I64), ("d_row_stride", _I64),
                 ("draft_tokens", _P), ("temperature", _P),
                 ("seed", _U64), ("offset", _U64),
-                ("out_tokens", _P), ("out_len", _P), ("near_ties", _P)]
+                ("out_tokens", _P), ("out_len", _P), ("near_ties", _P), ("draft_stats", _P)]
 
 
 class EmbedArgs(ctypes.Structure):
@@ -81,7 +81,7 @@ class RingArgs(ctypes.Structure):
 
 class HeadArgs(ctypes.Structure):
     _fields_ = [("dtype", _I32), ("B", _I32), ("V", _I64), ("y", _P), ("w_head", _P), ("temperature", _P),
-                ("seed", _U64), ("offset", _U64), ("logits", _P), ("draft_tokens", _P)]
+                ("seed", _U64), ("offset", _U64), ("logits", _P), ("draft_tokens", _P), ("draft_stats", _P)]
 
 
 class PathsArgs(ctypes.Structure):
@@ -339,13 +339,15 @@ def block_attn(*args, stream=None, **kw):
 
 # ---------------------------------------------------------------- spec_verify
 def prepare_spec_verify(target_logits, draft_logits, draft_tokens, temperature, seed=0, offset=0,
-                        out_tokens=None, out_len=None, near_ties=None, workspace=None):
+                        out_tokens=None, out_len=None, near_ties=None, workspace=None, draft_stats=None):
     """Exact speculative verification (include/dflash.h, dflash_spec_verify).
 
     target_logits [B, 8, V] and draft_logits [B, 7, V] (last dim contiguous;
     any 16-byte-aligned row/batch strides); draft_tokens int32 [B, 7];
     temperature float32 [B] (<= 0: greedy).  Outputs int32 [B, 8], int32 [B]
     and a uint64-sized int64 [1] near-tie counter (allocated if None).
+    draft_stats: optional float32 [B, 7, 2] from draft_head (the draft rows'
+    softmax statistics; their rows are then not read for statistics).
     """
     lib = load()
     dt = target_logits.dtype
@@ -367,6 +369,8 @@ def prepare_spec_verify(target_logits, draft_logits, draft_tokens, temperature, 
     _need(out_tokens, "out_tokens", torch.int32, (B, 8))
     _need(out_len, "out_len", torch.int32, (B,))
     _need(near_ties, "near_ties", torch.int64, (1,))
+    if draft_stats is not None:
+        _need(draft_stats, "draft_stats", torch.float32, (B, 7, 2))
     a = VerifyArgs()
     a.dtype = _dtype_code(target_logits)
     a.B, a.V = B, V
@@ -377,11 +381,13 @@ def prepare_spec_verify(target_logits, draft_logits, draft_tokens, temperature, 
     a.draft_tokens, a.temperature = draft_tokens.data_ptr(), temperature.data_ptr()
     a.seed, a.offset = int(seed), int(offset)
     a.out_tokens, a.out_len, a.near_ties = out_tokens.data_ptr(), out_len.data_ptr(), near_ties.data_ptr()
+    a.draft_stats = None if draft_stats is None else draft_stats.data_ptr()
     nbytes = ctypes.c_size_t()
     _check(lib.dflash_verify_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
     ws, wsb = _workspace(nbytes.value, workspace, dev)
     prep = Prepared(lib.dflash_spec_verify, a, ws, wsb,
-                    (target_logits, draft_logits, draft_tokens, temperature, out_tokens, out_len, near_ties))
+                    (target_logits, draft_logits, draft_tokens, temperature, out_tokens, out_len, near_ties,
+                     draft_stats))
     prep.outputs = (out_tokens, out_len, near_ties)
     return prep
 
@@ -411,7 +417,7 @@ def verify_scratch_bytes():
 
 
 def prepare_spec_verify_noalloc(target_logits, draft_logits, draft_tokens, temperature, out_tokens, out_len,
-                                near_ties, seed=0, offset=0):
+                                near_ties, seed=0, offset=0, draft_stats=None):
     """Allocation-free verification (include/dflash.h, dflash_spec_verify_noalloc):
     the arguments of prepare_spec_verify, with every output supplied by the
     caller; nothing is allocated here or in the library."""
@@ -419,7 +425,7 @@ def prepare_spec_verify_noalloc(target_logits, draft_logits, draft_tokens, tempe
         if t is None:
             raise DFlashError(-1, f"{n} must be supplied: this entry point allocates nothing")
     prep = prepare_spec_verify(target_logits, draft_logits, draft_tokens, temperature, seed, offset,
-                               out_tokens, out_len, near_ties, workspace=_NO_WORKSPACE)
+                               out_tokens, out_len, near_ties, workspace=_NO_WORKSPACE, draft_stats=draft_stats)
     out = PreparedNoAlloc(prep.args, prep._keep)
     out.outputs = prep.outputs
     return out
@@ -624,14 +630,17 @@ def ring_append(*args, stream=None, **kw):
 
 
 # ---------------------------------------------------------------- LM head
-def prepare_draft_head(y, w_head, temperature, seed=0, offset=0, logits=None, draft_tokens=None, workspace=None):
+def prepare_draft_head(y, w_head, temperature, seed=0, offset=0, logits=None, draft_tokens=None, workspace=None,
+                       draft_stats=None):
     """Shared LM head over the block rows and the seven draft proposals
     (include/dflash.h, dflash_draft_head).
 
     y [B, 8, 2560] final-norm output; w_head [V, 2560]; temperature float32
     [B] (<= 0: greedy).  Outputs logits [B, 8, V] (dtype of y) and
     draft_tokens int32 [B, 7] (allocated if None); logits[:, 1:] is the
-    draft_logits input of spec_verify.
+    draft_logits input of spec_verify.  draft_stats: None (not computed),
+    True (allocated) or a float32 [B, 7, 2] tensor; it is the draft_stats
+    input of spec_verify and is returned as a third output when requested.
     """
     lib = load()
     dt = y.dtype
@@ -647,16 +656,21 @@ def prepare_draft_head(y, w_head, temperature, seed=0, offset=0, logits=None, dr
         draft_tokens = torch.empty((B, BLOCK - 1), dtype=torch.int32, device=dev)
     _need(logits, "logits", dt, (B, BLOCK, V))
     _need(draft_tokens, "draft_tokens", torch.int32, (B, BLOCK - 1))
+    if draft_stats is True:
+        draft_stats = torch.empty((B, BLOCK - 1, 2), dtype=torch.float32, device=dev)
+    if draft_stats is not None:
+        _need(draft_stats, "draft_stats", torch.float32, (B, BLOCK - 1, 2))
     a = HeadArgs()
     a.dtype, a.B, a.V = _dtype_code(y), B, V
     a.y, a.w_head, a.temperature = y.data_ptr(), w_head.data_ptr(), temperature.data_ptr()
     a.seed, a.offset = int(seed), int(offset)
     a.logits, a.draft_tokens = logits.data_ptr(), draft_tokens.data_ptr()
+    a.draft_stats = None if draft_stats is None else draft_stats.data_ptr()
     nbytes = ctypes.c_size_t()
     _check(lib.dflash_draft_head_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
     ws, wsb = _workspace(nbytes.value, workspace, dev)
-    prep = Prepared(lib.dflash_draft_head, a, ws, wsb, (y, w_head, temperature, logits, draft_tokens))
-    prep.outputs = (logits, draft_tokens)
+    prep = Prepared(lib.dflash_draft_head, a, ws, wsb, (y, w_head, temperature, logits, draft_tokens, draft_stats))
+    prep.outputs = (logits, draft_tokens) if draft_stats is None else (logits, draft_tokens, draft_stats)
     return prep
 
 

@@ -333,6 +333,8 @@ int validate_verify(const char* fn, const dflash_verify_args* a) {
         return fail(DFLASH_EINVAL, "%s: negative batch stride", fn);
     if ((a->t_row_stride | a->d_row_stride | a->t_batch_stride | a->d_batch_stride) % 8 != 0)
         return fail(DFLASH_EINVAL, "%s: strides must be multiples of 8 elements", fn);
+    if (a->draft_stats && !aligned16(a->draft_stats))
+        return fail(DFLASH_EINVAL, "%s: draft_stats is not 16-byte aligned", fn);
     return DFLASH_OK;
 }
 
@@ -420,6 +422,8 @@ int dflash_draft_head(const dflash_head_args* a, void* ws, size_t ws_bytes, void
     REQUIRE_PTR(a->temperature);
     REQUIRE_PTR(a->logits);
     REQUIRE_PTR(a->draft_tokens);
+    if (a->draft_stats && !aligned16(a->draft_stats))
+        return fail(DFLASH_EINVAL, "%s: draft_stats is not 16-byte aligned", fn);
     rc = check_ws(fn, dflash::head_workspace_bytes(a->B, a->V), ws, ws_bytes);
     if (rc) return rc;
     return launched(fn, dflash::launch_head(*a, ws, static_cast<hipStream_t>(stream)));

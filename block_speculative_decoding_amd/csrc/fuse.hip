@@ -250,7 +250,9 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
             const float Tb = s_temp[row >> 3];
             const bool greedy = !(Tb > 0.f);
             const float invT = greedy ? 1.f : 1.0f / Tb;
-            float best = -INFINITY;
+            const bool stats = active && !greedy && hp.spart != nullptr;   // uniform over the quad
+            const StatScale sc = stat_scale(greedy ? 1.f : Tb);
+            float best = -INFINITY, sm = -INFINITY, ss = 0.f;
             int bi = 0x7FFFFFFF;
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
@@ -263,11 +265,20 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
                     f[0] = lo_bf16(w.x); f[1] = hi_bf16(w.x); f[2] = lo_bf16(w.y); f[3] = hi_bf16(w.y);
                     f[4] = lo_bf16(w.z); f[5] = hi_bf16(w.z); f[6] = lo_bf16(w.w); f[7] = hi_bf16(w.w);
                     draft_best8(f, i0, greedy, invT, 8ull * (uint64_t)b + (uint64_t)k, hp.seed, hp.offset, best, bi);
+                    if (stats) stat_add8(f, sc, sm, ss);
                 }
             }
             better_step<kDppXor1>(best, bi);
             better_step<kDppXor2>(best, bi);
-            if (active && q == 0) hp.part[((int64_t)b * 7 + k - 1) * hp.nparts + t.tn] = {best, bi};
+            if (stats) {
+                stat_merge(sm, ss, dpp_f<kDppXor1>(sm, -INFINITY), dpp_f<kDppXor1>(ss, 0.f), sc);
+                stat_merge(sm, ss, dpp_f<kDppXor2>(sm, -INFINITY), dpp_f<kDppXor2>(ss, 0.f), sc);
+            }
+            if (active && q == 0) {
+                const int64_t pi = ((int64_t)b * 7 + k - 1) * hp.nparts + t.tn;
+                hp.part[pi] = {best, bi};
+                if (stats) hp.spart[pi] = {sm, ss};
+            }
         }
         return;
     }

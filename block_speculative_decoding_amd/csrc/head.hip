@@ -18,9 +18,11 @@
 //                    output (or the fp32 kernel)
 //     sample      -- vocabulary-parallel over rows k = 1..7, one (key, index)
 //                    per row and 8192-entry chunk
-//   pick          -- one wave per row: the best partial is d_k
-// Keys are computed from the stored (rounded) logits, so the proposals are
-// those of the values verification will read.
+//   pick          -- one wave per row: the best partial is d_k; with
+//                    draft_stats requested, the row's statistics partials
+//                    are merged into (m, s) for verification
+// Keys and statistics are computed from the stored (rounded) logits, so the
+// proposals and q's normaliser are those of the values verification reads.
 #include "device_common.h"
 #include "gemm.h"
 #include "head_sample.h"
@@ -40,7 +42,9 @@ struct HeadParams {
     uint64_t seed, offset;
     int nch;              // partials per proposal row
     KeyIdx* part;         // [B][7][nch]
+    RowStat* spart;       // [B][7][nch] statistics partials of sampled rows (when dstats is set)
     int32_t* d;           // [B][7]
+    float* dstats;        // optional [B][7][2]: (m, s) per proposal row
 };
 
 // Eight consecutive stored logits as fp32 (one 16-byte load for bf16, two
@@ -73,7 +77,9 @@ __global__ __launch_bounds__(kThreads) void draft_sample_kernel(HeadParams p) {
     const T* z = static_cast<const T*>(p.logits) + ((int64_t)b * 8 + k) * p.V;
     const int64_t c0 = (int64_t)chunk * kChunk, c1 = min(p.V, c0 + kChunk);
     const uint64_t ctr1 = 8ull * (uint64_t)b + (uint64_t)k;
-    float best = -INFINITY;
+    const bool stats = !greedy && p.dstats != nullptr;
+    const StatScale sc = stat_scale(greedy ? 1.f : Tb);
+    float best = -INFINITY, sm = -INFINITY, ss = 0.f;
     int bi = 0x7FFFFFFF;
     // Every load of the thread is issued before any is used.
     constexpr int kIt = kChunk / (kThreads * 8);
@@ -86,16 +92,30 @@ __global__ __launch_bounds__(kThreads) void draft_sample_kernel(HeadParams p) {
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
         const int64_t i0 = c0 + ((int64_t)it * kThreads + threadIdx.x) * 8;
-        if (i0 < c1) draft_best8(f[it], i0, greedy, invT, ctr1, p.seed, p.offset, best, bi);
+        if (i0 < c1) {
+            draft_best8(f[it], i0, greedy, invT, ctr1, p.seed, p.offset, best, bi);
+            if (stats) stat_add8(f[it], sc, sm, ss);
+        }
     }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) better(best, bi, __shfl_xor(best, o), __shfl_xor(bi, o));
+    for (int o = 32; o > 0; o >>= 1) {
+        better(best, bi, __shfl_xor(best, o), __shfl_xor(bi, o));
+        if (stats) stat_merge(sm, ss, __shfl_xor(sm, o), __shfl_xor(ss, o), sc);
+    }
     __shared__ KeyIdx sw[kThreads / 64];
-    if ((threadIdx.x & 63) == 0) sw[threadIdx.x >> 6] = {best, bi};
+    __shared__ RowStat sst[kThreads / 64];
+    if ((threadIdx.x & 63) == 0) {
+        sw[threadIdx.x >> 6] = {best, bi};
+        sst[threadIdx.x >> 6] = {sm, ss};
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
-        for (int w = 1; w < kThreads / 64; ++w) better(best, bi, sw[w].key, sw[w].idx);
+        for (int w = 1; w < kThreads / 64; ++w) {
+            better(best, bi, sw[w].key, sw[w].idx);
+            if (stats) stat_merge(sm, ss, sst[w].m, sst[w].s, sc);
+        }
         p.part[(int64_t)row * p.nch + chunk] = {best, bi};
+        if (stats) p.spart[(int64_t)row * p.nch + chunk] = {sm, ss};
     }
 }
 
@@ -113,6 +133,29 @@ __global__ __launch_bounds__(kThreads) void draft_pick_kernel(HeadParams p) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) better(best, bi, __shfl_xor(best, o), __shfl_xor(bi, o));
     if (lane == 0) p.d[row] = bi == 0x7FFFFFFF ? -1 : bi;   // no finite key (non-finite logits): -1
+    if (!p.dstats) return;
+    // Statistics: the row's largest partial maximum, then the partial sums
+    // rescaled to it and added in fp64.  Greedy rows need none: (-inf, 0).
+    const float Tb = p.temp[row / 7];
+    float m = -INFINITY;
+    if (Tb > 0.f) {
+        for (int c = lane; c < p.nch; c += 64) m = fmaxf(m, p.spart[(int64_t)row * p.nch + c].m);
+        m = wave_max(m);
+    }
+    double sum = 0.0;
+    if (m != -INFINITY) {
+        const double sc = 1.4426950408889634 / (double)Tb;
+        for (int c = lane; c < p.nch; c += 64) {
+            const RowStat st = p.spart[(int64_t)row * p.nch + c];
+            if (st.m != -INFINITY) sum += (double)st.s * exp2((double)(st.m - m) * sc);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    }
+    if (lane == 0) {
+        p.dstats[2 * row] = m;
+        p.dstats[2 * row + 1] = (float)sum;
+    }
 }
 
 bool fused_path(const dflash_head_args& a) { return a.dtype == DFLASH_BF16 && 8 * a.B >= 256 && a.V % 256 == 0; }
@@ -121,9 +164,11 @@ bool fused_path(const dflash_head_args& a) { return a.dtype == DFLASH_BF16 && 8 
 
 size_t head_workspace_bytes(int B, int64_t V) {
     // The fused path keeps one partial per row and 256-column tile, the
-    // separate pass one per 8192-entry chunk: size for the larger.
+    // separate pass one per 8192-entry chunk: size for the larger; then as
+    // many statistics partials.
     const int64_t n = (V + 255) / 256;
-    return ((size_t)B * 7 * n * sizeof(KeyIdx) + 255) & ~(size_t)255;
+    return (((size_t)B * 7 * n * sizeof(KeyIdx) + 255) & ~(size_t)255) +
+           (((size_t)B * 7 * n * sizeof(RowStat) + 255) & ~(size_t)255);
 }
 
 hipError_t launch_head(const dflash_head_args& a, void* ws, hipStream_t s) {
@@ -142,7 +187,13 @@ hipError_t launch_head(const dflash_head_args& a, void* ws, hipStream_t s) {
     p.logits = a.logits; p.temp = a.temperature; p.B = a.B; p.V = a.V;
     p.seed = a.seed; p.offset = a.offset;
     p.part = static_cast<KeyIdx*>(ws);
+    {
+        const int64_t n = (a.V + 255) / 256;
+        p.spart = reinterpret_cast<RowStat*>(static_cast<char*>(ws) +
+                                             (((size_t)a.B * 7 * n * sizeof(KeyIdx) + 255) & ~(size_t)255));
+    }
     p.d = a.draft_tokens;
+    p.dstats = a.draft_stats;
     const int rows = a.B * 7;
     hipError_t e;
     if (fused_path(a)) {
@@ -151,6 +202,7 @@ hipError_t launch_head(const dflash_head_args& a, void* ws, hipStream_t s) {
         HeadEpilogue ep;
         ep.temp = a.temperature; ep.seed = a.seed; ep.offset = a.offset;
         ep.part = p.part;
+        ep.spart = a.draft_stats ? p.spart : nullptr;
         ep.nparts = (int)(a.V / 256);
         if ((e = launch_gemm_big_head(g, ep, s)) != hipSuccess) return e;
         p.nch = ep.nparts;

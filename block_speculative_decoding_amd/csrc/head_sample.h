@@ -60,13 +60,54 @@ __device__ __forceinline__ void half_wave_best(float& v, int& i) {
     better_step<kDppBcast15, 0xA>(v, i);
 }
 
+// Softmax statistics of a sampled proposal row at its temperature, for
+// verification's q normaliser: (m, s) with m the largest stored logit and
+// s = sum 2^((z - m) * log2(e) / T) = sum e^((z - m) / T).  The scale
+// log2(e) / T is split into hi + lo so that the exponent keeps the double
+// scale's accuracy: x = fma(z - m, hi, (z - m) * lo), z - m exact for bf16.
+struct RowStat { float m, s; };
+struct StatScale { float hi, lo; };
+__device__ __forceinline__ StatScale stat_scale(float T) {
+    const double sc = 1.4426950408889634 / (double)T;
+    StatScale r;
+    r.hi = (float)sc;
+    r.lo = (float)(sc - (double)r.hi);
+    return r;
+}
+__device__ __forceinline__ float stat_exp(float dz, StatScale sc) {
+    return dz == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fmaf(dz, sc.hi, dz * sc.lo));
+}
+// Online update with 8 consecutive stored values.
+__device__ __forceinline__ void stat_add8(const float* f, StatScale sc, float& m, float& s) {
+    float cm = f[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) cm = fmaxf(cm, f[e]);
+    if (cm > m) {
+        s = m == -INFINITY ? 0.f : s * stat_exp(m - cm, sc);
+        m = cm;
+    }
+    if (m == -INFINITY) return;
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += stat_exp(f[e] - m, sc);
+    s += acc;
+}
+__device__ __forceinline__ void stat_merge(float& m, float& s, float m2, float s2, StatScale sc) {
+    const float M = fmaxf(m, m2);
+    if (M == -INFINITY) return;
+    s = (m == -INFINITY ? 0.f : s * stat_exp(m - M, sc)) + (m2 == -INFINITY ? 0.f : s2 * stat_exp(m2 - M, sc));
+    m = M;
+}
+
 // Sampling epilogue of the 256 x 256 projection kernel: for each row
 // 8b + k (k >= 1, row < M) and 256-column tile tn, the tile's best key goes
-// to part[(7b + k - 1) * nparts + tn] (nparts = N / 256).
+// to part[(7b + k - 1) * nparts + tn] (nparts = N / 256), and, when spart is
+// set, a sampled row's statistics over the tile to spart at the same index.
 struct HeadEpilogue {
     const float* temp;     // [B]; <= 0 means greedy
     uint64_t seed, offset;
     KeyIdx* part;
+    RowStat* spart;        // optional
     int nparts;
 };
 

@@ -8,7 +8,9 @@
 // The work is HBM-bound streaming over [B, 8, V] target and [B, 7, V] draft
 // logits.  Four launches, no host round trip:
 //   1. stats     -- vocab-parallel, one pass over every row a sequence needs:
-//                   raw max, sum of exp at 1/T, argmax (lowest index on ties).
+//                   raw max, sum of exp at 1/T, argmax (lowest index on ties);
+//                   the draft rows' (max, sum) may come precomputed from the
+//                   shared head instead (draft_stats), and are then not read.
 //   2. decide    -- one wave per sequence: merge the chunk partials (fp64),
 //                   run the sequential accept scan on Philox uniforms, emit
 //                   accepted proposals (and the greedy correction/bonus).
@@ -43,6 +45,8 @@ struct Params {
     uint64_t seed, offset;
     int32_t* out_tokens; int32_t* out_len; unsigned long long* near_ties;
     int nch1, nch2;
+    int nrows;            // rows per sequence in the statistics grid: 15, or 8 with draft_stats
+    const float* dstats;  // optional [B][7][2] (m, s) of the draft rows
     StatPart* stats; Desc* desc; SamplePart* samp;
 };
 
@@ -159,11 +163,12 @@ __device__ __forceinline__ void stats_chunk(const T* src, int64_t c0, int64_t c1
 // Rows a sequence needs: greedy, target rows 0..7 (argmax); sampled, target
 // rows 0..6 and draft rows 0..6 (the bonus draw at row 7 is a Gumbel-max over
 // unnormalised logits and needs no statistics).
+// With draft_stats the grid covers target rows only (p.nrows = 8).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void stats_kernel(Params p) {
     const int row = blockIdx.x / p.nch1;
     const int chunk = blockIdx.x % p.nch1;
-    const int b = row / kRows, r = row % kRows;
+    const int b = row / p.nrows, r = row % p.nrows;
     const float Tb = p.temp[b];
     const bool greedy = is_greedy(Tb);
     if (greedy ? r >= 8 : r == 7) return;
@@ -196,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Params p) {
         }
         StatPart out;
         out.m = m; out.s = s; out.idx = am; out.pad = 0;
-        p.stats[(int64_t)row * p.nch1 + chunk] = out;
+        p.stats[((int64_t)b * kRows + r) * p.nch1 + chunk] = out;
     }
 }
 
@@ -225,7 +230,8 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(Params p) {
         float m = -INFINITY;
         int am = 0x7FFFFFFF;
         const StatPart* sp = p.stats + ((int64_t)b * kRows + min(r, kRows - 1)) * p.nch1;
-        const bool used = r < nrows && (greedy || r != 7);
+        const bool given = !greedy && r >= 8 && r < kRows && p.dstats != nullptr;   // from draft_stats
+        const bool used = r < nrows && (greedy || r != 7) && !given;
         if (used)
             for (int c = c0; c < p.nch1; c += 16) {
                 if (greedy) combine_arg(m, am, sp[c].m, sp[c].idx);
@@ -246,6 +252,10 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(Params p) {
             }
 #pragma unroll
         for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+        if (given) {
+            m = p.dstats[((int64_t)b * 7 + (r - 8)) * 2];
+            sum = (double)p.dstats[((int64_t)b * 7 + (r - 8)) * 2 + 1];
+        }
         if (c0 == 0) { s_m[r] = m; s_s[r] = sum; s_i[r] = am; }
     }
     __syncthreads();
@@ -499,6 +509,8 @@ hipError_t launch_verify(const dflash_verify_args& a, void* ws, hipStream_t s) {
     p.out_tokens = a.out_tokens; p.out_len = a.out_len; p.near_ties = a.near_ties;
     p.nch1 = (int)((a.V + kStatsChunk - 1) / kStatsChunk);
     p.nch2 = (int)((a.V + kSampleChunk - 1) / kSampleChunk);
+    p.dstats = a.draft_stats;
+    p.nrows = a.draft_stats ? 8 : kRows;
     char* w = static_cast<char*>(ws);
     size_t off = 0;
     p.stats = reinterpret_cast<StatPart*>(w + off);
@@ -508,7 +520,7 @@ hipError_t launch_verify(const dflash_verify_args& a, void* ws, hipStream_t s) {
     off += ((size_t)a.B * sizeof(Desc) + 255) & ~(size_t)255;
     p.samp = reinterpret_cast<SamplePart*>(w + off);
 
-    const dim3 g1(p.nch1 * a.B * kRows), g2(p.nch2 * a.B), gw((a.B + 3) / 4);
+    const dim3 g1(p.nch1 * a.B * p.nrows), g2(p.nch2 * a.B), gw((a.B + 3) / 4);
     if (a.dtype == DFLASH_BF16) {
         stats_kernel<uint16_t><<<g1, kThreads, 0, s>>>(p);
         decide_kernel<uint16_t><<<a.B, kThreads, 0, s>>>(p);

@@ -101,7 +101,7 @@ extern "C" {
 #define DFLASH_MAX_LAYERS 5      /* draft layers */
 #define DFLASH_INTER      5120   /* SwiGLU width (derived from the parameter count) */
 
-#define DFLASH_VERSION 10200     /* 1.2.0 */
+#define DFLASH_VERSION 10300     /* 1.3.0 */
 
 /*
  * dflash_ctx_fuse -- context fusion and K/V injection.
@@ -231,6 +231,10 @@ typedef struct dflash_verify_args {
     int32_t* out_tokens;         /* device [B][8]; emitted tokens, -1 padded */
     int32_t* out_len;            /* device [B]; 1..8 */
     unsigned long long* near_ties; /* device [1]; incremented, never cleared */
+    const float* draft_stats;    /* optional device [B][7][2]: (m, s) of draft row k-1 (proposal k) at the
+                                    sequence's temperature, m = max of the row, s = sum e^((z - m) / T), as
+                                    dflash_draft_head writes them for the same rows and temperatures; the
+                                    row statistics pass then reads no draft row.  NULL = computed here */
 } dflash_verify_args;
 
 /*
@@ -382,6 +386,10 @@ typedef struct dflash_head_args {
     void* logits;             /* device [B][8][V] (dtype), written */
     int32_t* draft_tokens;    /* device [B][7] proposals d_1..d_7, written (-1 if a row has no finite key,
                                  which only non-finite inputs cause; dflash_spec_verify rejects it) */
+    float* draft_stats;       /* optional device [B][7][2], written: for proposal row k = 1..7 of a sampled
+                                 sequence, m = max_i logits[b][k][i] and s = sum_i e^((logits[b][k][i] - m) / T_b)
+                                 of the STORED logits (the normaliser of q_k); (-inf, 0) for greedy
+                                 sequences.  Pass it as dflash_spec_verify's draft_stats.  NULL = not computed */
 } dflash_head_args;
 
 /*

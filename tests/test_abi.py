@@ -55,7 +55,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_struct_sizes_and_version(lib):
     from block_speculative_decoding_amd import _lib
-    assert lib.dflash_version() == 10200
+    assert lib.dflash_version() == 10300
     for kind, st in enumerate(_lib.ARG_STRUCTS):
         assert lib.dflash_args_size(kind) == ctypes.sizeof(st)
     assert lib.dflash_args_size(len(_lib.ARG_STRUCTS)) == 0
@@ -311,15 +311,17 @@ def test_draft_head_validation(lib):
             setattr(a, k, v)
         return a
     rc, n = _ws(lib, "draft_head", args())
-    # one (key, index) partial per 256-column tile of each proposal row
-    assert rc == 0 and n == 64 * 7 * 1024 * 8
+    # one (key, index) partial and one (max, sum) partial per 256-column
+    # tile of each proposal row
+    assert rc == 0 and n == 2 * 64 * 7 * 1024 * 8
     assert _ws(lib, "draft_head", args(V=262144 + 64))[0] == -1      # not a multiple of 128
     assert _ws(lib, "draft_head", args(V=0))[0] == -1
     assert _ws(lib, "draft_head", args(V=(1 << 21) + 128))[0] == -1
     assert _ws(lib, "draft_head", args(B=0))[0] == -1
     assert _ws(lib, "draft_head", args(B=8193))[0] == -1
     assert _ws(lib, "draft_head", args(dtype=3))[0] == -2
-    assert _ws(lib, "draft_head", args(V=128, B=1))[1] == 256        # one chunk, rounded to 256 bytes
+    assert _ws(lib, "draft_head", args(V=128, B=1))[1] == 512        # one chunk of each, rounded to 256 bytes
+    assert _call(lib, "dflash_draft_head", args(draft_stats=FAKE + 8), FAKE, n) == -1   # misaligned
     assert _call(lib, "dflash_draft_head", args(w_head=None), FAKE, n) == -1
     assert _call(lib, "dflash_draft_head", args(logits=FAKE + 4), FAKE, n) == -1
     assert _call(lib, "dflash_draft_head", args(temperature=None), FAKE, n) == -1

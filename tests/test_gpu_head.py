@@ -71,11 +71,41 @@ def _check_proposals(d_gpu, z_st, temp, rows, dtype, seed=SEED, offset=OFFSET):
     return near, close
 
 
-def _run(y_t, w_t, temp, dtype):
+def _run(y_t, w_t, temp, dtype, stats=False):
     import block_speculative_decoding_amd as dfl
-    logits, d = dfl.draft_head(y_t.cuda(), w_t.cuda(), torch.from_numpy(temp).cuda(), seed=SEED, offset=OFFSET)
+    out = dfl.draft_head(y_t.cuda(), w_t.cuda(), torch.from_numpy(temp).cuda(), seed=SEED, offset=OFFSET,
+                         draft_stats=True if stats else None)
     torch.cuda.synchronize()
-    return logits.double().cpu().numpy(), d.cpu().numpy()
+    res = (out[0].double().cpu().numpy(), out[1].cpu().numpy())
+    return res + (out[2].double().cpu().numpy(),) if stats else res
+
+
+def _check_stats(st_gpu, z_gpu, z_ref_st, temp, seqs):
+    """The head's (m, s) of proposal rows 1..7 of sequences seqs: against the
+    oracle's statistics of its own stored logits where the GPU stored the
+    same row (m exact, s to 2e-6 relative), else against the definition on
+    the GPU's stored row (the values verification reads).  Greedy
+    sequences carry (-inf, 0).  Returns the number of rows on the oracle's
+    values."""
+    on_oracle = 0
+    for j, b in enumerate(seqs):
+        T = float(temp[b])
+        if not T > 0:
+            assert np.all(st_gpu[b, :, 0] == -np.inf) and np.all(st_gpu[b, :, 1] == 0), b
+            continue
+        ref = oracle.draft_stats_ref(z_ref_st[j][None], [T])[0]
+        for k in range(1, 8):
+            row_gpu = z_gpu[b, k]
+            if np.array_equal(row_gpu, z_ref_st[j][k]):
+                want = ref[k - 1]
+                on_oracle += 1
+            else:   # the definition, evaluated on the stored row
+                m = np.max(row_gpu)
+                want = (m, np.sum(np.exp((row_gpu - m) / T)))
+            assert st_gpu[b, k - 1, 0] == want[0], (b, k, st_gpu[b, k - 1, 0], want[0])
+            rel = abs(st_gpu[b, k - 1, 1] - want[1]) / want[1]
+            assert rel <= 2e-6, (b, k, rel)
+    return on_oracle
 
 
 @pytest.mark.parametrize("dtype,B,V", [(BF16, 5, 3 * 8192 + 384), (F32, 3, 8192 + 128), (BF16, 1, 128),
@@ -94,12 +124,14 @@ def test_head_logits_and_proposals(dtype, B, V):
     if B >= 3:
         temp[:3] = [0.0, 0.8, 1e-6]              # greedy, sampled, vanishing temperature
     note(f"draft_head {dtype} B={B} V={V} T={temp.tolist()}")
-    z_gpu, d_gpu = _run(y_t, w_t, temp, dtype)
+    z_gpu, d_gpu, st_gpu = _run(y_t, w_t, temp, dtype, stats=True)
     z_ref = oracle.head_logits_ref(y, w)
     e = _logit_err(z_gpu, z_ref, dtype)
     note(f"  logits err/bound {e:.3f}")
     assert e <= 1.0
     _, z_st = _stored(z_ref, dtype)
+    n_or = _check_stats(st_gpu, z_gpu, z_st, temp, list(range(B)))
+    note(f"  draft stats: {n_or} rows on the oracle's stored logits")
     rows = [(b, k) for b in range(B) for k in range(1, 8)]
     near, close = _check_proposals(d_gpu, {b: z_st[b] for b in range(B)}, temp, rows, dtype)
     note(f"  proposals: {len(rows) - near} exact, {near} near-ties (of {close} rows within their key bounds)")
@@ -136,7 +168,7 @@ def test_head_full_vocabulary_batch64():
     y_t, y = _stored(synth.head_input(SEED, B), BF16)
     w_t = torch.from_numpy(synth.head_weight(SEED, V)).to(BF16)
     temp = synth.head_temperatures(SEED, B)
-    z_gpu, d_gpu = _run(y_t, w_t, temp, BF16)
+    z_gpu, d_gpu, st_gpu = _run(y_t, w_t, temp, BF16, stats=True)
     cols = np.sort(np.random.default_rng(SEED).choice(V, 512, replace=False))
     w_cols = w_t[torch.from_numpy(cols)].double().numpy()
     e = _logit_err(z_gpu[:, :, cols], oracle.head_logits_ref(y, w_cols), BF16)
@@ -152,8 +184,43 @@ def test_head_full_vocabulary_batch64():
     note(f"  full rows of sequences {seqs} err/bound {e:.3f}")
     assert e <= 1.0
     z_st = {b: _stored(zr[j], BF16)[1] for j, b in enumerate(seqs)}
+    n_or = _check_stats(st_gpu, z_gpu, [z_st[b] for b in seqs], temp, seqs)
+    note(f"  draft stats of sequences {seqs}: {n_or} rows on the oracle's stored logits")
     rows = [(b, k) for b in seqs for k in range(1, 8)]
     near, close = _check_proposals(d_gpu, z_st, temp, rows, BF16)
     note(f"  T={temp[seqs].tolist()}: {len(rows) - near} exact, {near} near-ties (of {close} within bounds)")
     assert near <= close
     assert np.all((d_gpu >= 0) & (d_gpu < V))
+
+
+def test_head_stats_feed_verification():
+    # The chain head -> verify at B = 64, V = 262144: verification fed the
+    # head's draft statistics reads no draft row for them and must decide as
+    # verification that computes them from the same stored logits (both on
+    # the GPU; each is checked against the oracle in its own tests).  Their
+    # normalisers differ only in summation order (~1e-7 relative), so the
+    # outputs are identical unless an acceptance decision sits within 1e-6
+    # of its uniform (counted by both).
+    import block_speculative_decoding_amd as dfl
+    B, V = 64, 262144
+    note("head -> verify with draft stats, B=64 V=262144")
+    y_t, _ = _stored(synth.head_input(SEED, B), BF16)
+    w_t = torch.from_numpy(synth.head_weight(SEED, V)).to(BF16).cuda()
+    temp = synth.head_temperatures(SEED, B)
+    t_d = torch.from_numpy(temp).cuda()
+    logits, d, st = dfl.draft_head(y_t.cuda(), w_t, t_d, seed=SEED, offset=OFFSET, draft_stats=True)
+    # target rows 0..6 = the draft rows 1..7 plus N(0, 0.3^2): most proposals are accepted
+    g = torch.Generator(device="cuda").manual_seed(SEED)
+    zt_d = torch.empty((B, 8, V), dtype=BF16, device="cuda")
+    zt_d[:, :7] = (logits[:, 1:].float() + 0.3 * torch.randn((B, 7, V), generator=g, device="cuda")).to(BF16)
+    zt_d[:, 7] = logits[:, 7]
+    a = dfl.spec_verify(zt_d, logits[:, 1:], d, t_d, seed=SEED, offset=OFFSET, draft_stats=st)
+    b = dfl.spec_verify(zt_d, logits[:, 1:], d, t_d, seed=SEED, offset=OFFSET)
+    torch.cuda.synchronize()
+    nt = int(a[2].item())
+    assert nt == int(b[2].item())
+    if nt == 0:
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    mean_len = a[1].float().mean().item()
+    note(f"  mean out_len {mean_len:.2f}, near-ties {nt}")
+    assert mean_len > 2.0

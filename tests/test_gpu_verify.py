@@ -191,3 +191,26 @@ def test_verify_single_stream_t1():
         excl += compare_verify(toks.cpu().numpy(), lens.cpu().numpy(), tr)
         note(f"  offset {off}: len {int(lens.cpu()[0])}")
     assert excl <= 1
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_verify_with_draft_stats_input(dtype):
+    """The draft rows' statistics given as an input (as the shared head
+    writes them; here the oracle's, rounded to fp32): verification reads no
+    draft row for them and matches the oracle bit for bit."""
+    import block_speculative_decoding_amd as dfl
+    B, V, seed = 24, 50000, 13
+    note(f"verify with draft stats B={B} V={V} {dtype}")
+    zt, zd = synth.logits(seed, B, V, 3.0, 1.0)
+    temp = np.array([0.0, 0.7, 1.0, 1.7] * (B // 4), dtype=np.float32)
+    zt_d, zd_d = dev(zt, dtype), dev(zd, dtype)
+    zfull = np.concatenate([np.zeros((B, 1, V)), exact(zd_d)], axis=1)
+    st = oracle.draft_stats_ref(zfull, temp)
+    d = synth.sample_drafts(seed, exact(zd_d), temp)
+    toks, lens, nt = dfl.spec_verify(zt_d, zd_d, dev(d, torch.int32), dev(temp, F32), seed=5, offset=17,
+                                     draft_stats=dev(st, F32))
+    torch.cuda.synchronize()
+    tr = oracle.spec_verify_ref(exact(zt_d), exact(zd_d), d, temp, 5, 17)
+    excl = compare_verify(toks.cpu().numpy(), lens.cpu().numpy(), tr)
+    assert excl <= 2
+    assert int(nt.item()) == tr.near_ties

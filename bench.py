@@ -42,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+FP32_VECTOR_PEAK_TFLOPS = 157.3 # MI355X fp32 vector
 B, S_CTX, V, LAYERS = 64, 8192, 262144, 5
 SEED = 2
 ATTN_SRC = os.path.join(ROOT, "block_speculative_decoding_amd", "csrc", "attn.hip")
@@ -314,6 +315,22 @@ def timed(torch, fn, warmup=2, reps=5):
     return e0.elapsed_time(e1) / reps
 
 
+def timed_cold(torch, fn, reps=10):
+    """Average time of fn with the MALL (256 MB) flushed before every rep by
+    writing a 512 MiB buffer; only fn is inside the events."""
+    flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda:0")
+    fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        flush.fill_(reps)
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    del flush
+    return sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
+
+
 def prefill_measurements(torch, dfl, synth):
     """Prefill workload: ctx_fuse of a 32768-token prompt into 5 layer caches
     (slots 0..32767 in order), then one verify-only step over B = 256."""
@@ -354,6 +371,123 @@ def prefill_measurements(torch, dfl, synth):
     return out
 
 
+def config_measurements(torch, dfl, synth):
+    """The smaller configurations, each as its own cycle (eager, 20 reps after
+    warm-up; per-kernel times from the same kind of loop):
+    tiny fp32  -- B = 1, S = 128: ctx_fuse of the 128 context rows (one layer),
+                  block attention over them, verify over V = 4096 (target and
+                  draft N(0, 3^2), independent) at T = 1 and greedy;
+    single     -- B = 1, S = 4096 bf16: ctx_fuse of the 4096 context rows into
+                  5 layers ([4096,12800]x[12800,2560] + K/V of 5 layers), 5 x
+                  block attention over 4096 cached tokens, verify over
+                  V = 262144 at T = 1 (draft = target + N(0, 1));
+    long-context verify -- B = 4, V = 262144, T = 1 (draft = target + N(0, 1)).
+    Launch-bound at these sizes: reported as latency, with the fusion's MFMA
+    fraction where it is a real contraction (M = 4096)."""
+    dev = torch.device("cuda:0")
+    out = {}
+
+    def cycle_of(fuse, attns, ver):
+        def run():
+            fuse()
+            for a in attns:
+                a()
+            ver()
+        return run
+
+    for name, dt, M, L, Vc, sig, T in (("tiny_fp32_cycle_b1_s128", torch.float32, 128, 1, 4096, 3.0, 1.0),
+                                        ("single_stream_cycle_b1_s4096", torch.bfloat16, 4096, LAYERS, V, 4.0, 1.0)):
+        d = lambda x, t=dt: torch.from_numpy(np.ascontiguousarray(x)).to(t).to(dev)
+        seed = SEED + 10 + M
+        hs = [d(h) for h in synth.capture_states(seed, M)]
+        w = {k: d(v) for k, v in synth.fuse_weights(seed, L).items()}
+        table, npages = synth.page_table(seed, [M + 8])
+        kc = [torch.zeros((npages, 8, 2048), dtype=dt, device=dev) for _ in range(L)]
+        vc = [torch.zeros((npages, 8, 2048), dtype=dt, device=dev) for _ in range(L)]
+        slot = np.array([table[0, t // 16] * 16 + t % 16 for t in range(M)], dtype=np.int64)
+        fuse = dfl.prepare_ctx_fuse(hs, w["wc"], w["gc"], w["wkv"], w["gk"],
+                                    torch.arange(M, dtype=torch.int32, device=dev), d(slot, torch.int64), kc, vc)
+        bt = d(table, torch.int32)
+        cl = torch.tensor([M], dtype=torch.int32, device=dev)
+        attns = []
+        for l in range(L):
+            blk = {k: d(v) for k, v in synth.attn_block(seed, 1, layer=l).items()}
+            attns.append(dfl.prepare_block_attn(blk["q"], blk["k_blk"], blk["v_blk"], blk["gq"], blk["gk"],
+                                                kc[l], vc[l], bt, cl))
+        if dt == torch.float32:
+            zt = synth.normal(seed, "zt_tiny", (1, 8, Vc), std=sig)
+            zd = synth.normal(seed, "zd_tiny", (1, 7, Vc), std=sig)
+        else:
+            zt, zd = synth.logits(seed, 1, Vc, sig, 1.0)
+        zt_d, zd_d = d(zt), d(zd)
+        temp = np.array([T], dtype=np.float32)
+        dr = d(synth.sample_drafts(seed, zd_d.float().cpu().numpy(), temp), torch.int32)
+        ver = dfl.prepare_spec_verify(zt_d, zd_d, dr, d(temp, torch.float32), seed=SEED, offset=0)
+        ver_g = dfl.prepare_spec_verify(zt_d, zd_d, dr, torch.zeros(1, device=dev), seed=SEED, offset=0)
+        fuse()
+        torch.cuda.synchronize()
+        c_ms = timed(torch, cycle_of(fuse, attns, ver), warmup=5, reps=20)
+        f_ms = timed(torch, fuse, warmup=5, reps=20)
+        a_ms = timed(torch, attns[0], warmup=5, reps=20)
+        v_ms = timed(torch, ver, warmup=5, reps=20)
+        vg_ms = timed(torch, ver_g, warmup=5, reps=20)
+        flops, _ = fuse_flops_bytes(M) if L == LAYERS else (2 * M * (12800 * 2560 + L * 2048 * 2560), 0)
+        a_bytes = attn_bytes(np.array([M]))
+        ent = {"cycle_ms": round(c_ms, 4), "layers": L, "dtype": "f32" if dt == torch.float32 else "bf16",
+               "ctx_fuse_ms": round(f_ms, 4), "ctx_fuse_rows": M,
+               "ctx_fuse_TFLOP/s": round(flops / (f_ms * 1e-3) / 1e12, 2),
+               "block_attn_ms": round(a_ms, 4), "block_attn_GB/s": round(a_bytes / (a_ms * 1e-3) / 1e9, 1),
+               "verify_ms": round(v_ms, 4), "verify_greedy_ms": round(vg_ms, 4), "V": Vc,
+               "timing": "eager, warm (the working set fits the 256 MB MALL)"}
+        if dt == torch.bfloat16:
+            ent["ctx_fuse_mfma_frac"] = round(flops / (f_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        else:
+            ent["ctx_fuse_fp32_vector_frac"] = round(flops / (f_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4)
+        out[name] = ent
+        del hs, w, kc, vc, fuse, attns, ver, ver_g, zt_d, zd_d
+        torch.cuda.empty_cache()
+
+    # Long-context workload's verify: B = 4, V = 262144, T = 1.
+    Bv = 4
+    zt, zd = synth.logits(SEED + 3, Bv, V, 4.0, 1.0)
+    d = lambda x, t=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(x)).to(t).to(dev)
+    zt_d, zd_d = d(zt), d(zd)
+    temp = np.ones(Bv, dtype=np.float32)
+    dr = d(synth.sample_drafts(SEED + 3, zd_d.float().cpu().numpy(), temp), torch.int32)
+    ver = dfl.prepare_spec_verify(zt_d, zd_d, dr, d(temp, torch.float32), seed=SEED, offset=0)
+    v_ms = timed(torch, ver, warmup=5, reps=20)
+    vb = verify_bytes(temp)
+    out["long_context_verify_b4"] = {"ms": round(v_ms, 4), "GB/s": round(vb / (v_ms * 1e-3) / 1e9, 1),
+                                     "hbm_frac": round(vb / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                     "algorithmic_bytes": vb,
+                                     "timing": "eager, warm (29 MB: MALL-resident, latency-bound)"}
+    return out
+
+
+def measured_peaks(torch):
+    """Practical ceilings of the part measured in the same run (warm clocks,
+    inputs in HBM): a device copy of 2 GiB (read + write bytes), a read-only
+    reduction over 2 GiB (torch's sum), and a bf16 matmul 8192^3 through
+    torch (hipBLASLt) with N(0, 1) operands.  Context for the roofline
+    fractions, which stay against the datasheet peaks."""
+    dev = torch.device("cuda:0")
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.bfloat16, device=dev).normal_()
+    y = torch.empty_like(x)
+    c_ms = timed(torch, lambda: y.copy_(x), warmup=3, reps=10)
+    r_ms = timed(torch, lambda: x.view(torch.int32).sum(), warmup=3, reps=10)
+    del y
+    a = torch.randn((8192, 8192), device=dev, dtype=torch.float32).to(torch.bfloat16)
+    b = torch.randn((8192, 8192), device=dev, dtype=torch.float32).to(torch.bfloat16)
+    m_ms = timed(torch, lambda: torch.matmul(a, b), warmup=3, reps=10)
+    del x, a, b
+    torch.cuda.empty_cache()
+    return {"copy_GB/s": round(4 * n / (c_ms * 1e-3) / 1e9, 1),
+            "read_GB/s": round(2 * n / (r_ms * 1e-3) / 1e9, 1),
+            "matmul_bf16_TFLOP/s": round(2 * 8192 ** 3 / (m_ms * 1e-3) / 1e12, 1),
+            "how": "torch copy_ of 2 GiB (read+write), torch sum over 2 GiB (read), torch.matmul bf16 8192^3"}
+
+
 def long_context_measurement(torch, dfl, synth):
     """One layer's block attention over 4 sequences of 131072 cached tokens
     (shuffled 16-token pages, 2.15 GB of K and V): split-K over each sequence,
@@ -389,10 +523,15 @@ def window_measurement(torch, dfl, wl):
     att = dfl.prepare_block_attn(d(blk["q"]), d(blk["k_blk"]), d(blk["v_blk"]), d(blk["gq"]), d(blk["gk"]),
                                  wl.kc[0], wl.vc[0], wl.block_table, wl.ctx_len, window=W)
     ms = timed(torch, att, warmup=3, reps=20)
+    cold = timed_cold(torch, att)
     nbytes = attn_bytes(np.minimum(wl.lens, W))
     return {"window_attn_b64_w1024": {"ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                                       "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                      "algorithmic_bytes": nbytes}}
+                                      "cold_ms": round(cold, 4),
+                                      "cold_hbm_frac": round(nbytes / (cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                      "algorithmic_bytes": nbytes,
+                                      "timing": "ms: warm (repeated; the 279 MB working set is about the "
+                                                "MALL's size); cold_ms: MALL flushed before each launch"}}
 
 
 def draft_measurement(torch, dfl, synth, wl):
@@ -675,6 +814,9 @@ def main():
                      "traffic": None if traffic is None else round(traffic / (a_ms * 1e-3) / 1e9, 1),
                      "algorithmic_bytes_per_launch": a_bytes, "avg_launch_ms": round(a_ms, 4)},
         "kernels": {
+            "timing": ("cycle kernels: per-launch events inside the eager timed steps; every launch follows "
+                       "at least 369 MB of other traffic and reads 131 MB or more (attention 2.16 GB), so "
+                       "none finds its inputs in the 256 MB MALL (cold)"),
             "block_attn": {"ms": round(a_ms, 4), "GB/s": round(a_gbs, 1), "hbm_frac": round(a_gbs / HBM_PEAK_GBS, 4)},
             "spec_verify": {"ms": round(v_ms, 4), "GB/s": round(v_bytes / (v_ms * 1e-3) / 1e9, 1),
                             "hbm_frac": round(v_bytes / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -701,6 +843,10 @@ def main():
         res["kernels"].update(ragged_measurement(torch, dfl, synth))
         log("[bench] shared LM head and draft proposals: B=64, V=262144")
         res["kernels"].update(head_measurement(torch, dfl, synth))
+        log("[bench] tiny fp32 and single-stream cycles, long-context verify")
+        res["kernels"].update(config_measurements(torch, dfl, synth))
+        log("[bench] measured copy / read / matmul ceilings")
+        res["measured_peaks"] = measured_peaks(torch)
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(wl)

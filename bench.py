@@ -464,28 +464,44 @@ def config_measurements(torch, dfl, synth):
     return out
 
 
-def measured_peaks(torch):
-    """Practical ceilings of the part measured in the same run (warm clocks,
-    inputs in HBM): a device copy of 2 GiB (read + write bytes), a read-only
-    reduction over 2 GiB (torch's sum), and a bf16 matmul 8192^3 through
-    torch (hipBLASLt) with N(0, 1) operands.  Context for the roofline
-    fractions, which stay against the datasheet peaks."""
+def measured_peaks(torch, dfl):
+    """Practical ceilings of the part measured in the same run with the
+    library's calibration kernels (dflash_calib_*): a streaming read of
+    4 GiB with 16-byte loads, a 2 GiB copy (read + write bytes), and a
+    register-only bf16 MFMA loop; for reference also torch's bf16 matmul
+    8192^3 (hipBLASLt, N(0, 1) operands).  The roofline fractions stay
+    against the datasheet peaks; these say how much of them the part
+    delivers to any kernel."""
     dev = torch.device("cuda:0")
-    n = 1 << 30
-    x = torch.empty(n, dtype=torch.bfloat16, device=dev).normal_()
-    y = torch.empty_like(x)
-    c_ms = timed(torch, lambda: y.copy_(x), warmup=3, reps=10)
-    r_ms = timed(torch, lambda: x.view(torch.int32).sum(), warmup=3, reps=10)
-    del y
+    sink = dfl.calib_sink(dev)
+    x = torch.empty(1 << 32, dtype=torch.uint8, device=dev).random_()
+    grids = (1024, 2048, 4096, 8192, 16384)
+    r_all = {gd: timed(torch, lambda: dfl.calib_stream(x, sink, grid=gd), warmup=2, reps=5) for gd in grids}
+    r_grid = min(r_all, key=r_all.get)
+    r_ms = r_all[r_grid]
+    src = x[: 1 << 31]
+    dst = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    c_ms = timed(torch, lambda: dfl.calib_stream(src, sink, dst=dst, grid=r_grid), warmup=3, reps=10)
+    del x, src, dst
+    iters = 20000
+    flops = dfl.calib_mfma(iters, sink)
+    f_ms = timed(torch, lambda: dfl.calib_mfma(iters, sink), warmup=2, reps=5)
     a = torch.randn((8192, 8192), device=dev, dtype=torch.float32).to(torch.bfloat16)
     b = torch.randn((8192, 8192), device=dev, dtype=torch.float32).to(torch.bfloat16)
     m_ms = timed(torch, lambda: torch.matmul(a, b), warmup=3, reps=10)
-    del x, a, b
+    del a, b
     torch.cuda.empty_cache()
-    return {"copy_GB/s": round(4 * n / (c_ms * 1e-3) / 1e9, 1),
-            "read_GB/s": round(2 * n / (r_ms * 1e-3) / 1e9, 1),
-            "matmul_bf16_TFLOP/s": round(2 * 8192 ** 3 / (m_ms * 1e-3) / 1e12, 1),
-            "how": "torch copy_ of 2 GiB (read+write), torch sum over 2 GiB (read), torch.matmul bf16 8192^3"}
+    read = (1 << 32) / (r_ms * 1e-3) / 1e9
+    mfma = flops / (f_ms * 1e-3) / 1e12
+    return {"read_GB/s": round(read, 1), "read_frac_of_datasheet": round(read / HBM_PEAK_GBS, 4),
+            "read_grid_sweep_GB/s": {str(gd): round((1 << 32) / (ms * 1e-3) / 1e9, 1) for gd, ms in r_all.items()},
+            "copy_GB/s": round(2 * (1 << 31) / (c_ms * 1e-3) / 1e9, 1),
+            "mfma_loop_TFLOP/s": round(mfma, 1), "mfma_loop_frac_of_datasheet": round(mfma / MFMA_BF16_PEAK_TFLOPS, 4),
+            "torch_matmul_bf16_TFLOP/s": round(2 * 8192 ** 3 / (m_ms * 1e-3) / 1e12, 1),
+            "how": ("dflash_calib_stream over 4 GiB (read; best of a grid sweep) and 2 GiB (copy, read+write "
+                    "bytes); dflash_calib_mfma "
+                    f"({iters} rounds of 8 bf16 32x32x16 MFMAs per wave, 2 waves per SIMD); torch.matmul bf16 "
+                    "8192^3")}
 
 
 def long_context_measurement(torch, dfl, synth):
@@ -846,7 +862,7 @@ def main():
         log("[bench] tiny fp32 and single-stream cycles, long-context verify")
         res["kernels"].update(config_measurements(torch, dfl, synth))
         log("[bench] measured copy / read / matmul ceilings")
-        res["measured_peaks"] = measured_peaks(torch)
+        res["measured_peaks"] = measured_peaks(torch, dfl)
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(wl)

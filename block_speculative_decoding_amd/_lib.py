@@ -99,7 +99,8 @@ EXPORTS = ["dflash_version", "dflash_last_error", "dflash_args_size",
            "dflash_ctx_fuse", "dflash_block_attn", "dflash_spec_verify",
            "dflash_spec_verify_noalloc", "dflash_verify_scratch_bytes",
            "dflash_draft_embed", "dflash_draft_qkv", "dflash_draft_mlp", "dflash_ring_append",
-           "dflash_draft_head", "dflash_draft_paths"]
+           "dflash_draft_head", "dflash_draft_paths",
+           "dflash_calib_sink_bytes", "dflash_calib_stream", "dflash_calib_mfma"]
 
 _lib = None
 
@@ -133,6 +134,12 @@ def load():
     lib.dflash_spec_verify_noalloc.argtypes = [ctypes.POINTER(VerifyArgs), _P]
     lib.dflash_verify_scratch_bytes.restype = ctypes.c_int
     lib.dflash_verify_scratch_bytes.argtypes = [ctypes.POINTER(ctypes.c_size_t)]
+    lib.dflash_calib_sink_bytes.restype = ctypes.c_int
+    lib.dflash_calib_sink_bytes.argtypes = [ctypes.POINTER(ctypes.c_size_t)]
+    lib.dflash_calib_stream.restype = ctypes.c_int
+    lib.dflash_calib_stream.argtypes = [_P, _P, ctypes.c_size_t, ctypes.c_int, _P, _P]
+    lib.dflash_calib_mfma.restype = ctypes.c_int
+    lib.dflash_calib_mfma.argtypes = [ctypes.c_int, _P, ctypes.POINTER(ctypes.c_double), _P]
     lib.dflash_draft_embed.restype = ctypes.c_int
     lib.dflash_draft_embed.argtypes = [ctypes.POINTER(EmbedArgs), _P]
     lib.dflash_ring_append.restype = ctypes.c_int
@@ -722,3 +729,25 @@ def draft_paths(*args, stream=None, **kw):
     prep = prepare_draft_paths(*args, **kw)
     prep(stream)
     return prep.outputs
+
+
+# ---------------------------------------------------------------- calibration
+def calib_sink(device="cuda"):
+    n = ctypes.c_size_t()
+    _check(load().dflash_calib_sink_bytes(ctypes.byref(n)))
+    return torch.empty(n.value, dtype=torch.uint8, device=device)
+
+
+def calib_stream(src, sink, dst=None, grid=0, stream=None):
+    """Read (dst None) or copy (dst given) every byte of src once over `grid`
+    workgroups (0: the default)."""
+    nbytes = src.numel() * src.element_size()
+    _check(load().dflash_calib_stream(_ptr(src), _ptr(dst), nbytes, int(grid), _ptr(sink), _stream(stream)))
+    return nbytes
+
+
+def calib_mfma(iters, sink, stream=None):
+    """Register-only bf16 MFMA loop; returns the launch's FLOPs."""
+    f = ctypes.c_double()
+    _check(load().dflash_calib_mfma(int(iters), _ptr(sink), ctypes.byref(f), _stream(stream)))
+    return f.value

@@ -21,7 +21,7 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I" + os.path.join(ROOT, "include")]
 
-SOURCES = ["api.cpp", "verify.hip", "attn.hip", "gemm.hip", "fuse.hip", "draft.hip", "ring.hip", "head.hip", "paths.hip"]
+SOURCES = ["api.cpp", "verify.hip", "attn.hip", "gemm.hip", "fuse.hip", "draft.hip", "ring.hip", "head.hip", "paths.hip", "calib.hip"]
 
 
 def _compile(src):

@@ -441,4 +441,31 @@ int dflash_draft_paths(const dflash_paths_args* a, void* ws, size_t ws_bytes, vo
     return launched(fn, dflash::launch_paths(*a, ws, static_cast<hipStream_t>(stream)));
 }
 
+// ---------------------------------------------------------------- calibration
+int dflash_calib_sink_bytes(size_t* bytes) {
+    if (!bytes) return fail(DFLASH_EINVAL, "dflash_calib_sink_bytes: null bytes");
+    const size_t a = (size_t)dflash::calib_stream_max_grid() * 16, b = (size_t)dflash::calib_mfma_grid() * 256 * 4;
+    *bytes = a > b ? a : b;
+    return ok();
+}
+
+int dflash_calib_stream(const void* src, void* dst, size_t bytes, int grid, void* sink, void* stream) {
+    const char* fn = "dflash_calib_stream";
+    REQUIRE_PTR(src);
+    REQUIRE_PTR(sink);
+    if (dst && !aligned16(dst)) return fail(DFLASH_EINVAL, "%s: dst is not 16-byte aligned", fn);
+    if (bytes == 0 || bytes % 16 != 0) return fail(DFLASH_EINVAL, "%s: bytes must be a positive multiple of 16", fn);
+    if (grid < 0 || grid > dflash::calib_stream_max_grid())
+        return fail(DFLASH_EINVAL, "%s: grid %d outside [0, %d]", fn, grid, dflash::calib_stream_max_grid());
+    return launched(fn, dflash::launch_calib_stream(src, dst, bytes, grid, sink, static_cast<hipStream_t>(stream)));
+}
+
+int dflash_calib_mfma(int iters, void* sink, double* flops, void* stream) {
+    const char* fn = "dflash_calib_mfma";
+    REQUIRE_PTR(sink);
+    if (iters < 1 || iters > (1 << 24)) return fail(DFLASH_EINVAL, "%s: iters %d outside [1, 2^24]", fn, iters);
+    if (flops) *flops = (double)dflash::calib_mfma_grid() * 4 * iters * 8 * (2.0 * 32 * 32 * 16);
+    return launched(fn, dflash::launch_calib_mfma(iters, sink, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -61,4 +61,10 @@ hipError_t launch_head(const dflash_head_args& a, void* ws, hipStream_t s);
 size_t paths_workspace_bytes(int B, int64_t V);
 hipError_t launch_paths(const dflash_paths_args& a, void* ws, hipStream_t s);
 
+// ---- calibration ----
+int calib_stream_max_grid();
+int calib_mfma_grid();
+hipError_t launch_calib_stream(const void* src, void* dst, size_t bytes, int grid, void* sink, hipStream_t s);
+hipError_t launch_calib_mfma(int iters, void* sink, hipStream_t s);
+
 }  // namespace dflash

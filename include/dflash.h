@@ -503,6 +503,25 @@ int dflash_draft_head(const dflash_head_args* args, void* workspace,
 int dflash_draft_paths(const dflash_paths_args* args, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* Calibration: the practical ceilings of the part the hot path runs on, for
+ * reading the roofline fractions against measured rather than datasheet
+ * peaks.  Not part of the draft-verify cycle.
+ *   dflash_calib_stream: reads `bytes` (a positive multiple of 16) of device
+ *     memory at src once with 16-byte loads, eight in flight per thread, each
+ *     workgroup of 256 threads reading 32 KiB contiguous runs, over `grid`
+ *     workgroups (0 = 2048; at most 65536); with dst != NULL also stores
+ *     every 16 bytes to dst (a copy).  sink receives one 16-byte xor per
+ *     workgroup.
+ *   dflash_calib_mfma: bf16 32x32x16 matrix instructions on register
+ *     operands only, `iters` rounds of eight per wave, two waves per SIMD on
+ *     256 CUs; *flops (if not NULL) receives the FLOPs of the launch.  sink
+ *     receives one float per thread.
+ * sink must hold dflash_calib_sink_bytes() bytes.  Time the calls with
+ * events on the stream. */
+int dflash_calib_sink_bytes(size_t* bytes);
+int dflash_calib_stream(const void* src, void* dst, size_t bytes, int grid, void* sink, void* stream);
+int dflash_calib_mfma(int iters, void* sink, double* flops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -364,3 +364,16 @@ def test_draft_mlp_conv_validation(lib):
     assert _call(lib, "dflash_draft_mlp", _mlp_args(conv_k=3, w_conv=FAKE), FAKE, m) == -1   # b_conv missing
     assert b"b_conv" in lib.dflash_last_error()
     assert _call(lib, "dflash_draft_mlp", _mlp_args(conv_k=3, b_conv=FAKE, w_conv=FAKE + 8), FAKE, m) == -1
+
+
+def test_calibration_validation(lib):
+    n = ctypes.c_size_t()
+    assert lib.dflash_calib_sink_bytes(ctypes.byref(n)) == 0 and n.value >= 65536 * 16
+    assert lib.dflash_calib_stream(None, None, 1024, 0, FAKE, None) == -1
+    assert lib.dflash_calib_stream(FAKE, None, 1000, 0, FAKE, None) == -1          # not a multiple of 16
+    assert lib.dflash_calib_stream(FAKE, FAKE + 8, 1024, 0, FAKE, None) == -1      # misaligned copy target
+    assert lib.dflash_calib_stream(FAKE, None, 1024, 0, None, None) == -1
+    assert lib.dflash_calib_stream(FAKE, None, 1024, 65537, FAKE, None) == -1
+    f = ctypes.c_double()
+    assert lib.dflash_calib_mfma(0, FAKE, ctypes.byref(f), None) == -1
+    assert lib.dflash_calib_mfma(5, None, ctypes.byref(f), None) == -1

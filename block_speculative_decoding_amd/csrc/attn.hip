@@ -463,47 +463,121 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnParams p) {
     float m = -INFINITY, l = 0.f, o[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[e] = 0.f;
-    const int ntok = sr.S - sr.t0 + 8;
-    for (int i = 0; i < ntok; ++i) {
-        const bool ctx = i < sr.S - sr.t0;
-        float kx[16], vx[16];
-        if (ctx) {
-            const int t = sr.t0 + i;
-            const int ph = p.bt[(int64_t)b * p.max_pages + (t >> 4)];
-            const bool okp = ph >= 0 && (int64_t)ph < p.num_pages;
-            const int tt = t & 15;
-            const float* kp = kc + ((int64_t)(okp ? ph : 0) * 8 + g) * 2048;
-            const float* vp = vc + ((int64_t)(okp ? ph : 0) * 8 + g) * 2048;
+
+    // Online-softmax update with up to four tokens (kx / vx rows; sc scaled
+    // scores, -inf for an unused slot).
+    auto step4 = [&](float (*kx)[16], float (*vx)[16], const bool* use) {
+        float sc[4];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int d = e < 8 ? 8 * part + e : 64 + 8 * part + (e - 8);
-                const int ko = 256 * ((d & 63) >> 3) + 8 * (tt + 16 * (d >> 6)) + (d & 7);
-                const int vo = 512 * (d >> 5) + 256 * ((tt >> 2) & 1) + 8 * (d & 31) + (((tt >> 3) << 2) | (tt & 3));
-                kx[e] = okp ? kp[ko] : 0.f;
-                vx[e] = okp ? vp[vo] : 0.f;
-            }
-        } else {
-            const int jb = i - (sr.S - sr.t0);
+        for (int u = 0; u < 4; ++u) {
+            float dot = 0.f;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int d = e < 8 ? 8 * part + e : 64 + 8 * part + (e - 8);
-                kx[e] = kbs[jb][d];
-                vx[e] = vb[jb * 128 + d];
+            for (int e = 0; e < 16; ++e) dot += q[e] * kx[u][e];
+            dot += __shfl_xor(dot, 1);
+            dot += __shfl_xor(dot, 2);
+            dot += __shfl_xor(dot, 4);
+            sc[u] = use[u] ? dot * sl2 : -INFINITY;
+        }
+        float mn = m;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mn = fmaxf(mn, sc[u]);
+        if (mn == -INFINITY) return;
+        const float a = exp2f(m - mn);
+        l *= a;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[e] *= a;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float pw = exp2f(sc[u] - mn);
+            l += pw;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[e] = fmaf(pw, vx[u][e], o[e]);
+        }
+        m = mn;
+    };
+
+    // Context, one page at a time: the page's K and V blocks of head g (two
+    // contiguous 8 KiB runs) are staged in LDS by all threads with 16-byte
+    // loads, the next page's loads in registers meanwhile.  Tokens outside
+    // [t0, S) of a page take no part; missing pages read as zeros.
+    __shared__ __align__(16) float ks[2048], vt[16][132];   // K in the page layout, V as [token][dim]
+    const int pg0 = sr.t0 >> 4, pg1 = (sr.S + 15) >> 4;
+    float4 rk[2], rv[2];
+    auto fetch = [&](int pg) {
+        const int ph = p.bt[(int64_t)b * p.max_pages + pg];
+        const bool okp = ph >= 0 && (int64_t)ph < p.num_pages;
+        const float4* kp = reinterpret_cast<const float4*>(kc + ((int64_t)(okp ? ph : 0) * 8 + g) * 2048);
+        const float4* vp = reinterpret_cast<const float4*>(vc + ((int64_t)(okp ? ph : 0) * 8 + g) * 2048);
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            rk[i] = okp ? kp[i * kThreads + tid] : z;
+            rv[i] = okp ? vp[i * kThreads + tid] : z;
+        }
+    };
+    if (pg0 < pg1) fetch(pg0);
+    for (int pg = pg0; pg < pg1; ++pg) {
+        __syncthreads();   // the previous page's reads of ks / vs are done
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            reinterpret_cast<float4*>(ks)[i * kThreads + tid] = rk[i];
+            // element f of the V block: dim 32 (f >> 9) + ((f >> 3) & 31), token
+            // from bit 8 and the low three bits (the layout's slot order)
+            const float v4[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int f = (i * kThreads + tid) * 4 + c;
+                const int jj = f & 7;
+                const int d = 32 * (f >> 9) + ((f >> 3) & 31);
+                const int tt = ((jj >> 2) << 3) | (((f >> 8) & 1) << 2) | (jj & 3);
+                vt[tt][d] = v4[c];
             }
         }
-        float dot = 0.f;
+        __syncthreads();
+        if (pg + 1 < pg1) fetch(pg + 1);
+        const int lo = max(sr.t0 - 16 * pg, 0), hi = min(sr.S - 16 * pg, 16);
+        for (int t0 = lo; t0 < hi; t0 += 4) {
+            float kx[4][16], vx[4][16];
+            bool use[4];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) dot += q[e] * kx[e];
-        dot += __shfl_xor(dot, 1);
-        dot += __shfl_xor(dot, 2);
-        dot += __shfl_xor(dot, 4);
-        const float sc = dot * sl2;
-        const float mn = fmaxf(m, sc);
-        const float a = exp2f(m - mn), pw = exp2f(sc - mn);
-        l = l * a + pw;
+            for (int u = 0; u < 4; ++u) {
+                const int tt = min(t0 + u, 15);
+                use[u] = t0 + u < hi;   // slots outside [t0, S) may hold anything (even NaN): zeroed
+                // dims 8 part .. +7 and 64 + 8 part .. +7: contiguous in both
+                const float4* k0 = reinterpret_cast<const float4*>(ks + 256 * part + 8 * tt);
+                const float4* k1 = reinterpret_cast<const float4*>(ks + 256 * part + 8 * (tt + 16));
+                const float4* v0 = reinterpret_cast<const float4*>(&vt[tt][8 * part]);
+                const float4* v1 = reinterpret_cast<const float4*>(&vt[tt][64 + 8 * part]);
+                const float4 kk[4] = {k0[0], k0[1], k1[0], k1[1]}, vv[4] = {v0[0], v0[1], v1[0], v1[1]};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[e] = o[e] * a + pw * vx[e];
-        m = mn;
+                for (int c = 0; c < 4; ++c) {
+                    const float kf[4] = {kk[c].x, kk[c].y, kk[c].z, kk[c].w};
+                    const float vf[4] = {vv[c].x, vv[c].y, vv[c].z, vv[c].w};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        kx[u][4 * c + r] = use[u] ? kf[r] : 0.f;
+                        vx[u][4 * c + r] = use[u] ? vf[r] : 0.f;
+                    }
+                }
+            }
+            step4(kx, vx, use);
+        }
+    }
+    // The block's own 8 keys and values.
+    for (int j0 = 0; j0 < 8; j0 += 4) {
+        float kx[4][16], vx[4][16];
+        bool use[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            use[u] = true;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int d = e < 8 ? 8 * part + e : 64 + 8 * part + (e - 8);
+                kx[u][e] = kbs[j0 + u][d];
+                vx[u][e] = vb[(j0 + u) * 128 + d];
+            }
+        }
+        step4(kx, vx, use);
     }
     const float inv = 1.0f / l;
     float* orow = static_cast<float*>(p.out) + ((((int64_t)b * 32 + 4 * g + hh) * 8 + j) * 128);

@@ -599,8 +599,9 @@ FusePlan fuse_plan(const dflash_fuse_args& a) {
     const int N2 = a.num_layers * 2048;
     const bool bf = a.dtype == DFLASH_BF16;
     pl.big = bf && M >= kBigM;
-    pl.ks1 = bf && !pl.big ? gemm_split(M, DFLASH_D, DFLASH_NCAPTURE * DFLASH_D) : 1;
-    pl.ks2 = bf && !pl.big ? gemm_split(M, N2, DFLASH_D) : 1;
+    pl.ks1 = pl.big ? 1 : bf ? gemm_split(M, DFLASH_D, DFLASH_NCAPTURE * DFLASH_D)
+                             : gemm_split_f32(M, DFLASH_D, DFLASH_NCAPTURE * DFLASH_D);
+    pl.ks2 = pl.big ? 1 : bf ? gemm_split(M, N2, DFLASH_D) : gemm_split_f32(M, N2, DFLASH_D);
     const size_t es = bf ? 2 : 4;
     pl.off_part1 = 0;
     pl.off_ht = align256((size_t)pl.ks1 * M * DFLASH_D * 4);

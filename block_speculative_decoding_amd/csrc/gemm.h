@@ -92,12 +92,13 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
 // CU on 256 CUs), at least 4 k-tiles of 64 per split, at most kGemmMaxKs, and
 // every split owns at least one k-tile.
 int gemm_split(int M, int N, int K);
-// Sets g.ks and g.kt_per_split for this dtype (the fp32 kernel ignores them
-// and needs ks = 1).
+// The same for the fp32 kernel's 64x64 tiles (at least 2 k-tiles per split).
+int gemm_split_f32(int M, int N, int K);
+// Sets g.ks and g.kt_per_split (splits own kt_per_split k-tiles of 64).
 void gemm_set_split(GemmParams& g, int dtype, int ks);
 // bf16: 128x128 tiles, N % 128 == 0, K and seg_w multiples of 64, 16-byte
 // aligned rows, a_stride < 2^23; fp32: 64x64 tiles, N % 64 == 0, K and
-// seg_w multiples of 16.
+// seg_w multiples of 16, a_stride a multiple of 4.
 hipError_t launch_gemm(const GemmParams& g, int dtype, hipStream_t s);
 
 }  // namespace dflash

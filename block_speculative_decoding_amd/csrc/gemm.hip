@@ -189,37 +189,54 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
 }
 
 // Plain fp32 GEMM for the fp32 path: 64x64 tile, 4x4 outputs per thread.
+// fp32 (small fp32 workloads): 64x64 tiles, 256 threads of 4x4 outputs,
+// 16-deep k steps staged in LDS from 16-byte loads, the next step's loads in
+// registers while the current one multiplies; split-K over blockIdx.z in
+// units of 64 k (kt_per_split), each split to its own partial.
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
-    const int tm = blockIdx.x, tn = blockIdx.y;
+    const int tm = blockIdx.x, tn = blockIdx.y, sp = blockIdx.z;
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-    __shared__ float as[16][65], bs[16][65];
+    __shared__ __align__(16) float as[16][68], bs[16][68];
     float acc[4][4] = {};
     const float* bmat = static_cast<const float*>(p.b);
-    for (int k0 = 0; k0 < p.K; k0 += 16) {
-        const int seg = k0 / p.seg_w;
+    const int kb = sp * p.kt_per_split * BKD;
+    const int ke = min(p.K, kb + p.kt_per_split * BKD);
+    // loader: row lr of the tile, k quad lq of the step
+    const int lr = tid >> 2, lq = (tid & 3) * 4;
+    const int gm = tm * 64 + lr;
+    float4 ra = make_float4(0.f, 0.f, 0.f, 0.f), rb = ra;
+    auto load = [&](int k0) {
+        const int seg = k0 / p.seg_w;            // a 16-wide step never crosses a segment
         const int kc = k0 - seg * p.seg_w;
         const float* a = static_cast<const float*>(p.aseg[seg]);
-        for (int i = tid; i < 64 * 16; i += kThreads) {
-            const int r = i >> 4, kk = i & 15;
-            const int gm = tm * 64 + r;
-            as[kk][r] = gm < p.M ? a[(int64_t)gm * p.a_stride + kc + kk] : 0.f;
-            bs[kk][r] = bmat[(int64_t)(tn * 64 + r) * p.K + k0 + kk];
-        }
+        ra = gm < p.M ? *reinterpret_cast<const float4*>(a + (int64_t)gm * p.a_stride + kc + lq)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+        rb = *reinterpret_cast<const float4*>(bmat + (int64_t)(tn * 64 + lr) * p.K + k0 + lq);
+    };
+    if (kb < ke) load(kb);
+    for (int k0 = kb; k0 < ke; k0 += 16) {
+        __syncthreads();   // the previous step's reads of as / bs are done
+        as[lq][lr] = ra.x; as[lq + 1][lr] = ra.y; as[lq + 2][lr] = ra.z; as[lq + 3][lr] = ra.w;
+        bs[lq][lr] = rb.x; bs[lq + 1][lr] = rb.y; bs[lq + 2][lr] = rb.z; bs[lq + 3][lr] = rb.w;
         __syncthreads();
+        if (k0 + 16 < ke) load(k0 + 16);
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk)
+        for (int kk = 0; kk < 16; ++kk) {
+            const float4 av = *reinterpret_cast<const float4*>(&as[kk][ty * 4]);
+            const float4 bv = *reinterpret_cast<const float4*>(&bs[kk][tx * 4]);
+            const float a4[4] = {av.x, av.y, av.z, av.w}, b4[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] += as[kk][ty * 4 + i] * bs[kk][tx * 4 + j];
-        __syncthreads();
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a4[i], b4[j], acc[i][j]);
+        }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int gm = tm * 64 + ty * 4 + i;
-        if (gm >= p.M) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p.part[(int64_t)gm * p.N + tn * 64 + tx * 4 + j] = acc[i][j];
+        const int m = tm * 64 + ty * 4 + i;
+        if (m >= p.M) continue;
+        *reinterpret_cast<float4*>(p.part + ((int64_t)sp * p.M + m) * p.N + tn * 64 + tx * 4) =
+            make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
     }
 }
 
@@ -237,8 +254,19 @@ int gemm_split(int M, int N, int K) {
     return (nk + per - 1) / per;
 }
 
+int gemm_split_f32(int M, int N, int K) {
+    const int tiles = ((M + 63) / 64) * (N / 64);
+    const int nk = K / BKD;
+    int ks = 512 / tiles;
+    if (ks > nk / 2) ks = nk / 2;         // keep >= 2 k-tiles (128 k) per split
+    if (ks > kGemmMaxKs) ks = kGemmMaxKs;
+    if (ks < 1) ks = 1;
+    const int per = (nk + ks - 1) / ks;
+    return (nk + per - 1) / per;
+}
+
 void gemm_set_split(GemmParams& g, int dtype, int ks) {
-    if (dtype != DFLASH_BF16) ks = 1;
+    (void)dtype;
     g.ks = ks;
     g.kt_per_split = (g.K / BKD + ks - 1) / ks;
 }
@@ -249,7 +277,7 @@ hipError_t launch_gemm(const GemmParams& g, int dtype, hipStream_t s) {
         const int grid = (tiles + kGemmXcds - 1) / kGemmXcds * kGemmXcds;
         gemm_bf16_kernel<<<grid, kThreads, 0, s>>>(g);
     } else {
-        gemm_f32_kernel<<<dim3((g.M + 63) / 64, g.N / 64), kThreads, 0, s>>>(g);
+        gemm_f32_kernel<<<dim3((g.M + 63) / 64, g.N / 64, g.ks), kThreads, 0, s>>>(g);
     }
     return hipGetLastError();
 }

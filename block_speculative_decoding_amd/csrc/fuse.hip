@@ -591,7 +591,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Large fused row counts use the 256x256 kernel (no split-K, fused K/V
 // epilogue); small ones the 128x128 split-K kernel.
-constexpr int kBigM = 8192;
+constexpr int kBigM = 4096;   // from here the 256x256 kernel (no split-K) beats the split-K one
 
 FusePlan fuse_plan(const dflash_fuse_args& a) {
     FusePlan pl;

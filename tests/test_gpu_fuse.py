@@ -129,11 +129,12 @@ def test_fuse_large_ragged_rows_scattered_slots():
     assert ht_err <= TOL[BF16] and kv_err <= TOL[BF16]
 
 
-@pytest.mark.parametrize("M", [8191, 8192])
+@pytest.mark.parametrize("M", [4095, 4096, 8191])
 def test_fuse_path_boundary(M):
-    """M = 8191 is the largest fusion on the split-K kernels, 8192 the
-    smallest on the 256x256 kernel with the K/V epilogue (32 full row tiles);
-    one layer, shuffled slots, sampled rows checked."""
+    """M = 4095 is the largest fusion on the split-K kernels, 4096 the
+    smallest on the 256x256 kernel with the K/V epilogue (16 full row tiles),
+    8191 that kernel with a ragged last row tile; one layer, shuffled slots,
+    sampled rows checked."""
     L = 1
     npages = (M + 15) // 16 + 3
     rng = np.random.default_rng(M)

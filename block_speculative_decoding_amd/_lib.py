@@ -12,7 +12,9 @@ import os
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libdflash.so")
+# DFLASH_LIBRARY names another build of the same library (the host-sanitized
+# build the ABI tests run against); by default the in-tree libdflash.so.
+LIB_PATH = os.environ.get("DFLASH_LIBRARY") or os.path.join(PKG, "libdflash.so")
 
 DFLASH_BF16, DFLASH_F32 = 0, 1
 D, NCAPTURE, HQ, HKV, HEAD_DIM, BLOCK, PAGE, INTER = 2560, 5, 32, 8, 128, 8, 16, 5120

@@ -377,3 +377,15 @@ def test_calibration_validation(lib):
     f = ctypes.c_double()
     assert lib.dflash_calib_mfma(0, FAKE, ctypes.byref(f), None) == -1
     assert lib.dflash_calib_mfma(5, None, ctypes.byref(f), None) == -1
+
+
+def test_sanitizer_runtime_present_when_expected(lib):
+    """Run under the host-sanitized library (test_abi_sanitized.py), this
+    process must have the AddressSanitizer and UBSan runtimes mapped and must
+    have loaded that library, not the default one."""
+    if os.environ.get("DFLASH_EXPECT_SANITIZERS") != "1":
+        return
+    from block_speculative_decoding_amd import _lib
+    maps = open("/proc/self/maps").read()
+    assert "libasan" in maps and "libubsan" in maps
+    assert _lib.LIB_PATH == os.environ["DFLASH_LIBRARY"] and _lib.LIB_PATH in maps

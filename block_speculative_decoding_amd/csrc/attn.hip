@@ -212,13 +212,13 @@ __global__ __launch_bounds__(kWgThreads, 1) void attn_bf16_kernel(AttnParams p) 
         const int myk = (m32 >> 4) ? ph1 : ph0;
         const uint4* kp = reinterpret_cast<const uint4*>(kc + ((int64_t)myk * 8 + g) * 2048 + 8 * ((m32 & 15) + 16 * hl));
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) kr[kb] = kp[32 * kb];
+        for (int kb = 0; kb < 8; ++kb) kr[kb] = ld_stream(kp + 32 * kb);
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
             const int ph = kb2 ? ph1 : ph0;
             const uint4* vp = reinterpret_cast<const uint4*>(vc + ((int64_t)ph * 8 + g) * 2048 + 256 * hl + 8 * m32);
 #pragma unroll
-            for (int db = 0; db < 4; ++db) vr[kb2][db] = vp[64 * db];
+            for (int db = 0; db < 4; ++db) vr[kb2][db] = ld_stream(vp + 64 * db);
         }
     };
 

@@ -1,7 +1,8 @@
 // Calibration kernels: the practical ceilings the roofline fractions are read
 // against, measured on the part that runs the hot path (gfx950).
 //
-//   stream_read  -- every byte of a buffer read once with 16-byte loads,
+//   stream_read  -- every byte of a buffer read once with 16-byte
+//                   nontemporal loads (the faster form for data read once),
 //                   eight in flight per thread, each workgroup reading 32 KiB
 //                   contiguous runs (grid given, 2048 by default); a
 //                   per-workgroup xor of the data goes to a sink so the
@@ -32,7 +33,7 @@ __global__ __launch_bounds__(kCalThreads) void stream_kernel(const uint4* __rest
 #pragma unroll
         for (int u = 0; u < kCalUnroll; ++u) {
             const int64_t j = i + (int64_t)u * kCalThreads;
-            v[u] = j < n16 ? src[j] : make_uint4(0u, 0u, 0u, 0u);
+            v[u] = j < n16 ? ld_stream(src + j) : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
         for (int u = 0; u < kCalUnroll; ++u) {

@@ -47,20 +47,21 @@ struct HeadParams {
     float* dstats;        // optional [B][7][2]: (m, s) per proposal row
 };
 
-// Eight consecutive stored logits as fp32 (one 16-byte load for bf16, two
-// for fp32); offsets are multiples of 8.
+// Eight consecutive stored logits as fp32 (one 16-byte streaming load for
+// bf16, two for fp32); offsets are multiples of 8.
 template <typename T> struct Group8;
 template <> struct Group8<uint16_t> {
     static __device__ __forceinline__ void load(const uint16_t* p, float* f) {
-        const uint4 w = *reinterpret_cast<const uint4*>(p);
+        const uint4 w = ld_stream(reinterpret_cast<const uint4*>(p));
         f[0] = lo_bf16(w.x); f[1] = hi_bf16(w.x); f[2] = lo_bf16(w.y); f[3] = hi_bf16(w.y);
         f[4] = lo_bf16(w.z); f[5] = hi_bf16(w.z); f[6] = lo_bf16(w.w); f[7] = hi_bf16(w.w);
     }
 };
 template <> struct Group8<float> {
     static __device__ __forceinline__ void load(const float* p, float* f) {
-        const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
-        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+        const uint4 a = ld_stream(reinterpret_cast<const uint4*>(p)), b = ld_stream(reinterpret_cast<const uint4*>(p + 4));
+        f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y); f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
+        f[4] = __uint_as_float(b.x); f[5] = __uint_as_float(b.y); f[6] = __uint_as_float(b.z); f[7] = __uint_as_float(b.w);
     }
 };
 

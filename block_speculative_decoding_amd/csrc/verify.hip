@@ -50,12 +50,12 @@ struct Params {
     StatPart* stats; Desc* desc; SamplePart* samp;
 };
 
-// 16 bytes of logits widened to fp32.
+// 16 bytes of logits widened to fp32 (streamed: nontemporal loads).
 template <typename T> struct Vec;
 template <> struct Vec<uint16_t> {
     static constexpr int N = 8;
     static __device__ __forceinline__ void load(const uint16_t* p, float* f) {
-        uint4 w = *reinterpret_cast<const uint4*>(p);
+        const uint4 w = ld_stream(reinterpret_cast<const uint4*>(p));
         f[0] = lo_bf16(w.x); f[1] = hi_bf16(w.x); f[2] = lo_bf16(w.y); f[3] = hi_bf16(w.y);
         f[4] = lo_bf16(w.z); f[5] = hi_bf16(w.z); f[6] = lo_bf16(w.w); f[7] = hi_bf16(w.w);
     }
@@ -63,8 +63,8 @@ template <> struct Vec<uint16_t> {
 template <> struct Vec<float> {
     static constexpr int N = 4;
     static __device__ __forceinline__ void load(const float* p, float* f) {
-        float4 w = *reinterpret_cast<const float4*>(p);
-        f[0] = w.x; f[1] = w.y; f[2] = w.z; f[3] = w.w;
+        const uint4 w = ld_stream(reinterpret_cast<const uint4*>(p));
+        f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y); f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);
     }
 };
 

@@ -252,6 +252,17 @@ def traffic_per_launch():
         return None
 
 
+def host_cpu_model():
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(wl):
     """The oracle as it stands, timed on the host cores on a bounded sample of
     the same workload and scaled to one full cycle: the fusion of all new rows,
@@ -295,6 +306,7 @@ def cpu_baseline(wl):
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {
         "value": round(1.0 / cycle, 6), "unit": "cycles/s", "cores": int(threads), "kind": "oracle",
+        "host": {"cpu_count": os.cpu_count(), "model": host_cpu_model()},
         "sample": (f"float64 numpy oracle: fusion of all {wl.M} new rows ({t_fuse:.2f}s), block attention of "
                    f"32 of 64 sequences x 5 layers ({t_attn:.2f}s, scaled x2), verification of all 64 "
                    f"sequences, 32 greedy + 32 sampled ({t_ver:.2f}s); "

@@ -7,21 +7,26 @@
 // per-head K RMSNorm before RoPE; unquantized K/V projections fused into one
 // matrix multiplication).
 //
-// Launch sequence on one stream (bf16, M below 8192 rows):
+// Launch sequence on one stream (bf16, M below 4096 rows):
 //   gemm  (A = the five capture pointers, one K segment each; B = W_c)
 //         -> fp32 split-K partials [ks1][M][2560]
-//   norm  -> sums the partials, RMSNorm with g_c, stores H_t (dtype)
+//   norm  -> sums the partials, RMSNorm with g_c, stores H_t (dtype); with
+//            the K/V epilogue below, also each row's RoPE table
 //   gemm  (A = H_t, B = W_KV of all layers at once, N = layers * 2048)
+//         while its 128x128 tiles fit one 512-thread workgroup per CU (up to
+//         256 tiles, e.g. M <= 384 rows at 5 layers): two 4-wave k-groups per
+//         tile added through LDS, then the K/V epilogue (per 128-wide head: K
+//         gets k_norm and RoPE, V is copied; both are stored into the paged
+//         cache layout); no partials and no kv launch.  Otherwise:
 //         -> fp32 split-K partials [ks2][M][N]
-//   kv    -> sums the partials; per 128-wide head: K gets k_norm and RoPE,
-//            V is copied; both are scattered into the paged cache layout.
-// From 8192 rows on, both GEMMs use 256x256 tiles without split-K and the
+//   kv    -> sums the partials and does the same per head.
+// From 4096 rows on, both GEMMs use 256x256 tiles without split-K and the
 // second one carries the K/V injection in its epilogue (no kv launch).
+// fp32 runs the fp32 GEMM with split-K, the norm and the kv launch.
 // The bf16 GEMMs run on the 32x32x16 bf16 matrix instruction with operands
-// staged through LDS by loads that write LDS directly (global_load_lds for
-// the split-K kernel, buffer loads for the large-M one); tiles are laid out
-// contiguously per XCD in 8-row groups so that tiles sharing an operand panel
-// run on the same L2.
+// staged through LDS by buffer loads that write LDS directly; tiles are laid
+// out contiguously per XCD in 8-row groups so that tiles sharing an operand
+// panel run on the same L2.
 #include <cmath>
 
 #include "device_common.h"
@@ -64,16 +69,6 @@ constexpr int kBigStageBytes = 2 * BMB * kBigPitch;
 constexpr int kBigPartsA = BMB * 8 / kBigThreads;  // buffer loads per thread per stage and operand (4)
 __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
-
-struct KvEpilogue {
-    const float2* cs;      // [M][64] (cos, sin) of pos[row] * inv_freq[i]
-    const void* gk;        // [L][128]
-    float eps;
-    const int64_t* slot;
-    int64_t num_pages;
-    void* kc[5];
-    void* vc[5];
-};
 
 // MODE 0: fp32 partials to p.part (the fusion GEMM); 1: the K/V epilogue
 // (ep); 2: the shared head's epilogue (hp): bf16 logits through LDS and the
@@ -448,16 +443,18 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
 // (cos, sin) of pos[m] * inv_freq[i] for every fused row: fp64 angle and
 // range reduction, fp32 sincos.
 struct RopeTabParams { const int32_t* pos; float2* cs; int M; double inv_freq[64]; };
-__global__ __launch_bounds__(256) void rope_table_kernel(RopeTabParams p) {
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= p.M * 64) return;
-    const int m = idx >> 6, i = idx & 63;
+__device__ __forceinline__ void rope_entry(const RopeTabParams& p, int m, int i) {
     double ang = (double)p.pos[m] * p.inv_freq[i];
     const double two_pi = 6.283185307179586;
     ang -= rint(ang * (1.0 / two_pi)) * two_pi;
     float sn, cs;
     sincosf((float)ang, &sn, &cs);
-    p.cs[idx] = make_float2(cs, sn);
+    p.cs[m * 64 + i] = make_float2(cs, sn);
+}
+__global__ __launch_bounds__(256) void rope_table_kernel(RopeTabParams p) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= p.M * 64) return;
+    rope_entry(p, idx >> 6, idx & 63);
 }
 
 // Sum split-K partials of one row, RMSNorm with g_c, store H_t.  The split
@@ -480,11 +477,13 @@ __device__ __forceinline__ void norm_store(const float* y, float rinv, const T* 
     }
 }
 
+// With rp.cs set, the workgroup of row m also writes row m's RoPE table.
 template <typename T>
 __global__ __launch_bounds__(kNormThreads) void fuse_norm_kernel(const float* part, int ks, int M, const T* gc,
-                                                                float eps, T* ht, T* ht_out) {
+                                                                float eps, T* ht, T* ht_out, RopeTabParams rp) {
     constexpr int D = DFLASH_D;
     const int m = blockIdx.x, tid = threadIdx.x;
+    if (rp.cs && tid < 64) rope_entry(rp, m, tid);
     float y[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < kMaxKs; ++s) {
@@ -592,6 +591,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Large fused row counts use the 256x256 kernel (no split-K, fused K/V
 // epilogue); small ones the 128x128 split-K kernel.
 constexpr int kBigM = 4096;   // from here the 256x256 kernel (no split-K) beats the split-K one
+constexpr int kPairTiles = 256;  // K/V GEMM tiles that one 512-thread workgroup per CU covers in one round
 
 FusePlan fuse_plan(const dflash_fuse_args& a) {
     FusePlan pl;
@@ -602,13 +602,21 @@ FusePlan fuse_plan(const dflash_fuse_args& a) {
     pl.ks1 = pl.big ? 1 : bf ? gemm_split(M, DFLASH_D, DFLASH_NCAPTURE * DFLASH_D)
                              : gemm_split_f32(M, DFLASH_D, DFLASH_NCAPTURE * DFLASH_D);
     pl.ks2 = pl.big ? 1 : bf ? gemm_split(M, N2, DFLASH_D) : gemm_split_f32(M, N2, DFLASH_D);
+    // bf16 below kBigM: where the K/V GEMM's tiles fit one 512-thread
+    // workgroup per CU, it runs unsplit on two k-groups with the K/V epilogue
+    // (no partials, no K/V kernel).  The first GEMM keeps its split-K
+    // partials: on two k-groups with half the splits it measured slower
+    // (31.9 against 28.9 us at M = 302) than the norm kernel gains from
+    // reading half the partials (5.6 against 6.9 us).
+    pl.pair2 = bf && !pl.big && ((M + 127) / 128) * (N2 / 128) <= kPairTiles;
+    if (pl.pair2) pl.ks2 = 1;
     const size_t es = bf ? 2 : 4;
     pl.off_part1 = 0;
     pl.off_ht = align256((size_t)pl.ks1 * M * DFLASH_D * 4);
     pl.off_part2 = pl.off_ht + align256((size_t)M * DFLASH_D * es);
-    // The big path needs no second partial buffer, only the RoPE table.
-    pl.ws_bytes = pl.off_part2 + (pl.big ? align256((size_t)M * 64 * sizeof(float2))
-                                         : align256((size_t)pl.ks2 * M * N2 * 4));
+    // The big and pair K/V paths need no second partial buffer, only the RoPE table.
+    pl.ws_bytes = pl.off_part2 + (pl.big || pl.pair2 ? align256((size_t)M * 64 * sizeof(float2))
+                                                     : align256((size_t)pl.ks2 * M * N2 * 4));
     return pl;
 }
 
@@ -645,6 +653,20 @@ hipError_t launch_fuse(const dflash_fuse_args& a, const FusePlan& pl, void* ws, 
         if (e != hipSuccess) return e;
     }
 
+    // The RoPE table of the K/V epilogues (big and pair paths), after H_t in
+    // the workspace: written by the norm kernel where it runs one workgroup
+    // per row, else by its own launch.
+    RopeTabParams rp = {};
+    if (pl.big || pl.pair2) {
+        rp.pos = a.pos; rp.cs = reinterpret_cast<float2*>(part2); rp.M = M;
+        for (int i = 0; i < 64; ++i) rp.inv_freq[i] = inv_freq[i];
+        ep.cs = rp.cs;
+        ep.gk = a.gk; ep.eps = a.eps; ep.slot = a.slot; ep.num_pages = a.num_pages;
+        for (int i = 0; i < 5; ++i) { ep.kc[i] = a.k_cache[i]; ep.vc[i] = a.v_cache[i]; }
+    }
+    const bool rope_in_norm = pl.ks1 > 1 && rp.cs != nullptr;
+    if (rp.cs && !rope_in_norm) rope_table_kernel<<<(M * 64 + 255) / 256, 256, 0, s>>>(rp);
+
     if (pl.ks1 == 1) {
         const int nb = (M + 3) / 4;
         if (bf)
@@ -657,10 +679,10 @@ hipError_t launch_fuse(const dflash_fuse_args& a, const FusePlan& pl, void* ws, 
     } else if (bf) {
         fuse_norm_kernel<uint16_t><<<M, kNormThreads, 0, s>>>(part1, pl.ks1, M, static_cast<const uint16_t*>(a.gc),
                                                               a.eps, static_cast<uint16_t*>(ht),
-                                                              static_cast<uint16_t*>(a.ht_out));
+                                                              static_cast<uint16_t*>(a.ht_out), rp);
     } else {
         fuse_norm_kernel<float><<<M, kNormThreads, 0, s>>>(part1, pl.ks1, M, static_cast<const float*>(a.gc), a.eps,
-                                                           static_cast<float*>(ht), static_cast<float*>(a.ht_out));
+                                                           static_cast<float*>(ht), static_cast<float*>(a.ht_out), rp);
     }
 
     GemmParams g2 = {};
@@ -669,17 +691,11 @@ hipError_t launch_fuse(const dflash_fuse_args& a, const FusePlan& pl, void* ws, 
     gemm_set_split(g2, a.dtype, pl.ks2);
     g2.part = part2;
     if (pl.big) {
-        RopeTabParams rp;
-        rp.pos = a.pos; rp.cs = reinterpret_cast<float2*>(part2); rp.M = M;
-        for (int i = 0; i < 64; ++i) rp.inv_freq[i] = inv_freq[i];
-        rope_table_kernel<<<(M * 64 + 255) / 256, 256, 0, s>>>(rp);
-        ep.cs = reinterpret_cast<const float2*>(part2);
-        ep.gk = a.gk; ep.eps = a.eps; ep.slot = a.slot; ep.num_pages = a.num_pages;
-        for (int i = 0; i < 5; ++i) { ep.kc[i] = a.k_cache[i]; ep.vc[i] = a.v_cache[i]; }
         const int tiles = ((M + BMB - 1) / BMB) * (N2 / BNB);
         gemm_bf16_big_kernel<1><<<(tiles + kXcds - 1) / kXcds * kXcds, kBigThreads, 0, s>>>(g2, ep, HeadEpilogue{});
         return hipGetLastError();
     }
+    if (pl.pair2) return launch_gemm_pair(g2, ep, s);
     hipError_t e = launch_gemm(g2, a.dtype, s);
     if (e != hipSuccess) return e;
 

@@ -27,6 +27,20 @@ struct GemmParams {
                           // goes here ([M][N]) instead of part
 };
 
+// K/V injection epilogue of the context fusion's second GEMM (N = L * 2048
+// columns [K_0 | V_0 | K_1 | ...], 128 per head): k_norm over each K head,
+// RoPE with the (cos, sin) table, bf16 store into the paged caches at each
+// row's slot (rows whose slot lies outside the cache are skipped).
+struct KvEpilogue {
+    const float2* cs;      // [M][64] (cos, sin) of pos[row] * inv_freq[i]
+    const void* gk;        // [L][128] bf16 k_norm weights
+    float eps;
+    const int64_t* slot;
+    int64_t num_pages;
+    void* kc[5];
+    void* vc[5];
+};
+
 // Tile id for this workgroup: XCD-contiguous ranges, then 8-row M groups.
 struct TileId { int tm, tn, ks; bool valid; };
 __device__ __forceinline__ TileId tile_id(const GemmParams& p, int tiles_m, int tiles_n) {
@@ -100,5 +114,11 @@ void gemm_set_split(GemmParams& g, int dtype, int ks);
 // aligned rows, a_stride < 2^23; fp32: 64x64 tiles, N % 64 == 0, K and
 // seg_w multiples of 16, a_stride a multiple of 4.
 hipError_t launch_gemm(const GemmParams& g, int dtype, hipStream_t s);
+// bf16 K/V projection with its epilogue (no partials): the same 128x128
+// tiles with two 4-wave groups per 512-thread workgroup (one workgroup per
+// CU), each group taking half of the tile's k-tiles; the halves are added
+// through LDS and the tile goes through the K/V epilogue.  g.ks == 1, N a
+// multiple of 2048: each 128-column tile is one head of one layer.
+hipError_t launch_gemm_pair(const GemmParams& g, const KvEpilogue& ep, hipStream_t s);
 
 }  // namespace dflash

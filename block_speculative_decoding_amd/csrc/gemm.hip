@@ -30,7 +30,97 @@ constexpr int kUnits = 2 * BM * 8;           // A then B, 16-byte units per stag
 constexpr int kStageBytes = kUnits * 16;     // 32 KiB
 __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
-__global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
+constexpr int kFtPitch = 136;   // floats per row of the fp32 [128][.] tile in LDS (conflict-free halves)
+
+// K/V epilogue of one 128x128 tile: rows m0 .. m0 + 127, column tile tn =
+// one head of one layer ([layer][K/V][head], 128 columns each), from the
+// fp32 tile ft in LDS.  512 threads, four per row: thread q of a row owns
+// dims 8q .. 8q+7 and 8q+32 .. 8q+39 and their RoPE partners d + 64.
+//   K: k_norm over the head's 128 values (the four threads' sums of squares
+//      added by two lane swaps), RoPE on (d, d + 64) with the (cos, sin)
+//      table, bf16; each run of 8 dims of one token is one 16-byte granule
+//      of the page layout: four stores per thread.
+//   V: as projected, bf16; a V granule holds one dim of 8 tokens, so each
+//      value is its own 2-byte store.
+__device__ __forceinline__ void kv_epilogue(const float* ft, int M, int m0, int tn, const KvEpilogue& ep, int tid) {
+    const int row = tid >> 2, q = tid & 3;
+    const int l = tn >> 4, isv = (tn >> 3) & 1, head = tn & 7;
+    const int gm = m0 + row;
+    const int64_t nslots = ep.num_pages * 16;
+    const int64_t slot = gm < M ? ep.slot[gm] : -1;
+    const bool ok = slot >= 0 && slot < nslots;
+    const int tt = (int)(slot & 15);
+    const float* fr = ft + row * kFtPitch;
+    float x[2][8], y[2][8];   // dims 8q + 32h + e and their partners + 64
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            const float4 a = *reinterpret_cast<const float4*>(fr + 8 * q + 32 * h + 4 * v);
+            const float4 b = *reinterpret_cast<const float4*>(fr + 64 + 8 * q + 32 * h + 4 * v);
+            x[h][4 * v + 0] = a.x; x[h][4 * v + 1] = a.y; x[h][4 * v + 2] = a.z; x[h][4 * v + 3] = a.w;
+            y[h][4 * v + 0] = b.x; y[h][4 * v + 1] = b.y; y[h][4 * v + 2] = b.z; y[h][4 * v + 3] = b.w;
+        }
+    if (!isv) {
+        float ss = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += x[h][e] * x[h][e] + y[h][e] * y[h][e];
+        ss += __shfl_xor(ss, 1);
+        ss += __shfl_xor(ss, 2);
+        if (!ok) return;
+        const float rinv = __builtin_amdgcn_rsqf(ss * (1.0f / 128.0f) + ep.eps);
+        const uint16_t* gk = static_cast<const uint16_t*>(ep.gk) + l * 128;
+        const float2* cs = ep.cs + (int64_t)gm * 64;
+        uint16_t* blk = static_cast<uint16_t*>(ep.kc[l]) + ((slot >> 4) * 8 + head) * 2048;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t w1[4], w2[4];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                float o1[2], o2[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int d = 8 * q + 32 * h + e + u;
+                    const float a = x[h][e + u] * (rinv * bf16_bits_to_f32(gk[d]));
+                    const float b = y[h][e + u] * (rinv * bf16_bits_to_f32(gk[d + 64]));
+                    const float2 c = cs[d];
+                    o1[u] = a * c.x - b * c.y;
+                    o2[u] = b * c.x + a * c.y;
+                }
+                w1[e >> 1] = pack_bf16x2(o1[0], o1[1]);
+                w2[e >> 1] = pack_bf16x2(o2[0], o2[1]);
+            }
+            *reinterpret_cast<uint4*>(blk + 256 * (q + 4 * h) + 8 * tt) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+            *reinterpret_cast<uint4*>(blk + 256 * (q + 4 * h) + 8 * (tt + 16)) = make_uint4(w2[0], w2[1], w2[2], w2[3]);
+        }
+        return;
+    }
+    if (!ok) return;
+    uint16_t* blk = static_cast<uint16_t*>(ep.vc[l]) + ((slot >> 4) * 8 + head) * 2048;
+    const int te = ((tt >> 3) << 2) | (tt & 3), th = (tt >> 2) & 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int d = 8 * q + 32 * h + e;
+            blk[512 * (d >> 5) + 256 * th + 8 * (d & 31) + te] = (uint16_t)f32_to_bf16_bits(x[h][e]);
+            blk[512 * ((d + 64) >> 5) + 256 * th + 8 * (d & 31) + te] = (uint16_t)f32_to_bf16_bits(y[h][e]);
+        }
+}
+
+// KG groups of four waves per workgroup (KG = 1: 256 threads, two
+// workgroups per CU; KG = 2: 512 threads, one per CU).  Group g runs the
+// loop above over its share of the tile's k-tiles with its own two stages;
+// both groups take the same number of steps (a group past its share loads a
+// clamped k-tile and skips the MFMAs), so the workgroup barriers pair up.
+// With KG = 2 group 1 then hands its products to group 0 through LDS, and
+// the summed tile goes through the K/V epilogue.
+
+template <int KG, bool KVE>
+__global__ __launch_bounds__(kThreads * KG, 2 / KG) void gemm_bf16_kernel(GemmParams p, KvEpilogue ep) {
+    static_assert((KG == 1 && !KVE) || (KG == 2 && KVE), "one k-group with partials or bf16 out; two with the K/V epilogue");
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = p.N / BN;
     const TileId t = tile_id(p, tiles_m, tiles_n);
     if (!t.valid) return;
@@ -40,20 +130,30 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
     if (kt0 >= kt1) return;
     const int nloc = kt1 - kt0;
 
-    __shared__ __attribute__((aligned(1024))) uint4 lds[2 * kUnits];
+    __shared__ __attribute__((aligned(1024))) uint4 lds[KG * 2 * kUnits];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // The group index is read as wave-uniform: every quantity derived from it
+    // (k range, descriptors, the padding-step test) is then scalar, so the
+    // padding steps skip their MFMAs by a branch (matrix instructions ignore
+    // the exec mask) and the buffer descriptors sit in SGPRs.
+    const int grp = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid / kThreads);
+    const int tg = tid % kThreads, wave = tg >> 6;   // thread and wave within the group
+    const int nh = (nloc + KG - 1) / KG;              // steps every group runs
+    const int g0 = kt0 + grp * nh;
+    const int ng = max(0, min(nloc - grp * nh, nh));  // k-tiles this group owns
+    auto ktile = [&](int i) { return ng > 0 ? g0 + min(i, ng - 1) : kt0; };
     const int m0 = t.tm * BM, n0 = t.tn * BN;
     const uint16_t* bmat = static_cast<const uint16_t*>(p.b) + (int64_t)n0 * p.K;
     const void *aseg0 = p.aseg[0], *aseg1 = p.aseg[1], *aseg2 = p.aseg[2], *aseg3 = p.aseg[3], *aseg4 = p.aseg[4];
     const uint32_t arows = (uint32_t)min(p.M - m0, BM);
 
-    // Load j (0..3) of a thread covers unit P = j * 256 + tid of the A (or B)
+    // Load j (0..3) of a thread covers unit P = j * 256 + tg of the A (or B)
     // half: row P >> 3, chunk (P & 7) ^ swz8(row).
     uint32_t voa[4], vob[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int P = j * kThreads + tid, r = P >> 3, c = (P & 7) ^ swz8(r);
+        const int P = j * kThreads + tg, r = P >> 3, c = (P & 7) ^ swz8(r);
         voa[j] = (uint32_t)(r * (int)p.a_stride + 8 * c) * 2u;
         vob[j] = (uint32_t)(r * p.K + 8 * c) * 2u;
     }
@@ -76,8 +176,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
     // The wave index read as wave-uniform, so that each load's LDS base (M0)
     // is scalar arithmetic.
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    uint4* const gl = lds + grp * 2 * kUnits;  // this group's two stages
     auto load_part = [&](const StageSrc& src, int slot, int part) {
-        uint4* sb = lds + slot * kUnits + wave_s * 64;
+        uint4* sb = gl + slot * kUnits + wave_s * 64;
         if (part < 4) {
             llvm_amdgcn_raw_buffer_load_lds(src.a, (__attribute__((address_space(3))) uint32_t*)(sb + part * kThreads),
                                             16, (int)voa[part], 0, 0, 0);
@@ -99,7 +200,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
     // Rows wr + 32 i + lr (A) and wc + 32 j + lr (B) all have swizzle
     // swz8(lr); substep s flips chunk bits 1-2 (address ^ 32 s), block 1 adds
     // 32 rows (4096 bytes).
-    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint4*)lds);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint4*)gl);
     const uint32_t a_lane = lds0 + 128u * (wr + lr) + 16u * (lh ^ swz8(lr));
     const uint32_t b_lane = lds0 + 16u * BM * 8 + 128u * (wc + lr) + 16u * (lh ^ swz8(lr));
     auto rd = [&](int slot, int ks, bf16x8* a, bf16x8* b) {
@@ -121,7 +222,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
     bf16x8 fa[2][2], fb[2][2];
 #pragma unroll
     for (int s0 = 0; s0 < 2; ++s0) {
-        const StageSrc src = stage_src(kt0 + min(s0, nloc - 1));
+        const StageSrc src = stage_src(ktile(s0));
 #pragma unroll
         for (int t2 = 0; t2 < 8; ++t2) load_part(src, s0, t2);
     }
@@ -129,15 +230,16 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     rd(0, 0, fa[0], fb[0]);
-    for (int i = 0; i < nloc; ++i) {
+    for (int i = 0; i < nh; ++i) {
         const int slot = i & 1;
-        const StageSrc nsrc = stage_src(kt0 + min(i + 2, nloc - 1));
+        const bool own = KG == 1 || i < ng;   // uniform per group: false only on a group's padding steps
+        const StageSrc nsrc = stage_src(ktile(i + 2));
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
             rd(slot, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
             wait_lgkm<4>();  // substep s's reads (issued before these 4) are back
             __builtin_amdgcn_sched_barrier(0);
-            mm(fa[s & 1], fb[s & 1]);
+            if (own) mm(fa[s & 1], fb[s & 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
         wait_lgkm<0>();
@@ -148,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t2 = 0; t2 < 8; ++t2) {
-            if ((t2 & 1) == 0) {
+            if ((t2 & 1) == 0 && own) {
                 const int q = t2 >> 1;
                 acc[q >> 1][q & 1] =
                     __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][q >> 1], fb[1][q & 1], acc[q >> 1][q & 1], 0, 0, 0);
@@ -162,6 +264,36 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
     wait_lgkm<0>();
 
     // Lane holds column lr of each 32x32 block, rows 8*(r/4) + 4*lh + (r%4).
+    float* const ft = reinterpret_cast<float*>(lds);  // [128][kFtPitch] fp32 tile (KG == 2)
+    auto ft_at = [&](int i, int j, int r) {
+        return (wr + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3)) * kFtPitch + wc + 32 * j + lr;
+    };
+    if (KG == 2) {
+        __syncthreads();  // both groups are done with their stages
+        if (grp == 1) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) ft[ft_at(i, j, r)] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (grp == 0) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int o = ft_at(i, j, r);
+                        ft[o] += acc[i][j][r];
+                    }
+        }
+        __syncthreads();
+        kv_epilogue(ft, p.M, m0, t.tn, ep, tid);
+        return;
+    }
     if (p.out_bf16) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -265,6 +397,13 @@ int gemm_split_f32(int M, int N, int K) {
     return (nk + per - 1) / per;
 }
 
+hipError_t launch_gemm_pair(const GemmParams& g, const KvEpilogue& ep, hipStream_t s) {
+    const int tiles = ((g.M + BM - 1) / BM) * (g.N / BN) * g.ks;
+    const int grid = (tiles + kGemmXcds - 1) / kGemmXcds * kGemmXcds;
+    gemm_bf16_kernel<2, true><<<grid, 2 * kThreads, 0, s>>>(g, ep);
+    return hipGetLastError();
+}
+
 void gemm_set_split(GemmParams& g, int dtype, int ks) {
     (void)dtype;
     g.ks = ks;
@@ -275,7 +414,7 @@ hipError_t launch_gemm(const GemmParams& g, int dtype, hipStream_t s) {
     if (dtype == DFLASH_BF16) {
         const int tiles = ((g.M + BM - 1) / BM) * (g.N / BN) * g.ks;
         const int grid = (tiles + kGemmXcds - 1) / kGemmXcds * kGemmXcds;
-        gemm_bf16_kernel<<<grid, kThreads, 0, s>>>(g);
+        gemm_bf16_kernel<1, false><<<grid, kThreads, 0, s>>>(g, KvEpilogue{});
     } else {
         gemm_f32_kernel<<<dim3((g.M + 63) / 64, g.N / 64, g.ks), kThreads, 0, s>>>(g);
     }

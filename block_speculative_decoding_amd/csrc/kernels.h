@@ -30,6 +30,7 @@ hipError_t launch_attn(const dflash_attn_args& a, const AttnPlan& plan, void* ws
 struct FusePlan {
     int ks1, ks2;          // split-K factors of the two GEMMs
     bool big;              // 256x256 kernels with the fused K/V epilogue
+    bool pair2;            // K/V GEMM on the 128x128 kernel with two k-groups and the K/V epilogue
     size_t off_part1, off_ht, off_part2, ws_bytes;
 };
 FusePlan fuse_plan(const dflash_fuse_args& a);

@@ -147,6 +147,27 @@ def test_fuse_path_boundary(M):
     assert ht_err <= TOL[BF16] and kv_err <= TOL[BF16]
 
 
+@pytest.mark.parametrize("M,L", [(384, 5), (385, 5), (2048, 1), (2049, 1)])
+def test_fuse_kv_pair_boundary(M, L):
+    """The K/V GEMM runs on two k-groups per workgroup with the K/V epilogue
+    while its 128x128 tiles number at most 256: M = 384 at five layers and
+    M = 2048 at one layer are the largest such fusions, 385 and 2049 the
+    smallest on the split-K GEMM + K/V kernel.  Shuffled slots, sampled rows
+    and the last row checked; slots not named keep their contents."""
+    npages = (M + 15) // 16 + 5
+    rng = np.random.default_rng(M + L)
+    slots = rng.permutation(npages * 16)[:M].astype(np.int64)
+    pos = rng.integers(0, 131072, M).astype(np.int32)
+    rows = np.sort(rng.choice(M, 48, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    ht_err, kv_err, kcs, vcs = _run(M, L, BF16, 10, npages, slots, pos, rows=rows)
+    note(f"fuse K/V path boundary M={M} L={L}: H_t err {ht_err:.3e}, K/V err {kv_err:.3e}")
+    assert ht_err <= TOL[BF16] and kv_err <= TOL[BF16]
+    untouched = np.setdiff1d(np.arange(npages * 16), slots)
+    assert np.all(read_slots(exact(kcs[L - 1]), untouched, k_offsets()) == -7.0)
+    assert np.all(read_slots(exact(vcs[L - 1]), untouched, v_offsets()) == -7.0)
+
+
 @pytest.mark.parametrize("shift", [16, 8])
 def test_fuse_large_contiguous_slots_page_offsets(shift):
     """Large-M path with slots in order starting at `shift`: with 16 every full

@@ -393,37 +393,62 @@ __global__ __launch_bounds__(kWgThreads, 1) void attn_bf16_kernel(AttnParams p) 
 }
 
 // ---------------------------------------------------------------- split merge
+// One workgroup per (KV head g, sequence b, quarter of the 32 query rows):
+// thread (row n, 4 dims) reads one float4 of each split's partial.  The
+// splits are taken kMergeU at a time with every load of a batch issued
+// before any is used, and batches combine online (running maximum M in log2
+// units, sum L and the weighted outputs rescaled when M grows).
+constexpr int kMergeU = 16;
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnParams p) {
-    const int g = blockIdx.x, b = blockIdx.y;
+    const int g = blockIdx.x, b = blockIdx.y, rq = blockIdx.z;
     const SeqRange sr = seq_range(p, b);
     if (sr.nspl <= 1) return;
     const int tid = threadIdx.x;
-    const int n = tid >> 3, d0 = 16 * (tid & 7);
+    const int n = 8 * rq + (tid >> 5), d0 = 4 * (tid & 31);
     const float* base = p.part + ((int64_t)b * 8 + g) * p.nsplit * kPartFloats;
-    float M = -INFINITY;
-    for (int c = 0; c < sr.nspl; ++c) M = fmaxf(M, base[c * kPartFloats + n]);
-    const float Mu = M == -INFINITY ? 0.f : M;
-    float L = 0.f, o[16];
+    float M = -INFINITY, L = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c0 = 0; c0 < sr.nspl; c0 += kMergeU) {
+        float mc[kMergeU], lc[kMergeU];
+        float4 ac[kMergeU];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[e] = 0.f;
-    for (int c = 0; c < sr.nspl; ++c) {
-        const float* pc = base + c * kPartFloats;
-        const float f = __builtin_amdgcn_exp2f(pc[n] - Mu);
-        L += pc[32 + n] * f;
-        const float4* av = reinterpret_cast<const float4*>(pc + 64 + n * 128 + d0);
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            const float4 v = av[e4];
-            o[4 * e4 + 0] += f * v.x; o[4 * e4 + 1] += f * v.y;
-            o[4 * e4 + 2] += f * v.z; o[4 * e4 + 3] += f * v.w;
+        for (int u = 0; u < kMergeU; ++u) {
+            if (c0 + u < sr.nspl) {
+                const float* pc = base + (int64_t)(c0 + u) * kPartFloats;
+                mc[u] = pc[n];
+                lc[u] = pc[32 + n];
+                ac[u] = *reinterpret_cast<const float4*>(pc + 64 + n * 128 + d0);
+            } else {
+                mc[u] = -INFINITY;
+                lc[u] = 0.f;
+                ac[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
+        float Mn = M;
+#pragma unroll
+        for (int u = 0; u < kMergeU; ++u) Mn = fmaxf(Mn, mc[u]);
+        if (Mn == -INFINITY) continue;
+        const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+        L *= sc;
+        o.x *= sc; o.y *= sc; o.z *= sc; o.w *= sc;
+#pragma unroll
+        for (int u = 0; u < kMergeU; ++u) {
+            const float f = mc[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc[u] - Mn);
+            L += lc[u] * f;
+            o.x += f * ac[u].x; o.y += f * ac[u].y; o.z += f * ac[u].z; o.w += f * ac[u].w;
+        }
+        M = Mn;
     }
+    const float Mu = M == -INFINITY ? 0.f : M;
     const float inv = 1.0f / L;
     T* orow = static_cast<T*>(p.out) + ((((int64_t)b * 32 + 4 * g + (n >> 3)) * 8 + (n & 7)) * 128) + d0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) Elem<T>::store(orow, e, o[e] * inv);
-    if (p.lse && (tid & 7) == 0)
+    Elem<T>::store(orow, 0, o.x * inv);
+    Elem<T>::store(orow, 1, o.y * inv);
+    Elem<T>::store(orow, 2, o.z * inv);
+    Elem<T>::store(orow, 3, o.w * inv);
+    if (p.lse && (tid & 31) == 0)
         p.lse[((int64_t)b * 32 + 4 * g + (n >> 3)) * 8 + (n & 7)] = (Mu + log2f(L)) * kLn2;
 }
 
@@ -637,7 +662,7 @@ hipError_t launch_attn(const dflash_attn_args& a, const AttnPlan& pl, void* ws, 
         return hipGetLastError();
     }
     attn_bf16_kernel<<<dim3(pl.nsplit, 8 / kHpw, a.B), kWgThreads, 0, s>>>(p);
-    if (pl.nsplit > 1) attn_merge_kernel<uint16_t><<<dim3(8, a.B), kThreads, 0, s>>>(p);
+    if (pl.nsplit > 1) attn_merge_kernel<uint16_t><<<dim3(8, a.B, 4), kThreads, 0, s>>>(p);
     return hipGetLastError();
 }
 

@@ -20,8 +20,9 @@
 // Launch sequence of dflash_draft_qkv:  norm -> gemm (N = 6144) -> scatter
 // Launch sequence of dflash_draft_mlp:  transpose -> gemm (N = 2560, K = 4096)
 //   -> residual + norm (with DFlash2's block convolution: residual + conv +
-//   norm per sequence) -> gemm (N = 10240) -> swiglu -> gemm (N = 2560,
-//   K = 5120) -> residual (+ final norm)
+//   norm per sequence) -> gemm (N = 10240; unsplit bf16 products go
+//   through the GEMM's SwiGLU epilogue, else the partials through swiglu)
+//   -> gemm (N = 2560, K = 5120) -> residual (+ final norm)
 #include "device_common.h"
 #include "gemm.h"
 #include "kernels.h"
@@ -364,9 +365,13 @@ hipError_t run_mlp(const dflash_mlp_args& a, const DraftMlpPlan& pl, char* ws, h
         residual_kernel<T><<<M, kRowThreads, 0, s>>>(part, g1.ks, M, static_cast<const T*>(a.x), h,
                                                    static_cast<const T*>(a.g_post), a.eps, c);
 
-    const GemmParams g2 = gemm_params(c, kD, a.w_gu, M, 2 * kInter, kD, pl.ks_gu, a.dtype, part);
+    // gate/up: unsplit bf16 products go straight through the SwiGLU epilogue;
+    // split-K (few rows) or fp32 products through the partials and swiglu_kernel.
+    GemmParams g2 = gemm_params(c, kD, a.w_gu, M, 2 * kInter, kD, pl.ks_gu, a.dtype, part);
+    const bool fused = a.dtype == DFLASH_BF16 && g2.ks == 1;
+    if (fused) g2.swiglu_out = reinterpret_cast<uint16_t*>(sw);
     if ((e = launch_gemm(g2, a.dtype, s)) != hipSuccess) return e;
-    swiglu_kernel<T><<<M, kRowThreads, 0, s>>>(part, g2.ks, M, sw);
+    if (!fused) swiglu_kernel<T><<<M, kRowThreads, 0, s>>>(part, g2.ks, M, sw);
 
     const GemmParams g3 = gemm_params(sw, kInter, a.w_d, M, kD, kInter, pl.ks_d, a.dtype, part);
     if ((e = launch_gemm(g3, a.dtype, s)) != hipSuccess) return e;

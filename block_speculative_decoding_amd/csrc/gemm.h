@@ -25,6 +25,10 @@ struct GemmParams {
     float* part;          // [ks][M][N]
     uint16_t* out_bf16;   // bf16 path with ks == 1: if set, the product rounded to bf16
                           // goes here ([M][N]) instead of part
+    uint16_t* swiglu_out; // bf16 path with ks == 1: if set, B is [gate ; up] (rows [0, N/2) and
+                          // [N/2, N)) and silu(gate) * up, from the fp32 products and rounded
+                          // to bf16, goes here ([M][N/2]); tile tn multiplies gate rows
+                          // 64 tn .. +63 and the same up rows
 };
 
 // K/V injection epilogue of the context fusion's second GEMM (N = L * 2048

@@ -144,7 +144,12 @@ __global__ __launch_bounds__(kThreads * KG, 2 / KG) void gemm_bf16_kernel(GemmPa
     const int ng = max(0, min(nloc - grp * nh, nh));  // k-tiles this group owns
     auto ktile = [&](int i) { return ng > 0 ? g0 + min(i, ng - 1) : kt0; };
     const int m0 = t.tm * BM, n0 = t.tn * BN;
-    const uint16_t* bmat = static_cast<const uint16_t*>(p.b) + (int64_t)n0 * p.K;
+    // SwiGLU tiles: B rows 0..63 of the tile are gate rows 64 tn .., rows
+    // 64..127 the up rows N/2 further on.
+    const bool swiglu = !KVE && p.swiglu_out != nullptr;
+    const int half = p.N / 2;
+    const uint16_t* bmat = static_cast<const uint16_t*>(p.b) + (int64_t)(swiglu ? 64 * t.tn : n0) * p.K;
+    const uint32_t brows = swiglu ? (uint32_t)(half + 64) : (uint32_t)BN;   // rows the descriptor spans
     const void *aseg0 = p.aseg[0], *aseg1 = p.aseg[1], *aseg2 = p.aseg[2], *aseg3 = p.aseg[3], *aseg4 = p.aseg[4];
     const uint32_t arows = (uint32_t)min(p.M - m0, BM);
 
@@ -154,8 +159,9 @@ __global__ __launch_bounds__(kThreads * KG, 2 / KG) void gemm_bf16_kernel(GemmPa
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int P = j * kThreads + tg, r = P >> 3, c = (P & 7) ^ swz8(r);
+        const int rb = swiglu && r >= 64 ? half - 64 + r : r;
         voa[j] = (uint32_t)(r * (int)p.a_stride + 8 * c) * 2u;
-        vob[j] = (uint32_t)(r * p.K + 8 * c) * 2u;
+        vob[j] = (uint32_t)(rb * p.K + 8 * c) * 2u;
     }
     // Both operands' buffer descriptors for k-tile kt, computed once per
     // k-tile at the top of the loop: the loads themselves sit between matrix
@@ -170,7 +176,7 @@ __global__ __launch_bounds__(kThreads * KG, 2 / KG) void gemm_bf16_kernel(GemmPa
         const uint16_t* a = static_cast<const uint16_t*>(av) + (int64_t)m0 * p.a_stride + kc;
         StageSrc s;
         s.a = buffer_rsrc(a, arows * (uint32_t)p.a_stride * 2u - (uint32_t)kc * 2u);
-        s.b = buffer_rsrc(bmat + kg, (uint32_t)BN * (uint32_t)p.K * 2u - (uint32_t)kg * 2u);
+        s.b = buffer_rsrc(bmat + kg, brows * (uint32_t)p.K * 2u - (uint32_t)kg * 2u);
         return s;
     };
     // The wave index read as wave-uniform, so that each load's LDS base (M0)
@@ -292,6 +298,39 @@ __global__ __launch_bounds__(kThreads * KG, 2 / KG) void gemm_bf16_kernel(GemmPa
         }
         __syncthreads();
         kv_epilogue(ft, p.M, m0, t.tn, ep, tid);
+        return;
+    }
+    if (swiglu) {
+        // The up waves (columns 64..127) hand their products to the gate
+        // waves through LDS ([128][68] fp32 over the operand stages); each
+        // gate wave then stores silu(gate) * up for its 64 x 64 block.
+        __syncthreads();  // every wave is done with the operand stages
+        constexpr int kUpPitch = 68;
+        float* up = reinterpret_cast<float*>(lds);
+        if (wc == 64) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        up[(wr + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3)) * kUpPitch + 32 * j + lr] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (wc == 64) return;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rl = wr + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    const int gm = m0 + rl;
+                    const float g = acc[i][j][r], u = up[rl * kUpPitch + 32 * j + lr];
+                    if (gm < p.M)
+                        p.swiglu_out[(int64_t)gm * half + 64 * t.tn + 32 * j + lr] =
+                            (uint16_t)f32_to_bf16_bits(g / (1.0f + expf(-g)) * u);
+                }
         return;
     }
     if (p.out_bf16) {

@@ -18,6 +18,8 @@
 // Every stored activation is rounded to the storage type once, from fp32.
 //
 // Launch sequence of dflash_draft_qkv:  norm -> gemm (N = 6144) -> scatter
+//   (where the GEMM would run two K splits, it runs unsplit on two k-groups
+//   per workgroup and writes the q / k_blk / v_blk layouts itself)
 // Launch sequence of dflash_draft_mlp:  transpose -> gemm (N = 2560, K = 4096)
 //   -> residual + norm (with DFlash2's block convolution: residual + conv +
 //   norm per sequence) -> gemm (N = 10240; unsplit bf16 products go
@@ -334,6 +336,13 @@ hipError_t run_qkv(const dflash_qkv_args& a, const DraftQkvPlan& pl, char* ws, h
     norm_rows_kernel<T><<<M, kRowThreads, 0, s>>>(static_cast<const T*>(a.x), static_cast<const T*>(a.g_in), a.eps,
                                                   an);
     const GemmParams g = gemm_params(an, kD, a.w_qkv, M, kQkvN, kD, pl.ks, a.dtype, part);
+    if (pl.pair) {
+        QkvEpilogue qe;
+        qe.q = static_cast<uint16_t*>(a.q);
+        qe.k = static_cast<uint16_t*>(a.k_blk);
+        qe.v = static_cast<uint16_t*>(a.v_blk);
+        return launch_gemm_pair_qkv(g, qe, s);
+    }
     hipError_t e = launch_gemm(g, a.dtype, s);
     if (e != hipSuccess) return e;
     qkv_scatter_kernel<T><<<M, kThreads, 0, s>>>(part, g.ks, M, static_cast<T*>(a.q), static_cast<T*>(a.k_blk),
@@ -397,9 +406,15 @@ DraftQkvPlan draft_qkv_plan(const dflash_qkv_args& a) {
     const int M = 8 * a.B;
     const bool bf = a.dtype == DFLASH_BF16;
     pl.ks = bf ? gemm_split(M, kQkvN, kD) : 1;
+    // Where the split-K kernel would run two splits (one residency round of
+    // two 4-wave workgroups per CU), one 8-wave workgroup per tile takes both
+    // halves of k and writes the head layout itself: the same sums, no fp32
+    // partials and no scatter launch.
+    pl.pair = bf && pl.ks == 2 && ((M + 127) / 128) * (kQkvN / 128) <= 256;
+    if (pl.pair) pl.ks = 1;
     pl.off_a = 0;
     pl.off_part = align256((size_t)M * kD * esize(a.dtype));
-    pl.ws_bytes = pl.off_part + align256((size_t)pl.ks * M * kQkvN * 4);
+    pl.ws_bytes = pl.off_part + (pl.pair ? 0 : align256((size_t)pl.ks * M * kQkvN * 4));
     return pl;
 }
 

@@ -45,6 +45,16 @@ struct KvEpilogue {
     void* vc[5];
 };
 
+// Head-layout epilogue of the draft layer's Q/K/V projection (N = 6144
+// columns [q heads 0..31 | k heads 0..7 | v heads 0..7], 128 per head): row
+// m = 8b + j, column 128h + d goes to q[b][h][j][d] (k_blk, v_blk: [b][h][j][d]
+// with 8 heads), rounded to bf16.
+struct QkvEpilogue {
+    uint16_t* q;
+    uint16_t* k;
+    uint16_t* v;
+};
+
 // Tile id for this workgroup: XCD-contiguous ranges, then 8-row M groups.
 struct TileId { int tm, tn, ks; bool valid; };
 __device__ __forceinline__ TileId tile_id(const GemmParams& p, int tiles_m, int tiles_n) {
@@ -124,5 +134,8 @@ hipError_t launch_gemm(const GemmParams& g, int dtype, hipStream_t s);
 // through LDS and the tile goes through the K/V epilogue.  g.ks == 1, N a
 // multiple of 2048: each 128-column tile is one head of one layer.
 hipError_t launch_gemm_pair(const GemmParams& g, const KvEpilogue& ep, hipStream_t s);
+// The same two-group kernel for the Q/K/V projection (g.ks == 1, N == 6144)
+// with the head-layout epilogue.
+hipError_t launch_gemm_pair_qkv(const GemmParams& g, const QkvEpilogue& qe, hipStream_t s);
 
 }  // namespace dflash

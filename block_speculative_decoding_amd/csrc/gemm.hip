@@ -110,17 +110,43 @@ __device__ __forceinline__ void kv_epilogue(const float* ft, int M, int m0, int 
         }
 }
 
+// Q/K/V head-layout epilogue of one 128x128 tile (column tile tn = one
+// head: q heads 0..31, then k and v heads 0..7) from the fp32 tile ft in
+// LDS.  512 threads, four per row, 32 dims each: a row's 128 dims are 256
+// contiguous bytes of the destination, and a sequence's 8 rows follow each
+// other.
+__device__ __forceinline__ void qkv_epilogue(const float* ft, int M, int m0, int tn, const QkvEpilogue& qe, int tid) {
+    const int row = tid >> 2, q4 = tid & 3;
+    const int m = m0 + row;
+    if (m >= M) return;
+    const int b = m >> 3, j = m & 7;
+    uint16_t* dst = tn < 32 ? qe.q + (((int64_t)b * 32 + tn) * 8 + j) * 128
+                  : tn < 40 ? qe.k + (((int64_t)b * 8 + (tn - 32)) * 8 + j) * 128
+                            : qe.v + (((int64_t)b * 8 + (tn - 40)) * 8 + j) * 128;
+    const float* fr = ft + row * kFtPitch + 32 * q4;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const float4 a = *reinterpret_cast<const float4*>(fr + 8 * v);
+        const float4 c = *reinterpret_cast<const float4*>(fr + 8 * v + 4);
+        *reinterpret_cast<uint4*>(dst + 32 * q4 + 8 * v) =
+            make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(c.x, c.y), pack_bf16x2(c.z, c.w));
+    }
+}
+
+constexpr int kEpiNone = 0, kEpiKv = 1, kEpiQkv = 2;
+
 // KG groups of four waves per workgroup (KG = 1: 256 threads, two
 // workgroups per CU; KG = 2: 512 threads, one per CU).  Group g runs the
 // loop above over its share of the tile's k-tiles with its own two stages;
 // both groups take the same number of steps (a group past its share loads a
 // clamped k-tile and skips the MFMAs), so the workgroup barriers pair up.
 // With KG = 2 group 1 then hands its products to group 0 through LDS, and
-// the summed tile goes through the K/V epilogue.
+// the summed tile goes through the K/V or the Q/K/V head-layout epilogue.
 
-template <int KG, bool KVE>
-__global__ __launch_bounds__(kThreads * KG, 2 / KG) void gemm_bf16_kernel(GemmParams p, KvEpilogue ep) {
-    static_assert((KG == 1 && !KVE) || (KG == 2 && KVE), "one k-group with partials or bf16 out; two with the K/V epilogue");
+template <int KG, int EPI>
+__global__ __launch_bounds__(kThreads * KG, 2 / KG) void gemm_bf16_kernel(GemmParams p, KvEpilogue ep, QkvEpilogue qe) {
+    static_assert((KG == 1 && EPI == kEpiNone) || (KG == 2 && EPI != kEpiNone),
+                  "one k-group with partials or bf16 out; two with the K/V or Q/K/V epilogue");
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = p.N / BN;
     const TileId t = tile_id(p, tiles_m, tiles_n);
     if (!t.valid) return;
@@ -146,7 +172,7 @@ __global__ __launch_bounds__(kThreads * KG, 2 / KG) void gemm_bf16_kernel(GemmPa
     const int m0 = t.tm * BM, n0 = t.tn * BN;
     // SwiGLU tiles: B rows 0..63 of the tile are gate rows 64 tn .., rows
     // 64..127 the up rows N/2 further on.
-    const bool swiglu = !KVE && p.swiglu_out != nullptr;
+    const bool swiglu = EPI == kEpiNone && p.swiglu_out != nullptr;
     const int half = p.N / 2;
     const uint16_t* bmat = static_cast<const uint16_t*>(p.b) + (int64_t)(swiglu ? 64 * t.tn : n0) * p.K;
     const uint32_t brows = swiglu ? (uint32_t)(half + 64) : (uint32_t)BN;   // rows the descriptor spans
@@ -297,7 +323,8 @@ __global__ __launch_bounds__(kThreads * KG, 2 / KG) void gemm_bf16_kernel(GemmPa
                     }
         }
         __syncthreads();
-        kv_epilogue(ft, p.M, m0, t.tn, ep, tid);
+        if (EPI == kEpiKv) kv_epilogue(ft, p.M, m0, t.tn, ep, tid);
+        else qkv_epilogue(ft, p.M, m0, t.tn, qe, tid);
         return;
     }
     if (swiglu) {
@@ -439,7 +466,14 @@ int gemm_split_f32(int M, int N, int K) {
 hipError_t launch_gemm_pair(const GemmParams& g, const KvEpilogue& ep, hipStream_t s) {
     const int tiles = ((g.M + BM - 1) / BM) * (g.N / BN) * g.ks;
     const int grid = (tiles + kGemmXcds - 1) / kGemmXcds * kGemmXcds;
-    gemm_bf16_kernel<2, true><<<grid, 2 * kThreads, 0, s>>>(g, ep);
+    gemm_bf16_kernel<2, kEpiKv><<<grid, 2 * kThreads, 0, s>>>(g, ep, QkvEpilogue{});
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_pair_qkv(const GemmParams& g, const QkvEpilogue& qe, hipStream_t s) {
+    const int tiles = ((g.M + BM - 1) / BM) * (g.N / BN) * g.ks;
+    const int grid = (tiles + kGemmXcds - 1) / kGemmXcds * kGemmXcds;
+    gemm_bf16_kernel<2, kEpiQkv><<<grid, 2 * kThreads, 0, s>>>(g, KvEpilogue{}, qe);
     return hipGetLastError();
 }
 
@@ -453,7 +487,7 @@ hipError_t launch_gemm(const GemmParams& g, int dtype, hipStream_t s) {
     if (dtype == DFLASH_BF16) {
         const int tiles = ((g.M + BM - 1) / BM) * (g.N / BN) * g.ks;
         const int grid = (tiles + kGemmXcds - 1) / kGemmXcds * kGemmXcds;
-        gemm_bf16_kernel<1, false><<<grid, kThreads, 0, s>>>(g, KvEpilogue{});
+        gemm_bf16_kernel<1, kEpiNone><<<grid, kThreads, 0, s>>>(g, KvEpilogue{}, QkvEpilogue{});
     } else {
         gemm_f32_kernel<<<dim3((g.M + 63) / 64, g.N / 64, g.ks), kThreads, 0, s>>>(g);
     }

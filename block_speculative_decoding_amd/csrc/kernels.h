@@ -40,6 +40,7 @@ hipError_t launch_fuse(const dflash_fuse_args& a, const FusePlan& plan, void* ws
 hipError_t launch_embed(const dflash_embed_args& a, hipStream_t s);
 struct DraftQkvPlan {
     int ks;                      // split-K factor of the Q/K/V GEMM
+    bool pair;                   // unsplit on two k-groups with the head-layout epilogue (no partials)
     size_t off_a, off_part, ws_bytes;
 };
 DraftQkvPlan draft_qkv_plan(const dflash_qkv_args& a);

@@ -51,9 +51,10 @@ def test_draft_embed_copies_rows(dtype):
     assert np.array_equal(exact(x), ref)
 
 
-@pytest.mark.parametrize("B", [1, 3, 40])
+@pytest.mark.parametrize("B", [1, 3, 40, 80])
 def test_draft_qkv_bf16_ragged_rows(B):
-    # 8, 24 and 320 block rows: one partial 128-row tile up to 2.5 tiles.
+    # 8, 24, 320 and 640 block rows: one partial 128-row tile up to 5 tiles;
+    # 640 rows run unsplit on two k-groups with the head-layout epilogue.
     import block_speculative_decoding_amd as dfl
     w = _weights(12, BF16)
     x = dev(synth.normal(12, "x", (B, 8, 2560)), BF16)

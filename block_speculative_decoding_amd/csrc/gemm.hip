@@ -1,4 +1,5 @@
-// Split-K bf16 GEMM and plain fp32 GEMM (gfx950); interface in gemm.h.
+// Split-K bf16 GEMM with fused epilogues and plain fp32 GEMM (gfx950);
+// interface in gemm.h.
 //
 // The bf16 kernel runs the 32x32x16 bf16 matrix instruction on operands
 // staged through LDS by buffer loads that write LDS directly; tiles are laid out
@@ -6,7 +7,10 @@
 // the same L2.  Used where the row count is a few hundred to a few thousand
 // (context fusion of newly verified rows, the draft layer's projections over
 // B x 8 block rows): the weights stream once, split over K so that every CU
-// gets a share.
+// gets a share.  Epilogues: fp32 split-K partials, bf16 products, SwiGLU of
+// [gate ; up] tiles; and, on the two-k-group form (one 512-thread workgroup
+// per tile, halves added through LDS), the context fusion's K/V injection or
+// the draft Q/K/V head layout, which need no partials.
 #include "device_common.h"
 #include "gemm.h"
 

@@ -639,22 +639,22 @@ def ragged_measurement(torch, dfl, synth):
     (mean ~4.6k) on shuffled pages: whole cycles (fusion of the new rows, 5
     attention layers, verification) eagerly, and attention per layer; once
     with the automatic split (one split per sequence: the batch alone fills
-    the chip, and the host does not see the lengths) and once with 2048-token
-    splits (a caller that knows its lengths; splits past a sequence's end
-    exit at once)."""
+    the chip, and the host does not see the lengths) and once with balanced
+    pieces (split_tokens = -1, for a caller whose batch mixes lengths: equal
+    shares of all sequences' tiles per workgroup, cut sequences merged)."""
     ctx = synth.ragged_lengths(SEED + 5, B, 1024, 8192)
     out = {}
-    for split in (0, 2048):
+    for split in (0, -1):
         wl = Workload(torch, dfl, synth, ctx=ctx, split_tokens=split)
         step_ms = timed(torch, lambda: wl.step(0), warmup=2, reps=10)
         a_ms = timed(torch, lambda: [a() for a in wl.attn], warmup=2, reps=10) / LAYERS
         a_bytes = attn_bytes(wl.lens)
-        out["serving_ragged_b64" + ("_split2048" if split else "")] = {
+        out["serving_ragged_b64" + ("_balanced" if split else "")] = {
             "cycles/s_eager": round(1000.0 / step_ms, 1), "ms_per_step_eager": round(step_ms, 4),
             "mean_ctx": round(float(np.mean(wl.lens)), 1), "attn_ms": round(a_ms, 4),
             "attn_GB/s": round(a_bytes / (a_ms * 1e-3) / 1e9, 1),
             "attn_hbm_frac": round(a_bytes / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "split_tokens": split if split else "auto (one split per sequence)"}
+            "split_tokens": "balanced pieces" if split else "auto (one split per sequence)"}
         del wl
         torch.cuda.empty_cache()
     return out

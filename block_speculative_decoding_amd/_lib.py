@@ -17,6 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("DFLASH_LIBRARY") or os.path.join(PKG, "libdflash.so")
 
 DFLASH_BF16, DFLASH_F32 = 0, 1
+SPLIT_BALANCED = -1   # dflash_attn_args.split_tokens: equal pieces of all sequences' tiles
 D, NCAPTURE, HQ, HKV, HEAD_DIM, BLOCK, PAGE, INTER = 2560, 5, 32, 8, 128, 8, 16, 5120
 
 _P = ctypes.c_void_p

@@ -77,8 +77,10 @@ int validate_attn_sizes(const char* fn, const dflash_attn_args* a) {
     if (a->page_size != DFLASH_PAGE) return fail(DFLASH_EINVAL, "%s: page_size must be 16 (got %d)", fn, a->page_size);
     if (a->block_len != DFLASH_BLOCK) return fail(DFLASH_EINVAL, "%s: block_len must be 8 (got %d)", fn, a->block_len);
     if (a->window < 0) return fail(DFLASH_EINVAL, "%s: negative window", fn);
-    if (a->split_tokens < 0 || a->split_tokens % 128 != 0 || a->split_tokens > 32768)
-        return fail(DFLASH_EINVAL, "%s: split_tokens must be 0 or a multiple of 128 up to 32768 (got %d)", fn,
+    if (a->split_tokens != DFLASH_SPLIT_BALANCED &&
+        (a->split_tokens < 0 || a->split_tokens % 128 != 0 || a->split_tokens > 32768))
+        return fail(DFLASH_EINVAL,
+                    "%s: split_tokens must be 0, DFLASH_SPLIT_BALANCED or a multiple of 128 up to 32768 (got %d)", fn,
                     a->split_tokens);
     return DFLASH_OK;
 }

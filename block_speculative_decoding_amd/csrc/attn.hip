@@ -46,6 +46,7 @@ struct AttnParams {
     const void* kc; const void* vc; int64_t num_pages;
     const int32_t* bt; int max_pages;
     const int32_t* ctx_len;
+    int B;
     int window; int split; int nsplit;
     void* out; float* lse;
     float* part;
@@ -109,20 +110,22 @@ __device__ __forceinline__ void load_row16(const T* row, int part, float* x) {
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
 
 // ---------------------------------------------------------------- bf16 MFMA kernel
-__global__ __launch_bounds__(kWgThreads, 1) void attn_bf16_kernel(AttnParams p) {
-    const int c = blockIdx.x, b = blockIdx.z;
+constexpr int kSmemFloats = kHpw * kWaves * (64 + 32 * kAccStride);
+
+// Attention of KV heads kHpw hp .. kHpw hp + kHpw - 1 of sequence b over the
+// context tokens [tb, te) (tb a multiple of the tile), plus the block's own
+// 8 keys when `last`.  part == nullptr: the result is final and goes to the
+// output (and LSE); else each head's partial (m, l, acc) goes to
+// part + head * part_stride (head within the workgroup).  Every thread of the
+// workgroup calls it with the same arguments; smem is the workgroup's
+// kSmemFloats of LDS.
+__device__ __forceinline__ void attend(const AttnParams& p, int b, int hp, const SeqRange& sr, int tb, int te,
+                                       bool last, float* part, int64_t part_stride, float* smem) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int hw = wave >> 2, wl = wave & 3;      // head within the workgroup, wave within the head
-    const int g = blockIdx.y * kHpw + hw;
-    const SeqRange sr = seq_range(p, b);
-    if (c >= sr.nspl) return;
-    const int tb = sr.a0 + c * p.split;
-    const int te = min(sr.S, tb + p.split);
-    const bool last = c == sr.nspl - 1;
+    const int g = hp * kHpw + hw;
     const int ntiles = te > tb ? (te - tb + kTile - 1) / kTile : 0;
-
-    __shared__ __attribute__((aligned(16))) float smem[kHpw * kWaves * (64 + 32 * kAccStride)];
     uint16_t* qs_all = reinterpret_cast<uint16_t*>(smem);        // [kHpw][32][kQStride]
     uint16_t* kbs_all = qs_all + kHpw * 32 * kQStride;           // [kHpw][8][kQStride]
     uint16_t* vbs_all = kbs_all + kHpw * 8 * kQStride;           // [kHpw][8][128]
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(kWgThreads, 1) void attn_bf16_kernel(AttnParams p) 
     {
         const int n = tid >> 3, part = tid & 7;  // n = hw2*32 + hh*8 + j
         const int hw2 = n >> 5, hh = (n >> 3) & 3, j = n & 7;
-        const int g2 = blockIdx.y * kHpw + hw2;
+        const int g2 = hp * kHpw + hw2;
         const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
                                ((((int64_t)b * 32 + 4 * g2 + hh) * 8 + j) * 128);
         float x[16], gw[16];
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(kWgThreads, 1) void attn_bf16_kernel(AttnParams p) 
         }
         if (tid < 64 * kHpw) {
             const int hk = tid >> 6, jj = (tid >> 3) & 7;
-            const int gk2 = blockIdx.y * kHpw + hk;
+            const int gk2 = hp * kHpw + hk;
             const uint16_t* krow = static_cast<const uint16_t*>(p.kb) + ((((int64_t)b * 8 + gk2) * 8 + jj) * 128);
             load_row16(krow, part, x);
             load_row16(gk, part, gw);
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(kWgThreads, 1) void attn_bf16_kernel(AttnParams p) 
             const int t2 = tid - 64 * kHpw;  // 128 threads x 16 B = the 2 KiB of v_blk (8 x 128 bf16) per head
             const int hv = t2 >> 7;
             const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.vb) +
-                                                              (((int64_t)b * 8 + blockIdx.y * kHpw + hv) * 8 * 128));
+                                                              (((int64_t)b * 8 + hp * kHpw + hv) * 8 * 128));
             reinterpret_cast<uint4*>(vbs_all + hv * 8 * 128)[t2 & 127] = src[t2 & 127];
         }
     }
@@ -347,7 +350,7 @@ __global__ __launch_bounds__(kWgThreads, 1) void attn_bf16_kernel(AttnParams p) 
     __syncthreads();
 
     // Threads [256 h, 256 h + 256) merge head h's four waves.
-    const int hm = tid >> 8, gm = blockIdx.y * kHpw + hm;
+    const int hm = tid >> 8, gm = hp * kHpw + hm;
     const int n = (tid & 255) >> 3, d0 = 16 * (tid & 7);
     const float* wbase = smem + hm * kWaves * (64 + 32 * kAccStride);
     float M = -INFINITY;
@@ -370,7 +373,7 @@ __global__ __launch_bounds__(kWgThreads, 1) void attn_bf16_kernel(AttnParams p) 
             o[4 * e4 + 2] += f * v.z; o[4 * e4 + 3] += f * v.w;
         }
     }
-    if (sr.nspl == 1) {
+    if (part == nullptr) {
         const float inv = 1.0f / L;
         uint16_t* orow = static_cast<uint16_t*>(p.out) + ((((int64_t)b * 32 + 4 * gm + (n >> 3)) * 8 + (n & 7)) * 128) + d0;
         uint4 w0, w1;
@@ -383,7 +386,7 @@ __global__ __launch_bounds__(kWgThreads, 1) void attn_bf16_kernel(AttnParams p) 
         if (p.lse && (tid & 7) == 0)
             p.lse[((int64_t)b * 32 + 4 * gm + (n >> 3)) * 8 + (n & 7)] = (Mu + log2f(L)) * kLn2;
     } else {
-        float* pp = p.part + (((int64_t)b * 8 + gm) * p.nsplit + c) * kPartFloats;
+        float* pp = part + hm * part_stride;
         if ((tid & 7) == 0) { pp[n] = M; pp[32 + n] = L; }
         float4* dst = reinterpret_cast<float4*>(pp + 64 + n * 128 + d0);
 #pragma unroll
@@ -392,31 +395,132 @@ __global__ __launch_bounds__(kWgThreads, 1) void attn_bf16_kernel(AttnParams p) 
     }
 }
 
+// Fixed splits: workgroup (split c, KV-head pair hp, sequence b) takes tokens
+// [a0 + c split, a0 + (c + 1) split) of its sequence; the last split also
+// takes the block's keys.  With several splits each writes its partial.
+__global__ __launch_bounds__(kWgThreads, 1) void attn_bf16_kernel(AttnParams p) {
+    const int c = blockIdx.x, hp = blockIdx.y, b = blockIdx.z;
+    const SeqRange sr = seq_range(p, b);
+    if (c >= sr.nspl) return;
+    const int tb = sr.a0 + c * p.split;
+    const int te = min(sr.S, tb + p.split);
+    __shared__ __attribute__((aligned(16))) float smem[kSmemFloats];
+    float* part = sr.nspl == 1 ? nullptr : p.part + (((int64_t)b * 8 + hp * kHpw) * p.nsplit + c) * kPartFloats;
+    attend(p, b, hp, sr, tb, te, c == sr.nspl - 1, part, (int64_t)p.nsplit * kPartFloats, smem);
+}
+
+// ---------------------------------------------------------------- balanced pieces
+// Balanced mode: the context tiles of all sequences, each followed by its
+// block tile, are laid end to end and cut into kPieces equal pieces per
+// KV-head pair; workgroup (piece, hp) walks the sequence segments of its
+// piece.  A segment holding a whole sequence writes the output; a sequence
+// cut by a piece boundary leaves one partial per piece it touches, in slot 0
+// of a piece whose first sequence it is, else slot 1 (only a piece's last
+// segment can be cut and not be its first), and the merge combines them.
+// Workgroup (0, 0) also writes the merge table after the partials: entry b =
+// P0 | P1 << 8 | slot << 16 (the pieces sequence b touches, and the slot of
+// its partial in P0), entry B = the tile total.
+constexpr int kPieces = 64;             // pieces per KV-head pair: 4 x 64 workgroups, one per CU
+constexpr int kMaxBalancedB = 1024;
+constexpr size_t kBalancedPartFloats = (size_t)kPieces * 2 * 8 * kPartFloats;   // merge table after these
+
+// Tiles of a sequence: its context tiles, then the block tile.
+__device__ __forceinline__ int seq_tiles(const SeqRange& sr) {
+    return (sr.S > sr.a0 ? (sr.S - sr.a0 + kTile - 1) / kTile : 0) + 1;
+}
+
+// s_pref[b] = first global tile of sequence b, s_pref[B] = all tiles (the
+// return value); every thread of the workgroup takes part.
+__device__ int tile_prefix(const AttnParams& p, int* s_pref, int* s_tmp) {
+    const int nt = blockDim.x, tid = threadIdx.x;
+    const int per = (p.B + nt - 1) / nt;
+    const int b0 = tid * per;
+    int sum = 0;
+    for (int i = 0; i < per; ++i)
+        if (b0 + i < p.B) sum += seq_tiles(seq_range(p, b0 + i));
+    s_tmp[tid] = sum;
+    __syncthreads();
+    for (int o = 1; o < nt; o <<= 1) {   // inclusive scan over the threads' sums
+        const int v = tid >= o ? s_tmp[tid - o] : 0;
+        __syncthreads();
+        s_tmp[tid] += v;
+        __syncthreads();
+    }
+    int run = s_tmp[tid] - sum;
+    for (int i = 0; i < per; ++i)
+        if (b0 + i < p.B) {
+            s_pref[b0 + i] = run;
+            run += seq_tiles(seq_range(p, b0 + i));
+        }
+    if (tid == nt - 1) s_pref[p.B] = s_tmp[nt - 1];
+    __syncthreads();
+    return s_pref[p.B];
+}
+
+__device__ __forceinline__ int piece_lo(int piece, int TT) { return (int)((int64_t)piece * TT / kPieces); }
+// The piece holding global tile t: the last one that starts at or before t.
+__device__ __forceinline__ int piece_of(int t, int TT) {
+    return min(kPieces - 1, (int)(((int64_t)(t + 1) * kPieces - 1) / TT));
+}
+
+__global__ __launch_bounds__(kWgThreads, 1) void attn_bf16_balanced_kernel(AttnParams p) {
+    const int piece = blockIdx.x, hp = blockIdx.y;
+    __shared__ __attribute__((aligned(16))) float smem[kSmemFloats];
+    __shared__ int s_pref[kMaxBalancedB + 1];
+    __shared__ int s_tmp[kWgThreads];
+    const int TT = tile_prefix(p, s_pref, s_tmp);
+    if (piece == 0 && hp == 0) {
+        int* table = reinterpret_cast<int*>(p.part + kBalancedPartFloats);
+        for (int b = threadIdx.x; b < p.B; b += blockDim.x) {
+            const int t0 = s_pref[b], P0 = piece_of(t0, TT), P1 = piece_of(s_pref[b + 1] - 1, TT);
+            table[b] = P0 | (P1 << 8) | ((piece_lo(P0, TT) == t0 ? 0 : 1) << 16);
+        }
+        if (threadIdx.x == 0) table[p.B] = TT;
+    }
+    const int lo = piece_lo(piece, TT), hi = piece_lo(piece + 1, TT);
+    if (lo >= hi) return;
+    int first = 0, top = p.B - 1;   // the sequence holding tile lo: last b with s_pref[b] <= lo
+    while (first < top) {
+        const int mid = (first + top + 1) >> 1;
+        if (s_pref[mid] <= lo) first = mid;
+        else top = mid - 1;
+    }
+    for (int b = first; b < p.B && s_pref[b] < hi; ++b) {
+        const SeqRange sr = seq_range(p, b);
+        const int nt = seq_tiles(sr) - 1;   // context tiles; the block tile is local tile nt
+        const int g0 = max(lo, s_pref[b]) - s_pref[b], g1 = min(hi, s_pref[b + 1]) - s_pref[b];
+        const int tb = sr.a0 + kTile * g0;
+        const int te = min(sr.S, sr.a0 + kTile * min(g1, nt));
+        const bool last = g1 > nt;
+        float* part = g0 == 0 && last ? nullptr
+                                      : p.part + (((int64_t)piece * 2 + (b == first ? 0 : 1)) * 8 + hp * kHpw) * kPartFloats;
+        __syncthreads();   // the previous segment is done with the LDS
+        attend(p, b, hp, sr, tb, te, last, part, kPartFloats, smem);
+    }
+}
+
 // ---------------------------------------------------------------- split merge
 // One workgroup per (KV head g, sequence b, quarter of the 32 query rows):
-// thread (row n, 4 dims) reads one float4 of each split's partial.  The
-// splits are taken kMergeU at a time with every load of a batch issued
-// before any is used, and batches combine online (running maximum M in log2
-// units, sum L and the weighted outputs rescaled when M grows).
+// thread (row n, 4 dims) reads one float4 of each of the count partials
+// (at(i), i < count; a null at(i) holds nothing).  They are taken kMergeU at a time with every load of a
+// batch issued before any is used, and batches combine online (running
+// maximum M in log2 units, sum L and the weighted outputs rescaled when M
+// grows).
 constexpr int kMergeU = 16;
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnParams p) {
-    const int g = blockIdx.x, b = blockIdx.y, rq = blockIdx.z;
-    const SeqRange sr = seq_range(p, b);
-    if (sr.nspl <= 1) return;
+template <typename T, typename PartAt>
+__device__ __forceinline__ void merge_rows(const AttnParams& p, int g, int b, int rq, int count, PartAt at) {
     const int tid = threadIdx.x;
     const int n = 8 * rq + (tid >> 5), d0 = 4 * (tid & 31);
-    const float* base = p.part + ((int64_t)b * 8 + g) * p.nsplit * kPartFloats;
     float M = -INFINITY, L = 0.f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int c0 = 0; c0 < sr.nspl; c0 += kMergeU) {
+    for (int c0 = 0; c0 < count; c0 += kMergeU) {
         float mc[kMergeU], lc[kMergeU];
         float4 ac[kMergeU];
 #pragma unroll
         for (int u = 0; u < kMergeU; ++u) {
-            if (c0 + u < sr.nspl) {
-                const float* pc = base + (int64_t)(c0 + u) * kPartFloats;
+            const float* pc = c0 + u < count ? at(c0 + u) : nullptr;
+            if (pc) {
                 mc[u] = pc[n];
                 lc[u] = pc[32 + n];
                 ac[u] = *reinterpret_cast<const float4*>(pc + 64 + n * 128 + d0);
@@ -450,6 +554,34 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnParams p) {
     Elem<T>::store(orow, 3, o.w * inv);
     if (p.lse && (tid & 31) == 0)
         p.lse[((int64_t)b * 32 + 4 * g + (n >> 3)) * 8 + (n & 7)] = (Mu + log2f(L)) * kLn2;
+}
+
+// Fixed splits: partial c of (b, g) at ((b * 8 + g) * nsplit + c) * kPartFloats.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnParams p) {
+    const int g = blockIdx.x, b = blockIdx.y, rq = blockIdx.z;
+    const SeqRange sr = seq_range(p, b);
+    if (sr.nspl <= 1) return;
+    const float* base = p.part + ((int64_t)b * 8 + g) * p.nsplit * kPartFloats;
+    merge_rows<T>(p, g, b, rq, sr.nspl, [&](int c) { return base + (int64_t)c * kPartFloats; });
+}
+
+// Balanced pieces: sequence b's partials in the pieces P0 .. P1 it touches.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void attn_merge_balanced_kernel(AttnParams p) {
+    const int g = blockIdx.x, b = blockIdx.y, rq = blockIdx.z;
+    const int* table = reinterpret_cast<const int*>(p.part + kBalancedPartFloats);
+    const int e = table[b];
+    const int P0 = e & 0xFF, P1 = (e >> 8) & 0xFF, slot0 = e >> 16;
+    if (P0 == P1) return;   // whole in one piece: written by the attention kernel
+    const int TT = table[p.B];
+    // With fewer tiles than pieces, pieces between P0 and P1 can be empty:
+    // they wrote no partial.
+    merge_rows<T>(p, g, b, rq, P1 - P0 + 1, [&](int i) -> const float* {
+        const int piece = P0 + i;
+        if (piece_lo(piece, TT) >= piece_lo(piece + 1, TT)) return nullptr;
+        return p.part + (((int64_t)piece * 2 + (i == 0 ? slot0 : 0)) * 8 + g) * kPartFloats;
+    });
 }
 
 // ---------------------------------------------------------------- fp32 VALU kernel
@@ -624,6 +756,20 @@ AttnPlan attn_plan(const dflash_attn_args& a) {
         pl.ws_bytes = 0;
         return pl;
     }
+    pl.balanced = false;
+    if (a.split_tokens == DFLASH_SPLIT_BALANCED) {
+        // Balanced pieces, while every piece fits the page-id staging of one
+        // split (a piece spans at most its share of the tiles, plus one).
+        const int64_t tiles = (int64_t)a.B * (cap / kTile + 2);
+        const int64_t piece_tokens = (tiles / kPieces + 2) * kTile;
+        if (a.B <= kMaxBalancedB && piece_tokens <= kMaxSplit) {
+            pl.balanced = true;
+            pl.split_tokens = 0;
+            pl.nsplit = 1;
+            pl.ws_bytes = kBalancedPartFloats * sizeof(float) + ((size_t)a.B + 1) * sizeof(int);
+            return pl;
+        }
+    }
     int split;
     if (a.split_tokens > 0) {
         split = a.split_tokens;
@@ -652,13 +798,18 @@ hipError_t launch_attn(const dflash_attn_args& a, const AttnPlan& pl, void* ws, 
     p.q = a.q; p.kb = a.k_blk; p.vb = a.v_blk; p.gq = a.gq; p.gk = a.gk;
     p.eps = a.eps; p.theta = a.rope_theta;
     p.kc = a.k_cache; p.vc = a.v_cache; p.num_pages = a.num_pages;
-    p.bt = a.block_table; p.max_pages = a.max_pages; p.ctx_len = a.ctx_len;
+    p.bt = a.block_table; p.max_pages = a.max_pages; p.ctx_len = a.ctx_len; p.B = a.B;
     p.window = a.window; p.split = pl.split_tokens > 0 ? pl.split_tokens : (1 << 30); p.nsplit = pl.nsplit;
     p.out = a.out; p.lse = a.lse_out;
     p.part = static_cast<float*>(ws);
     for (int i = 0; i < 64; ++i) p.inv_freq[i] = std::pow((double)a.rope_theta, -(double)i / 64.0);
     if (a.dtype == DFLASH_F32) {
         attn_f32_kernel<<<dim3(8, a.B), kThreads, 0, s>>>(p);
+        return hipGetLastError();
+    }
+    if (pl.balanced) {
+        attn_bf16_balanced_kernel<<<dim3(kPieces, 8 / kHpw), kWgThreads, 0, s>>>(p);
+        attn_merge_balanced_kernel<uint16_t><<<dim3(8, a.B, 4), kThreads, 0, s>>>(p);
         return hipGetLastError();
     }
     attn_bf16_kernel<<<dim3(pl.nsplit, 8 / kHpw, a.B), kWgThreads, 0, s>>>(p);

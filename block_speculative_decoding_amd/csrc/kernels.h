@@ -21,6 +21,7 @@ hipError_t verify_scratch(void** ptr);
 struct AttnPlan {
     int split_tokens;  // tokens per split-K chunk (multiple of 128)
     int nsplit;        // chunks per (sequence, kv head) in the grid
+    bool balanced;     // equal pieces of all sequences' tiles (DFLASH_SPLIT_BALANCED)
     size_t ws_bytes;
 };
 AttnPlan attn_plan(const dflash_attn_args& a);

@@ -101,7 +101,16 @@ extern "C" {
 #define DFLASH_MAX_LAYERS 5      /* draft layers */
 #define DFLASH_INTER      5120   /* SwiGLU width (derived from the parameter count) */
 
-#define DFLASH_VERSION 10300     /* 1.3.0 */
+#define DFLASH_VERSION 10400     /* 1.4.0 */
+
+/* dflash_attn_args.split_tokens: cut the context tiles of all sequences,
+ * laid end to end (each sequence's 32-token tiles, then its block's keys as
+ * one more tile), into equal pieces per pair of KV heads, one workgroup each,
+ * and merge the sequences a piece boundary cuts.  For batches whose context
+ * lengths differ (the split by sequence waits for the longest).  Falls back to
+ * the automatic split when B > 1024 or a piece could exceed 32768 tokens
+ * (B * (max_pages * 16 or window) / 64, roughly). */
+#define DFLASH_SPLIT_BALANCED (-1)
 
 /*
  * dflash_ctx_fuse -- context fusion and K/V injection.
@@ -175,7 +184,8 @@ typedef struct dflash_attn_args {
     int32_t page_size;        /* must be 16 */
     int32_t block_len;        /* must be 8 */
     int32_t window;           /* 0 = full context; > 0 = latest `window` tokens */
-    int32_t split_tokens;     /* 0 = automatic; else tokens per split-K chunk, multiple of 128, <= 32768 */
+    int32_t split_tokens;     /* 0 = automatic; DFLASH_SPLIT_BALANCED; else tokens per split-K chunk,
+                                 multiple of 128, <= 32768 */
     void* out;                /* device [B][32][8][128] (dtype) */
     float* lse_out;           /* optional device [B][32][8] natural-log LSE; NULL = not written */
 } dflash_attn_args;

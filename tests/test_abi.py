@@ -55,7 +55,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_struct_sizes_and_version(lib):
     from block_speculative_decoding_amd import _lib
-    assert lib.dflash_version() == 10300
+    assert lib.dflash_version() == 10400
     for kind, st in enumerate(_lib.ARG_STRUCTS):
         assert lib.dflash_args_size(kind) == ctypes.sizeof(st)
     assert lib.dflash_args_size(len(_lib.ARG_STRUCTS)) == 0
@@ -188,6 +188,17 @@ def test_attn_validation(lib):
     assert sizes == sorted(sizes)
     # fp32 path needs no workspace
     assert _ws(lib, "attn", _attn_args(dtype=1, max_pages=1000))[1] == 0
+    # Balanced pieces (split_tokens = -1): 64 pieces x 2 slots x 8 KV heads of
+    # (m[32], l[32], acc[32][128]) fp32 partials, then B + 1 ints of merge
+    # table; -2 is not a mode.
+    kpart = (64 + 32 * 128) * 4
+    assert _ws(lib, "attn", _attn_args(B=64, max_pages=513, split_tokens=-1)) == (0, 64 * 2 * 8 * kpart + 65 * 4)
+    assert _ws(lib, "attn", _attn_args(split_tokens=-2))[0] == -1
+    # Beyond 1024 sequences, or where a piece could pass 32768 tokens, the
+    # automatic split takes over (one split per sequence here: no workspace).
+    assert _ws(lib, "attn", _attn_args(B=1025, max_pages=8, split_tokens=-1)) == (0, 0)
+    assert _ws(lib, "attn", _attn_args(B=1024, max_pages=8192, split_tokens=-1)) == \
+        _ws(lib, "attn", _attn_args(B=1024, max_pages=8192, split_tokens=0))
 
 
 def test_fuse_validation(lib):

@@ -44,7 +44,10 @@ def _case(ctx_lens, dtype, seed, window=0, split=0, spare=3):
     return exact(out), exact(lse), ref, ref_lse
 
 
-@pytest.mark.parametrize("split", [0, 128, 256])
+BALANCED = -1   # DFLASH_SPLIT_BALANCED
+
+
+@pytest.mark.parametrize("split", [0, 128, 256, BALANCED])
 def test_attn_bf16_ragged_paged(split):
     lens = [0, 1, 37, 300, 129]
     note(f"attn bf16 lens={lens} split={split}")
@@ -56,7 +59,7 @@ def test_attn_bf16_ragged_paged(split):
     assert np.max(np.abs(lse - ref_lse)) <= 2e-2
 
 
-@pytest.mark.parametrize("split", [0, 128])
+@pytest.mark.parametrize("split", [0, 128, BALANCED])
 def test_attn_bf16_window(split):
     lens = [100, 1500, 1024, 1041]
     note(f"attn bf16 window=1024 lens={lens} split={split}")
@@ -88,7 +91,22 @@ def test_attn_bf16_single_stream_4096():
     assert err <= TOL[BF16]
 
 
-def _big_case(B, S, seed, check, n_new=None):
+def test_attn_bf16_balanced_ragged_batch():
+    """Balanced pieces over 20 sequences of 1..3000 cached tokens (about 800
+    tiles in 64 pieces per KV-head pair): pieces span several sequences, and
+    sequences are cut by one or more piece boundaries."""
+    lens = [int(x) for x in np.random.default_rng(21).integers(1, 3000, 20)]
+    lens[3], lens[11] = 0, 2999
+    note(f"attn bf16 balanced lens={lens}")
+    out, lse, ref, ref_lse = _case(lens, BF16, 21, split=BALANCED)
+    assert np.all(np.isfinite(out))
+    err = np.max(np.abs(out - ref))
+    note(f"  max abs err {err:.3e}")
+    assert err <= TOL[BF16]
+    assert np.max(np.abs(lse - ref_lse)) <= 2e-2
+
+
+def _big_case(B, S, seed, check, n_new=None, split=0):
     """Full-size serving / long-context layer: caches filled on the device
     with N(0,1) bf16 (i.i.d., so layout-agnostic); sampled sequences are read
     back through the documented layout and checked against the oracle."""
@@ -100,7 +118,8 @@ def _big_case(B, S, seed, check, n_new=None):
     vc = torch.randn((npages, 8, 2048), generator=gen, device="cuda", dtype=torch.float32).to(BF16)
     blk = synth.attn_block(seed, B)
     q, kb, vb, gq, gk = (dev(blk[n], BF16) for n in ("q", "k_blk", "v_blk", "gq", "gk"))
-    out = dfl.block_attn(q, kb, vb, gq, gk, kc, vc, dev(table, torch.int32), dev(lens, torch.int32))
+    out = dfl.block_attn(q, kb, vb, gq, gk, kc, vc, dev(table, torch.int32), dev(lens, torch.int32),
+                         split_tokens=split)
     torch.cuda.synchronize()
     out_h = exact(out)
     assert np.all(np.isfinite(out_h))
@@ -131,4 +150,18 @@ def test_attn_long_context_full_size():
     """B=4, S=131072: split-K with many chunks and the LSE merge."""
     err = _big_case(4, 131072, 3, check=[1])
     note(f"attn long context B=4 S=131072 sampled max abs err {err:.3e}")
+    assert err <= TOL[BF16]
+
+
+@pytest.mark.parametrize("shape", ["serving_ragged", "long_context"])
+def test_attn_balanced_full_size(shape):
+    """Balanced pieces at full size: the serving batch with ragged contexts
+    (B = 64, 1024..8192 cached tokens, pieces cutting most sequences) and the
+    long context (B = 4, S = 131072: every sequence spread over 16 pieces)."""
+    if shape == "serving_ragged":
+        n_new = synth.ragged_lengths(7, 64, 1024, 8192) - 8192
+        err = _big_case(64, 8192, 7, check=[0, 17, 40, 63], n_new=n_new, split=BALANCED)
+    else:
+        err = _big_case(4, 131072, 8, check=[2], split=BALANCED)
+    note(f"attn balanced {shape} sampled max abs err {err:.3e}")
     assert err <= TOL[BF16]

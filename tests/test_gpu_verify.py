@@ -214,3 +214,52 @@ def test_verify_with_draft_stats_input(dtype):
     excl = compare_verify(toks.cpu().numpy(), lens.cpu().numpy(), tr)
     assert excl <= 2
     assert int(nt.item()) == tr.near_ties
+
+
+def test_verify_sampler_statistics_tiny_vocab():
+    """The GPU sampler's own statistics, independent of the oracle's draws.
+
+    8192 sequences share one fp32 (target, draft) logit pair at T = 1 and
+    V = 64, and each draws its proposals d_k ~ q_k with numpy.  The accepted
+    prefix length must follow the closed form P(n) = beta_1 ... beta_n
+    (1 - beta_{n+1}), with beta_k = sum_x min(p_{k-1}(x), q_k(x)).  The
+    first emitted token must follow p_0 (accepted d_1 or correction).  Where
+    d_1 is rejected, the correction must follow max(0, p_0 - q_1)
+    normalised.  Each is a chi-square test at p > 1e-4 on fixed seeds."""
+    from scipy.stats import chisquare
+    import block_speculative_decoding_amd as dfl
+    B, V = 8192, 64
+    rng = np.random.default_rng(404)
+    zt1 = 1.5 * rng.standard_normal((8, V))
+    zd1 = zt1[:7] + rng.standard_normal((7, V))
+    zt1, zd1 = zt1.astype(np.float32), zd1.astype(np.float32)
+    sm = lambda z: np.exp(z - z.max(-1, keepdims=True)) / np.exp(z - z.max(-1, keepdims=True)).sum(-1, keepdims=True)
+    p, q = sm(zt1.astype(np.float64)), sm(zd1.astype(np.float64))
+    d = np.stack([rng.choice(V, size=B, p=q[k]) for k in range(7)], axis=1).astype(np.int32)
+    zt = np.broadcast_to(zt1, (B, 8, V)).copy()
+    zd = np.broadcast_to(zd1, (B, 7, V)).copy()
+    note(f"verify sampler statistics B={B} V={V}")
+    toks, lens, _ = dfl.spec_verify(dev(zt, F32), dev(zd, F32), dev(d, torch.int32),
+                                    torch.ones(B, dtype=torch.float32, device="cuda"), seed=77, offset=5)
+    torch.cuda.synchronize()
+    toks, lens = toks.cpu().numpy(), lens.cpu().numpy()
+
+    def chi2(observed, expected):
+        # Bins expected below 5 are pooled.
+        small = expected < 5
+        obs = np.append(observed[~small], observed[small].sum())
+        exp_ = np.append(expected[~small], expected[small].sum())
+        keep = exp_ > 0
+        return chisquare(obs[keep], exp_[keep] * obs[keep].sum() / exp_[keep].sum()).pvalue
+
+    beta = np.array([np.minimum(p[k], q[k]).sum() for k in range(7)])
+    law = np.array([np.prod(beta[:n]) * (1 - beta[n]) for n in range(7)] + [np.prod(beta)])
+    p_len = chi2(np.bincount(lens - 1, minlength=8).astype(float), B * law)
+    p_first = chi2(np.bincount(toks[:, 0], minlength=V).astype(float), B * p[0])
+    rej = lens == 1
+    resid = np.maximum(p[0] - q[0], 0.0)
+    p_resid = chi2(np.bincount(toks[rej, 0], minlength=V).astype(float), rej.sum() * resid / resid.sum())
+    note(f"  beta={np.round(beta, 3)} p(len)={p_len:.3g} p(first)={p_first:.3g} "
+         f"p(correction)={p_resid:.3g} ({rej.sum()} rejections at k=1)")
+    assert np.all((lens >= 1) & (lens <= 8))
+    assert p_len > 1e-4 and p_first > 1e-4 and p_resid > 1e-4

@@ -352,7 +352,7 @@ def test_draft_paths_validation(lib):
             setattr(a, k, v)
         return a
     rc, n = _ws(lib, "draft_paths", args())
-    assert rc == 0 and n == 64 * 7 * 64 * 80          # one 80-byte partial per 4096 entries of a row (one per wave)
+    assert rc == 0 and n == 64 * 7 * 32 * 80          # one 80-byte partial per 8192 entries of a row (one per wave)
     assert _ws(lib, "draft_paths", args(m=0))[0] == -1
     assert _ws(lib, "draft_paths", args(m=9))[0] == -1
     assert _ws(lib, "draft_paths", args(P=65))[0] == -1

@@ -546,7 +546,7 @@ def measured_peaks(torch, dfl):
     dev = torch.device("cuda:0")
     sink = dfl.calib_sink(dev)
     x = torch.empty(1 << 32, dtype=torch.uint8, device=dev).random_()
-    grids = (1024, 2048, 4096, 8192, 16384)
+    grids = (256, 512, 1024, 2048, 4096, 8192, 16384)
     r_all = {gd: timed(torch, lambda: dfl.calib_stream(x, sink, grid=gd), warmup=2, reps=5) for gd in grids}
     r_grid = min(r_all, key=r_all.get)
     r_ms = r_all[r_grid]

@@ -538,7 +538,8 @@ def config_measurements(torch, dfl, synth):
 def measured_peaks(torch, dfl):
     """Practical ceilings of the part measured in the same run with the
     library's calibration kernels (dflash_calib_*): a streaming read of
-    4 GiB with 16-byte loads, a 2 GiB copy (read + write bytes), and a
+    4 GiB with 16-byte loads, the same 4 GiB gathered as randomly ordered
+    8-KiB or 32-KiB chunks, a 2 GiB copy (read + write bytes), and a
     register-only bf16 MFMA loop; for reference also torch's bf16 matmul
     8192^3 (hipBLASLt, N(0, 1) operands).  The roofline fractions stay
     against the datasheet peaks; these say how much of them the part
@@ -550,6 +551,16 @@ def measured_peaks(torch, dfl):
     r_all = {gd: timed(torch, lambda: dfl.calib_stream(x, sink, grid=gd), warmup=2, reps=5) for gd in grids}
     r_grid = min(r_all, key=r_all.get)
     r_ms = r_all[r_grid]
+    # The same 4 GiB read as chunks in a random order: the access pattern of
+    # shuffled cache pages (attention reads 8-KiB runs of 32-KiB pages).
+    gen = torch.Generator(device=dev).manual_seed(SEED)
+    gather = {}
+    for cb in (8192, 32768):
+        ids = torch.randperm((1 << 32) // cb, generator=gen, device=dev).to(torch.int32)
+        best = min(timed(torch, lambda: dfl.calib_gather(x, ids, cb, sink, grid=gd), warmup=2, reps=5)
+                   for gd in (256, 1024, 2048, 4096))
+        gather[f"{cb // 1024}KiB"] = round((1 << 32) / (best * 1e-3) / 1e9, 1)
+        del ids
     src = x[: 1 << 31]
     dst = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
     c_ms = timed(torch, lambda: dfl.calib_stream(src, sink, dst=dst, grid=r_grid), warmup=3, reps=10)
@@ -566,11 +577,13 @@ def measured_peaks(torch, dfl):
     mfma = flops / (f_ms * 1e-3) / 1e12
     return {"read_GB/s": round(read, 1), "read_frac_of_datasheet": round(read / HBM_PEAK_GBS, 4),
             "read_grid_sweep_GB/s": {str(gd): round((1 << 32) / (ms * 1e-3) / 1e9, 1) for gd, ms in r_all.items()},
+            "gather_random_chunks_GB/s": gather,
             "copy_GB/s": round(2 * (1 << 31) / (c_ms * 1e-3) / 1e9, 1),
             "mfma_loop_TFLOP/s": round(mfma, 1), "mfma_loop_frac_of_datasheet": round(mfma / MFMA_BF16_PEAK_TFLOPS, 4),
             "torch_matmul_bf16_TFLOP/s": round(2 * 8192 ** 3 / (m_ms * 1e-3) / 1e12, 1),
             "how": ("dflash_calib_stream over 4 GiB (read; best of a grid sweep) and 2 GiB (copy, read+write "
-                    "bytes); dflash_calib_mfma "
+                    "bytes); dflash_calib_gather over the same 4 GiB as 8-KiB or 32-KiB chunks in a random order "
+                    "(best of 256-4096 workgroups); dflash_calib_mfma "
                     f"({iters} rounds of 8 bf16 32x32x16 MFMAs per wave, 2 waves per SIMD); torch.matmul bf16 "
                     "8192^3")}
 

@@ -11,7 +11,7 @@ from ._lib import (DFlashError, load, ctx_fuse, block_attn, spec_verify,
                    draft_embed, draft_qkv, draft_mlp,
                    prepare_draft_embed, prepare_draft_qkv, prepare_draft_mlp,
                    ring_append, prepare_ring_append, draft_head, prepare_draft_head,
-                   draft_paths, prepare_draft_paths, calib_sink, calib_stream, calib_mfma, EXPORTS)
+                   draft_paths, prepare_draft_paths, calib_sink, calib_stream, calib_gather, calib_mfma, EXPORTS)
 
 __all__ = ["DFlashError", "load", "ctx_fuse", "block_attn", "spec_verify",
            "prepare_ctx_fuse", "prepare_block_attn", "prepare_spec_verify",
@@ -19,4 +19,4 @@ __all__ = ["DFlashError", "load", "ctx_fuse", "block_attn", "spec_verify",
            "draft_embed", "draft_qkv", "draft_mlp",
            "prepare_draft_embed", "prepare_draft_qkv", "prepare_draft_mlp",
            "ring_append", "prepare_ring_append", "draft_head", "prepare_draft_head",
-           "draft_paths", "prepare_draft_paths", "calib_sink", "calib_stream", "calib_mfma", "EXPORTS"]
+           "draft_paths", "prepare_draft_paths", "calib_sink", "calib_stream", "calib_gather", "calib_mfma", "EXPORTS"]

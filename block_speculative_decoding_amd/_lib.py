@@ -103,7 +103,7 @@ EXPORTS = ["dflash_version", "dflash_last_error", "dflash_args_size",
            "dflash_spec_verify_noalloc", "dflash_verify_scratch_bytes",
            "dflash_draft_embed", "dflash_draft_qkv", "dflash_draft_mlp", "dflash_ring_append",
            "dflash_draft_head", "dflash_draft_paths",
-           "dflash_calib_sink_bytes", "dflash_calib_stream", "dflash_calib_mfma"]
+           "dflash_calib_sink_bytes", "dflash_calib_stream", "dflash_calib_gather", "dflash_calib_mfma"]
 
 _lib = None
 
@@ -141,6 +141,8 @@ def load():
     lib.dflash_calib_sink_bytes.argtypes = [ctypes.POINTER(ctypes.c_size_t)]
     lib.dflash_calib_stream.restype = ctypes.c_int
     lib.dflash_calib_stream.argtypes = [_P, _P, ctypes.c_size_t, ctypes.c_int, _P, _P]
+    lib.dflash_calib_gather.restype = ctypes.c_int
+    lib.dflash_calib_gather.argtypes = [_P, ctypes.c_size_t, _P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _P, _P]
     lib.dflash_calib_mfma.restype = ctypes.c_int
     lib.dflash_calib_mfma.argtypes = [ctypes.c_int, _P, ctypes.POINTER(ctypes.c_double), _P]
     lib.dflash_draft_embed.restype = ctypes.c_int
@@ -747,6 +749,18 @@ def calib_stream(src, sink, dst=None, grid=0, stream=None):
     nbytes = src.numel() * src.element_size()
     _check(load().dflash_calib_stream(_ptr(src), _ptr(dst), nbytes, int(grid), _ptr(sink), _stream(stream)))
     return nbytes
+
+
+def calib_gather(src, chunk_ids, chunk_bytes, sink, grid=0, stream=None):
+    """Read the chunk_bytes-sized chunks of src listed in chunk_ids (device
+    int32) in that order over `grid` workgroups (0: the default); returns
+    nchunks x chunk_bytes."""
+    nbytes = src.numel() * src.element_size()
+    if chunk_ids.dtype != torch.int32 or not chunk_ids.is_contiguous():
+        raise DFlashError("calib_gather: chunk_ids must be contiguous int32")
+    _check(load().dflash_calib_gather(_ptr(src), nbytes, _ptr(chunk_ids), chunk_ids.numel(), int(chunk_bytes),
+                                      int(grid), _ptr(sink), _stream(stream)))
+    return chunk_ids.numel() * int(chunk_bytes)
 
 
 def calib_mfma(iters, sink, stream=None):

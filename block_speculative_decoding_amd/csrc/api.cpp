@@ -462,6 +462,24 @@ int dflash_calib_stream(const void* src, void* dst, size_t bytes, int grid, void
     return launched(fn, dflash::launch_calib_stream(src, dst, bytes, grid, sink, static_cast<hipStream_t>(stream)));
 }
 
+int dflash_calib_gather(const void* src, size_t bytes, const int32_t* chunk_ids, int64_t nchunks, int chunk_bytes,
+                        int grid, void* sink, void* stream) {
+    const char* fn = "dflash_calib_gather";
+    REQUIRE_PTR(src);
+    REQUIRE_PTR(chunk_ids);
+    REQUIRE_PTR(sink);
+    if (!aligned16(src)) return fail(DFLASH_EINVAL, "%s: src is not 16-byte aligned", fn);
+    if (bytes == 0 || bytes % 16 != 0) return fail(DFLASH_EINVAL, "%s: bytes must be a positive multiple of 16", fn);
+    if (chunk_bytes < 4096 || chunk_bytes > (1 << 20) || chunk_bytes % 4096 != 0)
+        return fail(DFLASH_EINVAL, "%s: chunk_bytes %d must be a multiple of 4096 in [4096, 2^20]", fn, chunk_bytes);
+    if (nchunks < 1 || nchunks > ((int64_t)1 << 31) / (chunk_bytes / 4096))
+        return fail(DFLASH_EINVAL, "%s: nchunks %lld outside [1, 2^31 / (chunk_bytes / 4096)]", fn, (long long)nchunks);
+    if (grid < 0 || grid > dflash::calib_stream_max_grid())
+        return fail(DFLASH_EINVAL, "%s: grid %d outside [0, %d]", fn, grid, dflash::calib_stream_max_grid());
+    return launched(fn, dflash::launch_calib_gather(src, bytes, chunk_ids, nchunks, chunk_bytes, grid, sink,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 int dflash_calib_mfma(int iters, void* sink, double* flops, void* stream) {
     const char* fn = "dflash_calib_mfma";
     REQUIRE_PTR(sink);

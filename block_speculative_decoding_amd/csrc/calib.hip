@@ -8,6 +8,10 @@
 //                   per-workgroup xor of the data goes to a sink so the
 //                   loads are not dead.
 //   stream_copy  -- the same loads, each stored to a second buffer.
+//   gather_read  -- chunks of a buffer read in the order of a list of chunk
+//                   ids (a random permutation gives the page-like pattern of
+//                   the paged KV cache), 4-KiB pieces, eight in flight per
+//                   thread; ids outside the buffer read nothing.
 //   mfma_loop    -- bf16 32x32x16 matrix instructions on register operands
 //                   only (no memory in the loop), eight independent
 //                   accumulators per wave, two waves per SIMD.
@@ -43,6 +47,47 @@ __global__ __launch_bounds__(kCalThreads) void stream_kernel(const uint4* __rest
         }
     }
     // xor over the workgroup, one 16-byte result per workgroup
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        x.x ^= __shfl_xor(x.x, o); x.y ^= __shfl_xor(x.y, o);
+        x.z ^= __shfl_xor(x.z, o); x.w ^= __shfl_xor(x.w, o);
+    }
+    __shared__ uint4 red[kCalThreads / 64];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kCalThreads / 64; ++w) {
+            x.x ^= red[w].x; x.y ^= red[w].y; x.z ^= red[w].z; x.w ^= red[w].w;
+        }
+        sink[blockIdx.x] = x;
+    }
+}
+
+// Piece p (4 KiB) of the list is piece p % ppc of chunk ids[p / ppc]; load u
+// of a thread reads 16 bytes of piece p0 + u, so a wave's load is one
+// contiguous 1-KiB run and a workgroup's eight loads cover 32 KiB.
+__global__ __launch_bounds__(kCalThreads) void gather_kernel(const uint4* __restrict__ src, int64_t n16,
+                                                             const int32_t* __restrict__ ids, int64_t nchunks,
+                                                             int ppc, uint4* __restrict__ sink) {
+    const int64_t npieces = nchunks * ppc;
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    for (int64_t p0 = (int64_t)blockIdx.x * kCalUnroll; p0 < npieces; p0 += (int64_t)gridDim.x * kCalUnroll) {
+        uint4 v[kCalUnroll];
+#pragma unroll
+        for (int u = 0; u < kCalUnroll; ++u) {
+            const int64_t pc = p0 + u;
+            v[u] = make_uint4(0u, 0u, 0u, 0u);
+            if (pc < npieces) {
+                const int64_t id = ids[pc / ppc];
+                const int64_t j = (id * ppc + pc % ppc) * kCalThreads + threadIdx.x;
+                if (id >= 0 && j < n16) v[u] = ld_stream(src + j);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kCalUnroll; ++u) {
+            x.x ^= v[u].x; x.y ^= v[u].y; x.z ^= v[u].z; x.w ^= v[u].w;
+        }
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         x.x ^= __shfl_xor(x.x, o); x.y ^= __shfl_xor(x.y, o);
@@ -100,6 +145,14 @@ hipError_t launch_calib_stream(const void* src, void* dst, size_t bytes, int gri
     else
         stream_kernel<false><<<grid, kCalThreads, 0, s>>>(static_cast<const uint4*>(src), nullptr, n16,
                                                           static_cast<uint4*>(sink));
+    return hipGetLastError();
+}
+
+hipError_t launch_calib_gather(const void* src, size_t bytes, const int32_t* ids, int64_t nchunks, int chunk_bytes,
+                               int grid, void* sink, hipStream_t s) {
+    if (grid <= 0) grid = 2048;
+    gather_kernel<<<grid, kCalThreads, 0, s>>>(static_cast<const uint4*>(src), (int64_t)(bytes / 16), ids, nchunks,
+                                               chunk_bytes / 4096, static_cast<uint4*>(sink));
     return hipGetLastError();
 }
 

@@ -68,6 +68,8 @@ hipError_t launch_paths(const dflash_paths_args& a, void* ws, hipStream_t s);
 int calib_stream_max_grid();
 int calib_mfma_grid();
 hipError_t launch_calib_stream(const void* src, void* dst, size_t bytes, int grid, void* sink, hipStream_t s);
+hipError_t launch_calib_gather(const void* src, size_t bytes, const int32_t* ids, int64_t nchunks, int chunk_bytes,
+                               int grid, void* sink, hipStream_t s);
 hipError_t launch_calib_mfma(int iters, void* sink, hipStream_t s);
 
 }  // namespace dflash

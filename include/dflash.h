@@ -101,7 +101,7 @@ extern "C" {
 #define DFLASH_MAX_LAYERS 5      /* draft layers */
 #define DFLASH_INTER      5120   /* SwiGLU width (derived from the parameter count) */
 
-#define DFLASH_VERSION 10400     /* 1.4.0 */
+#define DFLASH_VERSION 10500     /* 1.5.0 */
 
 /* dflash_attn_args.split_tokens: cut the context tiles of all sequences,
  * laid end to end (each sequence's 32-token tiles, then its block's keys as
@@ -522,6 +522,16 @@ int dflash_draft_paths(const dflash_paths_args* args, void* workspace,
  *     workgroups (0 = 2048; at most 65536); with dst != NULL also stores
  *     every 16 bytes to dst (a copy).  sink receives one 16-byte xor per
  *     workgroup.
+ *   dflash_calib_gather: reads chunks of the `bytes` (a positive multiple
+ *     of 16) at src (16-byte aligned) in the order of the device list
+ *     chunk_ids[nchunks] (int32): chunk c covers bytes [c chunk_bytes,
+ *     (c + 1) chunk_bytes), chunk_bytes a multiple of 4096 in [4096, 2^20].
+ *     Pieces of 4 KiB, eight in flight per thread, over `grid` workgroups
+ *     (0 = 2048; at most 65536).  A negative id, or the part of a chunk
+ *     past `bytes`, reads nothing.  A random permutation of the chunks gives
+ *     the access pattern of shuffled cache pages.  sink receives one 16-byte
+ *     xor per workgroup.  nchunks times chunk_bytes / 4096 must not exceed
+ *     2^31.
  *   dflash_calib_mfma: bf16 32x32x16 matrix instructions on register
  *     operands only, `iters` rounds of eight per wave, two waves per SIMD on
  *     256 CUs; *flops (if not NULL) receives the FLOPs of the launch.  sink
@@ -530,6 +540,8 @@ int dflash_draft_paths(const dflash_paths_args* args, void* workspace,
  * events on the stream. */
 int dflash_calib_sink_bytes(size_t* bytes);
 int dflash_calib_stream(const void* src, void* dst, size_t bytes, int grid, void* sink, void* stream);
+int dflash_calib_gather(const void* src, size_t bytes, const int32_t* chunk_ids, int64_t nchunks, int chunk_bytes,
+                        int grid, void* sink, void* stream);
 int dflash_calib_mfma(int iters, void* sink, double* flops, void* stream);
 
 #ifdef __cplusplus

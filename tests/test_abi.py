@@ -55,7 +55,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_struct_sizes_and_version(lib):
     from block_speculative_decoding_amd import _lib
-    assert lib.dflash_version() == 10400
+    assert lib.dflash_version() == 10500
     for kind, st in enumerate(_lib.ARG_STRUCTS):
         assert lib.dflash_args_size(kind) == ctypes.sizeof(st)
     assert lib.dflash_args_size(len(_lib.ARG_STRUCTS)) == 0
@@ -385,6 +385,20 @@ def test_calibration_validation(lib):
     assert lib.dflash_calib_stream(FAKE, FAKE + 8, 1024, 0, FAKE, None) == -1      # misaligned copy target
     assert lib.dflash_calib_stream(FAKE, None, 1024, 0, None, None) == -1
     assert lib.dflash_calib_stream(FAKE, None, 1024, 65537, FAKE, None) == -1
+    g = lib.dflash_calib_gather
+    g.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    assert g(None, 1 << 20, FAKE, 4, 8192, 0, FAKE, None) == -1
+    assert g(FAKE, 1 << 20, None, 4, 8192, 0, FAKE, None) == -1
+    assert g(FAKE, 1 << 20, FAKE, 4, 8192, 0, None, None) == -1
+    assert g(FAKE + 8, 1 << 20, FAKE, 4, 8192, 0, FAKE, None) == -1                 # misaligned source
+    assert g(FAKE, 1000, FAKE, 4, 8192, 0, FAKE, None) == -1                        # not a multiple of 16
+    assert g(FAKE, 1 << 20, FAKE, 4, 6000, 0, FAKE, None) == -1                     # chunk not 4 KiB pieces
+    assert g(FAKE, 1 << 20, FAKE, 4, 2 << 20, 0, FAKE, None) == -1                  # chunk above 1 MiB
+    assert g(FAKE, 1 << 20, FAKE, 0, 8192, 0, FAKE, None) == -1
+    assert g(FAKE, 1 << 20, FAKE, (1 << 30) + 1, 8192, 0, FAKE, None) == -1         # over 2^31 pieces
+    assert g(FAKE, 1 << 20, FAKE, 4, 8192, 65537, FAKE, None) == -1
+    assert b"dflash_calib_gather" in lib.dflash_last_error()
     f = ctypes.c_double()
     assert lib.dflash_calib_mfma(0, FAKE, ctypes.byref(f), None) == -1
     assert lib.dflash_calib_mfma(5, None, ctypes.byref(f), None) == -1

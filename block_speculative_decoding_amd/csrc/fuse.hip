@@ -21,7 +21,10 @@
 //         -> fp32 split-K partials [ks2][M][N]
 //   kv    -> sums the partials and does the same per head.
 // From 4096 rows on, both GEMMs use 256x256 tiles without split-K and the
-// second one carries the K/V injection in its epilogue (no kv launch).
+// second one carries the K/V injection in its epilogue (no kv launch); where
+// the first GEMM's tiles do not fill whole rounds of one workgroup per CU it
+// runs stream-K (equal runs of k-tiles, a few fp32 slots per tile that the
+// norm adds).
 // fp32 runs the fp32 GEMM with split-K, the norm and the kv launch.
 // The bf16 GEMMs run on the 32x32x16 bf16 matrix instruction with operands
 // staged through LDS by buffer loads that write LDS directly; tiles are laid
@@ -69,28 +72,60 @@ constexpr int kBigStageBytes = 2 * BMB * kBigPitch;
 constexpr int kBigPartsA = BMB * 8 / kBigThreads;  // buffer loads per thread per stage and operand (4)
 __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
+// Tile t of the stream-K order: groups of kGemmGroupM row tiles, and within
+// a group the row tile fastest, so consecutive tiles share a weight panel and
+// a group's rows are reused across every column tile.  sk_tile_index is the
+// inverse.
+__host__ __device__ __forceinline__ void sk_tile(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int in_group = kGemmGroupM * tiles_n;
+    const int first_m = t / in_group * kGemmGroupM;
+    const int gm = tiles_m - first_m < kGemmGroupM ? tiles_m - first_m : kGemmGroupM;
+    const int q = t % in_group;
+    tm = first_m + q % gm;
+    tn = q / gm;
+}
+__host__ __device__ __forceinline__ int sk_tile_index(int tm, int tn, int tiles_m, int tiles_n) {
+    const int first_m = tm / kGemmGroupM * kGemmGroupM;
+    const int gm = tiles_m - first_m < kGemmGroupM ? tiles_m - first_m : kGemmGroupM;
+    return first_m * tiles_n + tn * gm + (tm - first_m);
+}
+
 
 // MODE 0: fp32 partials to p.part (the fusion GEMM); 1: the K/V epilogue
 // (ep); 2: the shared head's epilogue (hp): bf16 logits through LDS and the
 // draft keys of its rows.
-template <int MODE>
+template <int MODE, bool SK = false>
 __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParams p, KvEpilogue ep, HeadEpilogue hp) {
+    static_assert(!SK || MODE == 0, "stream-K only for the fp32-partial GEMM");
     constexpr bool KV = MODE == 1;
     const int tiles_m = (p.M + BMB - 1) / BMB, tiles_n = p.N / BNB;
-    const TileId t = tile_id(p, tiles_m, tiles_n);
-    if (!t.valid) return;
     const int nk = p.K / BKB;
+    // Stream-K (SK): the tiles' k-tiles are laid end to end in the order of
+    // sk_tile and cut into runs of p.sk_q, one per workgroup; the runs are
+    // dealt to the XCDs in contiguous ranges.  A run covers the end of one
+    // tile and the start of the next, so a tile's k-range is shared by the
+    // workgroups whose runs meet it, each writing its products to its own
+    // slot (its position minus that of the tile's first workgroup).
+    int sk_pos = 0;
+    int64_t sk_u = 0, sk_end = 0;
+    TileId t = {};
+    if (SK) {
+        const int per = gridDim.x / kXcds;
+        sk_pos = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+        sk_u = (int64_t)sk_pos * p.sk_q;
+        sk_end = min((int64_t)tiles_m * tiles_n * nk, sk_u + p.sk_q);
+        if (sk_u >= sk_end) return;
+    } else {
+        t = tile_id(p, tiles_m, tiles_n);
+        if (!t.valid) return;
+    }
 
     // Two operand stages; the K epilogue reuses them as a [256][256] bf16
     // staging tile plus 4 KiB of row sums after them.
     __shared__ __attribute__((aligned(16))) uint4 lds[2 * kBigStageBytes / 16 + 256];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int m0 = t.tm * BMB, n0 = t.tn * BNB;
-    const uint16_t* bmat = static_cast<const uint16_t*>(p.b) + (int64_t)n0 * p.K;
     const void *aseg0 = p.aseg[0], *aseg1 = p.aseg[1], *aseg2 = p.aseg[2], *aseg3 = p.aseg[3], *aseg4 = p.aseg[4];
-    const uint32_t arows = (uint32_t)min(p.M - m0, BMB);
-
     // Load j of a thread covers unit P = j * 512 + tid of the A (or B) half:
     // row P >> 3, chunk (P & 7) ^ swz8(row).
     uint32_t voa[kBigPartsA], vob[kBigPartsA];
@@ -100,23 +135,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
         voa[j] = (uint32_t)(r * (int)p.a_stride + 8 * c) * 2u;
         vob[j] = (uint32_t)(r * p.K + 8 * c) * 2u;
     }
-    // Both operands' buffer descriptors for k-tile kt, computed once per
-    // k-tile at the top of the loop: the loads themselves sit between matrix
-    // instructions, where a segment select (a division and a five-way pointer
-    // choice per load) would hold up the next one.
     struct StageSrc { i32x4 a, b; };
-    auto stage_src = [&](int kt) {
-        const int kg = kt * BKB;
-        // The K/V projection's A operand (H_t) and the head's (y) are one segment.
-        const int seg = MODE != 0 ? 0 : kg / p.seg_w;
-        const int kc = kg - seg * p.seg_w;
-        const void* av = seg == 0 ? aseg0 : seg == 1 ? aseg1 : seg == 2 ? aseg2 : seg == 3 ? aseg3 : aseg4;
-        const uint16_t* a = static_cast<const uint16_t*>(av) + (int64_t)m0 * p.a_stride + kc;
-        StageSrc s;
-        s.a = buffer_rsrc(a, arows * (uint32_t)p.a_stride * 2u - (uint32_t)kc * 2u);
-        s.b = buffer_rsrc(bmat + kg, (uint32_t)BNB * (uint32_t)p.K * 2u - (uint32_t)kg * 2u);
-        return s;
-    };
     // The wave index read as wave-uniform, so that each load's LDS base (M0)
     // is scalar arithmetic.
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
@@ -133,11 +152,6 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
     };
 
     f32x16 acc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16){};
-
     const int wq = wave & 3;
     const int wr = (wave >> 2) * 128;
     const int wc = KV ? 128 * (wq >> 1) + 32 * (wq & 1) : 64 * wq;  // column of block 0
@@ -166,45 +180,102 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     };
 
-    bf16x8 fa[2][4], fb[2][2];
+    // Prologue and main loop over k-tiles [kb, ke) of the tile at (m0, n0);
+    // leaves the tile's products in acc.
+    auto run = [&](const int m0, const int n0, const int kb, const int ke) {
+        const uint16_t* bmat = static_cast<const uint16_t*>(p.b) + (int64_t)n0 * p.K;
+        const uint32_t arows = (uint32_t)min(p.M - m0, BMB);
+        // Both operands' buffer descriptors for k-tile kt, computed once per
+        // k-tile at the top of the loop: the loads themselves sit between matrix
+        // instructions, where a segment select (a division and a five-way pointer
+        // choice per load) would hold up the next one.
+        auto stage_src = [&](int kt) {
+            const int kg = kt * BKB;
+            // The K/V projection's A operand (H_t) and the head's (y) are one segment.
+            const int seg = MODE != 0 ? 0 : kg / p.seg_w;
+            const int kc = kg - seg * p.seg_w;
+            const void* av = seg == 0 ? aseg0 : seg == 1 ? aseg1 : seg == 2 ? aseg2 : seg == 3 ? aseg3 : aseg4;
+            const uint16_t* a = static_cast<const uint16_t*>(av) + (int64_t)m0 * p.a_stride + kc;
+            StageSrc s;
+            s.a = buffer_rsrc(a, arows * (uint32_t)p.a_stride * 2u - (uint32_t)kc * 2u);
+            s.b = buffer_rsrc(bmat + kg, (uint32_t)BNB * (uint32_t)p.K * 2u - (uint32_t)kg * 2u);
+            return s;
+        };
 #pragma unroll
-    for (int s0 = 0; s0 < 2; ++s0) {
-        const StageSrc src = stage_src(min(s0, nk - 1));
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int t2 = 0; t2 < 2 * kBigPartsA; ++t2) load_part(src, s0, t2);
-    }
-    wait_vm<2 * kBigPartsA>();  // stage 0 landed
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    rd(0, 0, fa[0], fb[0]);
-    for (int i = 0; i < nk; ++i) {
-        const int slot = i & 1;
-        const StageSrc nsrc = stage_src(min(i + 2, nk - 1));
+            for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16){};
+
+        bf16x8 fa[2][4], fb[2][2];
 #pragma unroll
-        for (int s = 0; s < 3; ++s) {
-            rd(slot, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-            wait_lgkm<6>();  // substep s's reads (issued before these 6) are back
-            __builtin_amdgcn_sched_barrier(0);
-            mm(fa[s & 1], fb[s & 1]);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int s0 = 0; s0 < 2; ++s0) {
+            const StageSrc src = stage_src(kb + min(s0, ke - kb - 1));
+#pragma unroll
+            for (int t2 = 0; t2 < 2 * kBigPartsA; ++t2) load_part(src, s0, t2);
         }
-        wait_lgkm<0>();
-        wait_vm<0>();                  // stage i+1 landed
-        __builtin_amdgcn_s_barrier();  // and every wave is done reading stage i
+        wait_vm<2 * kBigPartsA>();  // stage 0 landed
+        __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        rd(slot ^ 1, 0, fa[0], fb[0]);
-        __builtin_amdgcn_sched_barrier(0);
+        rd(0, 0, fa[0], fb[0]);
+        for (int i = 0; i < ke - kb; ++i) {
+            const int slot = i & 1;
+            const StageSrc nsrc = stage_src(kb + min(i + 2, ke - kb - 1));
 #pragma unroll
-        for (int t2 = 0; t2 < 8; ++t2) {
-            acc[t2 >> 1][t2 & 1] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][t2 >> 1], fb[1][t2 & 1], acc[t2 >> 1][t2 & 1], 0, 0, 0);
+            for (int s = 0; s < 3; ++s) {
+                rd(slot, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+                wait_lgkm<6>();  // substep s's reads (issued before these 6) are back
+                __builtin_amdgcn_sched_barrier(0);
+                mm(fa[s & 1], fb[s & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            wait_lgkm<0>();
+            wait_vm<0>();                  // stage i+1 landed
+            __builtin_amdgcn_s_barrier();  // and every wave is done reading stage i
+            asm volatile("" ::: "memory");
+            rd(slot ^ 1, 0, fa[0], fb[0]);
             __builtin_amdgcn_sched_barrier(0);
-            load_part(nsrc, slot, t2);  // stage i+2 into the slot stage i used
-            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t2 = 0; t2 < 8; ++t2) {
+                acc[t2 >> 1][t2 & 1] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][t2 >> 1], fb[1][t2 & 1], acc[t2 >> 1][t2 & 1], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                load_part(nsrc, slot, t2);  // stage i+2 into the slot stage i used
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
+        wait_vm<0>();  // the clamped trailing loads must land before the workgroup exits
+        wait_lgkm<0>();
+    };
+
+    if (SK) {
+        // The run's pieces of one or more tiles, each written to this
+        // workgroup's slot of its tile.
+        while (sk_u < sk_end) {
+            const int64_t tile = sk_u / nk;
+            const int kb = (int)(sk_u - tile * nk);
+            const int ke = (int)min((int64_t)nk, kb + (sk_end - sk_u));
+            int tm, tn;
+            sk_tile((int)tile, tiles_m, tiles_n, tm, tn);
+            const int slot = sk_pos - (int)(tile * nk / p.sk_q);
+            run(tm * BMB, tn * BNB, kb, ke);
+            float* out = p.part + (int64_t)slot * p.M * p.N;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int gm = tm * BMB + wr + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                        const int gn = tn * BNB + wc + kBstep * j + lr;
+                        if (gm < p.M) out[(int64_t)gm * p.N + gn] = acc[i][j][r];
+                    }
+            sk_u += ke - kb;
+            __syncthreads();  // every wave is done with the stages before the next run's loads
+        }
+        return;
     }
-    wait_vm<0>();  // the clamped trailing loads must land before the workgroup exits
-    wait_lgkm<0>();
+    const int m0 = t.tm * BMB, n0 = t.tn * BNB;
+    run(m0, n0, 0, nk);
 
     // Lane holds column lr of each 32x32 block, rows 8*(r/4) + 4*lh + (r%4).
     if (MODE == 2) {
@@ -465,16 +536,22 @@ constexpr int kMaxKs = kGemmMaxKs;
 // 2560-wide row per workgroup, all ks partial loads of a thread in flight.
 constexpr int kNormThreads = DFLASH_D / 4;
 
+// Four consecutive values (c0 a multiple of 4) in one store: ht lies in the
+// 256-byte aligned workspace and ht_out is 16-byte aligned by the contract.
+__device__ __forceinline__ void store4(float* p, const float* h) {
+    *reinterpret_cast<float4*>(p) = make_float4(h[0], h[1], h[2], h[3]);
+}
+__device__ __forceinline__ void store4(uint16_t* p, const float* h) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+}
 template <typename T>
 __device__ __forceinline__ void norm_store(const float* y, float rinv, const T* gc, int64_t base, int c0, T* ht,
                                            T* ht_out) {
+    float h[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int c = c0 + e;
-        const float h = Elem<T>::load(gc, c) * (y[e] * rinv);
-        Elem<T>::store(ht, base + c, h);
-        if (ht_out) Elem<T>::store(ht_out, base + c, h);
-    }
+    for (int e = 0; e < 4; ++e) h[e] = Elem<T>::load(gc, c0 + e) * (y[e] * rinv);
+    store4(ht + base + c0, h);
+    if (ht_out) store4(ht_out + base + c0, h);
 }
 
 // With rp.cs set, the workgroup of row m also writes row m's RoPE table.
@@ -505,17 +582,49 @@ __global__ __launch_bounds__(kNormThreads) void fuse_norm_kernel(const float* pa
 }
 
 // Single-partial path (large M): one wave per row, 4 rows per workgroup, ten
-// 16-byte loads per lane in flight, a wave-only reduction.
+// 16-byte loads per lane in flight, a wave-only reduction.  Under stream-K
+// (sk_q > 0) float4 i of a lane lies in column tile i (256 columns), whose
+// products sit in the slots of the workgroups whose runs met that tile; they
+// are added in slot order.
+constexpr int kMaxSkSlots = 4;
 template <typename T>
 __global__ __launch_bounds__(kThreads) void fuse_norm_rows_kernel(const float* part, int M, const T* gc, float eps,
-                                                                 T* ht, T* ht_out) {
+                                                                 T* ht, T* ht_out, int sk_q, int nk) {
     constexpr int D = DFLASH_D, PER = D / (64 * 4);  // 10 float4 per lane
+    static_assert(PER * 256 == D, "one float4 of a lane per 256-column tile");
     const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (m >= M) return;
     const float4* row = reinterpret_cast<const float4*>(part + (int64_t)m * D);
     float4 v[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) v[i] = row[64 * i + lane];
+    if (sk_q > 0) {
+        // Every slot load in flight before the first add.  The workgroup's
+        // four rows share a row tile, so the slot counts are scalar work
+        // (tile index times 200 stays below 2^31).
+        const int tiles_m = (M + BMB - 1) / BMB, tm = blockIdx.x / (BMB / 4);
+        const int64_t slot_stride = (int64_t)M * D / 4;
+        int n[PER];
+        float4 w[kMaxSkSlots - 1][PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const unsigned t = (unsigned)sk_tile_index(tm, i, tiles_m, PER), q = (unsigned)sk_q, k = (unsigned)nk;
+            n[i] = (int)(((t + 1) * k - 1) / q - t * k / q) + 1;
+        }
+#pragma unroll
+        for (int sl = 1; sl < kMaxSkSlots; ++sl)
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+                w[sl - 1][i] = sl < n[i] ? row[sl * slot_stride + 64 * i + lane] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int sl = 1; sl < kMaxSkSlots; ++sl)
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+                if (sl < n[i]) {
+                    v[i].x += w[sl - 1][i].x; v[i].y += w[sl - 1][i].y;
+                    v[i].z += w[sl - 1][i].z; v[i].w += w[sl - 1][i].w;
+                }
+    }
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
@@ -592,6 +701,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // epilogue); small ones the 128x128 split-K kernel.
 constexpr int kBigM = 4096;   // from here the 256x256 kernel (no split-K) beats the split-K one
 constexpr int kPairTiles = 256;  // K/V GEMM tiles that one 512-thread workgroup per CU covers in one round
+constexpr int kSkWorkgroups = 256;  // stream-K runs of the big first GEMM: one 8-wave workgroup per CU
 
 FusePlan fuse_plan(const dflash_fuse_args& a) {
     FusePlan pl;
@@ -610,9 +720,27 @@ FusePlan fuse_plan(const dflash_fuse_args& a) {
     // reading half the partials (5.6 against 6.9 us).
     pl.pair2 = bf && !pl.big && ((M + 127) / 128) * (N2 / 128) <= kPairTiles;
     if (pl.pair2) pl.ks2 = 1;
+    // Stream-K for the big first GEMM where its tiles do not fill whole
+    // rounds of one workgroup per CU (M = 4096: 160 tiles on 256 CUs): the
+    // k-tiles of all tiles are cut into kSkWorkgroups equal runs.
+    pl.sk_q = 0;
+    pl.sk_slots = 1;
+    if (pl.big) {
+        const int tiles_m = (M + BMB - 1) / BMB, tiles = tiles_m * (DFLASH_D / BNB);
+        const int64_t nk = DFLASH_NCAPTURE * DFLASH_D / BKB;
+        if (tiles % kSkWorkgroups != 0 && (int64_t)tiles * nk < ((int64_t)1 << 31)) {
+            const int64_t units = (int64_t)tiles * nk;
+            pl.sk_q = (int)((units + kSkWorkgroups - 1) / kSkWorkgroups);
+            for (int64_t t = 0; t < tiles; ++t) {
+                const int n = (int)(((t + 1) * nk - 1) / pl.sk_q - t * nk / pl.sk_q) + 1;
+                if (n > pl.sk_slots) pl.sk_slots = n;
+            }
+            if (pl.sk_slots > kMaxSkSlots) { pl.sk_q = 0; pl.sk_slots = 1; }
+        }
+    }
     const size_t es = bf ? 2 : 4;
     pl.off_part1 = 0;
-    pl.off_ht = align256((size_t)pl.ks1 * M * DFLASH_D * 4);
+    pl.off_ht = align256((size_t)pl.ks1 * pl.sk_slots * M * DFLASH_D * 4);
     pl.off_part2 = pl.off_ht + align256((size_t)M * DFLASH_D * es);
     // The big and pair K/V paths need no second partial buffer, only the RoPE table.
     pl.ws_bytes = pl.off_part2 + (pl.big || pl.pair2 ? align256((size_t)M * 64 * sizeof(float2))
@@ -645,7 +773,10 @@ hipError_t launch_fuse(const dflash_fuse_args& a, const FusePlan& pl, void* ws, 
     gemm_set_split(g1, a.dtype, pl.ks1);
     g1.part = part1;
     KvEpilogue ep = {};
-    if (pl.big) {
+    if (pl.big && pl.sk_q > 0) {
+        g1.sk_q = pl.sk_q;
+        gemm_bf16_big_kernel<0, true><<<kSkWorkgroups, kBigThreads, 0, s>>>(g1, ep, HeadEpilogue{});
+    } else if (pl.big) {
         const int tiles = ((M + BMB - 1) / BMB) * (DFLASH_D / BNB);
         gemm_bf16_big_kernel<0><<<(tiles + kXcds - 1) / kXcds * kXcds, kBigThreads, 0, s>>>(g1, ep, HeadEpilogue{});
     } else {
@@ -672,10 +803,12 @@ hipError_t launch_fuse(const dflash_fuse_args& a, const FusePlan& pl, void* ws, 
         if (bf)
             fuse_norm_rows_kernel<uint16_t><<<nb, kThreads, 0, s>>>(part1, M, static_cast<const uint16_t*>(a.gc), a.eps,
                                                                     static_cast<uint16_t*>(ht),
-                                                                    static_cast<uint16_t*>(a.ht_out));
+                                                                    static_cast<uint16_t*>(a.ht_out), pl.sk_q,
+                                                                    g1.K / BKB);
         else
             fuse_norm_rows_kernel<float><<<nb, kThreads, 0, s>>>(part1, M, static_cast<const float*>(a.gc), a.eps,
-                                                                 static_cast<float*>(ht), static_cast<float*>(a.ht_out));
+                                                                 static_cast<float*>(ht), static_cast<float*>(a.ht_out),
+                                                                 0, 1);
     } else if (bf) {
         fuse_norm_kernel<uint16_t><<<M, kNormThreads, 0, s>>>(part1, pl.ks1, M, static_cast<const uint16_t*>(a.gc),
                                                               a.eps, static_cast<uint16_t*>(ht),

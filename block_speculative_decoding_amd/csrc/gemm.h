@@ -25,6 +25,8 @@ struct GemmParams {
     float* part;          // [ks][M][N]
     uint16_t* out_bf16;   // bf16 path with ks == 1: if set, the product rounded to bf16
                           // goes here ([M][N]) instead of part
+    int sk_q;             // 256x256 fp32-partial GEMM only: k-tiles per workgroup run under
+                          // stream-K (0: one whole tile per workgroup); see gemm_bf16_big_kernel
     uint16_t* swiglu_out; // bf16 path with ks == 1: if set, B is [gate ; up] (rows [0, N/2) and
                           // [N/2, N)) and silu(gate) * up, from the fp32 products and rounded
                           // to bf16, goes here ([M][N/2]); tile tn multiplies gate rows

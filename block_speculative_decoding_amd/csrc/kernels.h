@@ -32,6 +32,8 @@ struct FusePlan {
     int ks1, ks2;          // split-K factors of the two GEMMs
     bool big;              // 256x256 kernels with the fused K/V epilogue
     bool pair2;            // K/V GEMM on the 128x128 kernel with two k-groups and the K/V epilogue
+    int sk_q;              // big first GEMM under stream-K: k-tiles per workgroup (0: off)
+    int sk_slots;          // product slots a tile's workgroups write under stream-K (1 otherwise)
     size_t off_part1, off_ht, off_part2, ws_bytes;
 };
 FusePlan fuse_plan(const dflash_fuse_args& a);

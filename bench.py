@@ -67,6 +67,9 @@ def parse():
                     help="only run the prefill fusion at M=32768 (2 warm-up + 5 timed calls) and, as a "
                          "reference on the same two GEMM shapes, torch's bf16 matmul (2 + 5 each): the "
                          "run behind the GEMM counter passes")
+    ap.add_argument("--gemm-probe-rows", type=int, default=32768,
+                    help="rows M of the --gemm-probe fusion (default 32768, the prefill; 4096 is the "
+                         "single-stream context)")
     ap.add_argument("--serving-gemm-probe", action="store_true",
                     help="only time ctx_fuse on the serving batch's new rows in its place in the cycle, "
                          "back to back (weights left in the MALL) and cold (MALL flushed before each "
@@ -87,18 +90,18 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "repeats": 5}))
 
 
-def gemm_probe():
-    """The prefill fusion (first GEMM [32768,12800] x [12800,2560], the K/V
-    GEMM [32768,2560] x [2560,10240] with its epilogue) and torch's bf16
-    matmul on the same two shapes, for counter passes that compare the
-    matrix pipes' busy fraction, the shader clock and the L2 traffic."""
+def gemm_probe(M=32768):
+    """The context fusion at M rows (first GEMM [M,12800] x [12800,2560], the
+    K/V GEMM [M,2560] x [2560,10240] with its epilogue; M = 32768 is the
+    prefill) and torch's bf16 matmul on the same two shapes, for counter
+    passes that compare the matrix pipes' busy fraction, the shader clock and
+    the L2 traffic."""
     import torch
     import block_speculative_decoding_amd as dfl
     from block_speculative_decoding_amd import synth
     dev = torch.device("cuda:0")
     bf = torch.bfloat16
     g = torch.Generator(device=dev).manual_seed(SEED + 1)
-    M = 32768
     hs = [torch.randn((M, 2560), generator=g, device=dev, dtype=torch.float32).to(bf) for _ in range(5)]
     w = {k: torch.from_numpy(np.ascontiguousarray(v)).to(bf).to(dev) for k, v in synth.fuse_weights(SEED, LAYERS).items()}
     npages = M // 16
@@ -119,7 +122,7 @@ def gemm_probe():
     t2 = timed(torch, lambda: torch.matmul(h, wkv_t))
     f1, f2 = 2 * M * 12800 * 2560, 2 * M * 2560 * LAYERS * 2048
     print(json.dumps({"gemm_probe": {
-        "ctx_fuse_m32768_ms": round(f_ms, 4), "ctx_fuse_TFLOP/s": round(flops / (f_ms * 1e-3) / 1e12, 1),
+        "M": M, "ctx_fuse_ms": round(f_ms, 4), "ctx_fuse_TFLOP/s": round(flops / (f_ms * 1e-3) / 1e12, 1),
         "torch_matmul_fuse_gemm_ms": round(t1, 4), "torch_matmul_fuse_gemm_TFLOP/s": round(f1 / (t1 * 1e-3) / 1e12, 1),
         "torch_matmul_kv_gemm_ms": round(t2, 4), "torch_matmul_kv_gemm_TFLOP/s": round(f2 / (t2 * 1e-3) / 1e12, 1)}}))
 
@@ -408,7 +411,6 @@ def prefill_measurements(torch, dfl, synth):
     dev = torch.device("cuda:0")
     bf = torch.bfloat16
     g = torch.Generator(device=dev).manual_seed(SEED + 1)
-    M = 32768
     hs = [torch.randn((M, 2560), generator=g, device=dev, dtype=torch.float32).to(bf) for _ in range(5)]
     w = {k: torch.from_numpy(np.ascontiguousarray(v)).to(bf).to(dev) for k, v in synth.fuse_weights(SEED, LAYERS).items()}
     npages = M // 16
@@ -813,7 +815,7 @@ def main():
         copy_probe()
         return
     if args.gemm_probe:
-        gemm_probe()
+        gemm_probe(args.gemm_probe_rows)
         return
     if args.serving_gemm_probe:
         serving_gemm_probe()

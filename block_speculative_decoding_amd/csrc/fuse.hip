@@ -45,7 +45,8 @@ constexpr int kXcds = kGemmXcds;
 
 // ---- bf16 GEMM for large M: 256x256 tile, eight waves (two per SIMD) of
 // 128x64 (4x2 blocks of the 32x32x16 instruction, 128 fp32 accumulators per
-// lane), 64 k per stage in a two-stage LDS ring (2 x 64 KiB), no split-K.
+// lane), 64 k per stage in a two-stage LDS ring (2 x 64 KiB), no split-K
+// (the fp32-output mode has a stream-K form, below).
 //  * Operands reach LDS through buffer loads that write LDS directly (16 B per
 //    lane, lane l at the wave's LDS base + 16 l).  The descriptor's range stops
 //    at row M, so rows of the last A tile past M read as zero.

@@ -411,6 +411,7 @@ def prefill_measurements(torch, dfl, synth):
     dev = torch.device("cuda:0")
     bf = torch.bfloat16
     g = torch.Generator(device=dev).manual_seed(SEED + 1)
+    M = 32768
     hs = [torch.randn((M, 2560), generator=g, device=dev, dtype=torch.float32).to(bf) for _ in range(5)]
     w = {k: torch.from_numpy(np.ascontiguousarray(v)).to(bf).to(dev) for k, v in synth.fuse_weights(SEED, LAYERS).items()}
     npages = M // 16

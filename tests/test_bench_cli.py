@@ -58,3 +58,41 @@ def test_fusion_flops_and_bytes():
     assert flops == 2 * M * (w_c + w_kv)
     # Weights once, the five captured rows in, K and V of every layer out.
     assert nbytes == (w_c + w_kv) * BF16 + M * (5 * 2560 + 5 * 2 * 8 * 128) * BF16
+
+
+def test_every_name_a_function_reads_is_defined():
+    # bench.py's measurement functions only run on a GPU; this catches a name
+    # read in one of them that nothing defines (a local lost in an edit) on
+    # the CPU: locals, parameters, comprehension targets, module globals and
+    # builtins are the names a function may read.
+    import ast
+    import builtins
+    tree = ast.parse(open(os.path.join(ROOT, "bench.py")).read())
+    known = set(dir(builtins))
+    for node in tree.body:
+        if isinstance(node, (ast.FunctionDef, ast.ClassDef)):
+            known.add(node.name)
+        elif isinstance(node, (ast.Import, ast.ImportFrom)):
+            known.update((a.asname or a.name).split(".")[0] for a in node.names)
+        elif isinstance(node, (ast.Assign, ast.AnnAssign)):
+            for t in node.targets if isinstance(node, ast.Assign) else [node.target]:
+                known.update(n.id for n in ast.walk(t) if isinstance(n, ast.Name))
+    missing = []
+    for fn in (n for n in tree.body if isinstance(n, ast.FunctionDef)):
+        local = set()
+        for n in ast.walk(fn):
+            if isinstance(n, (ast.FunctionDef, ast.Lambda)):
+                args = n.args
+                local.update(a.arg for a in args.args + args.kwonlyargs)
+                local.update(a.arg for a in (args.vararg, args.kwarg) if a)
+                if isinstance(n, ast.FunctionDef):
+                    local.add(n.name)
+            elif isinstance(n, ast.Name) and isinstance(n.ctx, (ast.Store, ast.Del)):
+                local.add(n.id)
+            elif isinstance(n, (ast.Import, ast.ImportFrom)):
+                local.update((a.asname or a.name).split(".")[0] for a in n.names)
+            elif isinstance(n, ast.ExceptHandler) and n.name:
+                local.add(n.name)
+        missing += [(fn.name, n.lineno, n.id) for n in ast.walk(fn)
+                    if isinstance(n, ast.Name) and isinstance(n.ctx, ast.Load) and n.id not in local | known]
+    assert not missing, missing

@@ -58,9 +58,9 @@ struct AttnParams {
 
 struct SeqRange { int S, t0, a0, nspl; };
 
-__device__ __forceinline__ SeqRange seq_range(const AttnParams& p, int b) {
+// The ranges of a sequence whose ctx_len entry is S.
+__device__ __forceinline__ SeqRange seq_range_of(const AttnParams& p, int S) {
     SeqRange r;
-    int S = p.ctx_len[b];
     const int cap = p.max_pages * 16;
     S = S < 0 ? 0 : (S > cap ? cap : S);
     r.S = S;
@@ -70,6 +70,7 @@ __device__ __forceinline__ SeqRange seq_range(const AttnParams& p, int b) {
     r.nspl = n <= 0 ? 1 : (n + p.split - 1) / p.split;
     return r;
 }
+__device__ __forceinline__ SeqRange seq_range(const AttnParams& p, int b) { return seq_range_of(p, p.ctx_len[b]); }
 
 // cos/sin of pos * inv_freq[i]: angle and range reduction in fp64, then fp32.
 __device__ __forceinline__ void rope_cs(int pos, int i, const double* inv_freq, float& c, float& s) {
@@ -96,6 +97,42 @@ __device__ __forceinline__ void norm_rope_16(float* x, const float* g, int part,
         const float bb = x[8 + e] * rinv * g[8 + e];
         float c, s;
         rope_cs(pos, 8 * part + e, inv_freq, c, s);
+        x[e] = a * c - bb * s;
+        x[8 + e] = bb * c + a * s;
+    }
+}
+
+// Raw bf16 of dims [8p, 8p+8) and [64+8p, 64+8p+8) of a 128-wide row, and
+// their widening to x[0..15] in the order norm_rope_16 takes.
+__device__ __forceinline__ void load_raw16(const uint16_t* row, int part, uint4 (&r)[2]) {
+    __builtin_memcpy(&r[0], row + 8 * part, 16);
+    __builtin_memcpy(&r[1], row + 64 + 8 * part, 16);
+}
+__device__ __forceinline__ void widen16(const uint4 (&r)[2], float* x) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t w[4] = {r[h].x, r[h].y, r[h].z, r[h].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[8 * h + e] = bf16_bits_to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1))));
+    }
+}
+
+// norm_rope_16 with the lane's 8 frequencies inv_freq[8p + e] already in
+// registers (the same arithmetic).
+__device__ __forceinline__ void norm_rope_16f(float* x, const float* g, const double* fr, int pos, float eps) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ss += x[e] * x[e];
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    ss += __shfl_xor(ss, 4);
+    const float rinv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + eps);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float a = x[e] * rinv * g[e];
+        const float bb = x[8 + e] * rinv * g[8 + e];
+        float c, s;
+        rope_cs(pos, e, fr, c, s);
         x[e] = a * c - bb * s;
         x[8 + e] = bb * c + a * s;
     }
@@ -139,40 +176,36 @@ __device__ __forceinline__ void attend(const AttnParams& p, int b, int hp, const
     const uint16_t* gq = static_cast<const uint16_t*>(p.gq);
     const uint16_t* gk = static_cast<const uint16_t*>(p.gk);
 
-    // ---- prologue: q^ for 32 rows, k^blk / v_blk of each head into LDS
+    // ---- prologue.  Every global read it needs (q and block k rows with
+    // their norm weights, v_blk, the split's page ids) is issued first; once
+    // the page ids are in LDS the first context tile's K/V loads go out, and
+    // q^ / k^blk (norm + RoPE) are computed while those are in flight.
+    const int rn = tid >> 3, rp = tid & 7;  // q row rn = hw2*32 + hh*8 + j, dims of part rp
+    const int hw2 = rn >> 5, hh = (rn >> 3) & 3, j = rn & 7;
+    const bool kthr = tid < 64 * kHpw;
+    const bool vthr = !kthr && tid < 64 * kHpw + 128 * kHpw;
+    uint4 rq[2], rgq[2], rk[2], rgk[2];   // raw bf16 rows and norm weights
+    uint4 vcopy = make_uint4(0, 0, 0, 0);
+    double fr[8];                         // inv_freq[8 rp + e]
     {
-        const int n = tid >> 3, part = tid & 7;  // n = hw2*32 + hh*8 + j
-        const int hw2 = n >> 5, hh = (n >> 3) & 3, j = n & 7;
         const int g2 = hp * kHpw + hw2;
         const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
                                ((((int64_t)b * 32 + 4 * g2 + hh) * 8 + j) * 128);
-        float x[16], gw[16];
-        load_row16(qrow, part, x);
-        load_row16(gq, part, gw);
-        norm_rope_16(x, gw, part, sr.S + j, p.eps, p.inv_freq);
+        load_raw16(qrow, rp, rq);
+        load_raw16(gq, rp, rgq);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            qs_all[n * kQStride + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[e]);
-            qs_all[n * kQStride + 64 + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[8 + e]);
-        }
-        if (tid < 64 * kHpw) {
+        for (int e = 0; e < 8; ++e) fr[e] = p.inv_freq[8 * rp + e];
+        if (kthr) {
             const int hk = tid >> 6, jj = (tid >> 3) & 7;
-            const int gk2 = hp * kHpw + hk;
-            const uint16_t* krow = static_cast<const uint16_t*>(p.kb) + ((((int64_t)b * 8 + gk2) * 8 + jj) * 128);
-            load_row16(krow, part, x);
-            load_row16(gk, part, gw);
-            norm_rope_16(x, gw, part, sr.S + jj, p.eps, p.inv_freq);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                kbs_all[(hk * 8 + jj) * kQStride + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[e]);
-                kbs_all[(hk * 8 + jj) * kQStride + 64 + 8 * part + e] = (uint16_t)f32_to_bf16_bits(x[8 + e]);
-            }
-        } else if (tid < 64 * kHpw + 128 * kHpw) {
+            const uint16_t* krow = static_cast<const uint16_t*>(p.kb) + ((((int64_t)b * 8 + hp * kHpw + hk) * 8 + jj) * 128);
+            load_raw16(krow, rp, rk);
+            load_raw16(gk, rp, rgk);
+        } else if (vthr) {
             const int t2 = tid - 64 * kHpw;  // 128 threads x 16 B = the 2 KiB of v_blk (8 x 128 bf16) per head
             const int hv = t2 >> 7;
             const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.vb) +
                                                               (((int64_t)b * 8 + hp * kHpw + hv) * 8 * 128));
-            reinterpret_cast<uint4*>(vbs_all + hv * 8 * 128)[t2 & 127] = src[t2 & 127];
+            vcopy = src[t2 & 127];
         }
     }
     // Physical page ids of this split, staged once in LDS (-1 past the sequence
@@ -195,18 +228,8 @@ __device__ __forceinline__ void attend(const AttnParams& p, int b, int hp, const
     __syncthreads();
 
     const int m32 = lane & 31, hl = lane >> 5;
-    const uint16_t* qlds = qs + m32 * kQStride + 64 * hl;  // this lane's Q^T operand row
-    bf16x8 qreg[8];
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) qreg[kb] = *reinterpret_cast<const bf16x8*>(qlds + 8 * kb);
-    const float sl2 = kLog2e * 0.08838834764831845f;      // log2(e) / sqrt(128)
     const uint16_t* kc = static_cast<const uint16_t*>(p.kc);
     const uint16_t* vc = static_cast<const uint16_t*>(p.vc);
-
-    f32x16 acc[4];
-#pragma unroll
-    for (int db = 0; db < 4; ++db) acc[db] = (f32x16){};
-    float m_run = -INFINITY, l_run = 0.f;
     const uint4 z4 = make_uint4(0, 0, 0, 0);
 
     // Issue the loads of context tile `it` into kr / vr.  Loads are
@@ -227,6 +250,51 @@ __device__ __forceinline__ void attend(const AttnParams& p, int b, int hp, const
             for (int db = 0; db < 4; ++db) vr[kb2][db] = ld_stream(vp + 64 * db);
         }
     };
+    // The prologue's own reads were issued before the page ids and have
+    // arrived by now; waiting for them here (vmcnt 0 only) keeps the compiler
+    // from waiting on the tile loads below to reach them.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    uint4 ka[8], va[2][4];
+    if (wl < ntiles) load(wl, ka, va);
+
+    {
+        float xq[16], gwq[16];
+        widen16(rq, xq);
+        widen16(rgq, gwq);
+        norm_rope_16f(xq, gwq, fr, sr.S + j, p.eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            qs_all[rn * kQStride + 8 * rp + e] = (uint16_t)f32_to_bf16_bits(xq[e]);
+            qs_all[rn * kQStride + 64 + 8 * rp + e] = (uint16_t)f32_to_bf16_bits(xq[8 + e]);
+        }
+    }
+    if (kthr) {
+        const int hk = tid >> 6, jj = (tid >> 3) & 7;
+        float xk[16], gwk[16];
+        widen16(rk, xk);
+        widen16(rgk, gwk);
+        norm_rope_16f(xk, gwk, fr, sr.S + jj, p.eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            kbs_all[(hk * 8 + jj) * kQStride + 8 * rp + e] = (uint16_t)f32_to_bf16_bits(xk[e]);
+            kbs_all[(hk * 8 + jj) * kQStride + 64 + 8 * rp + e] = (uint16_t)f32_to_bf16_bits(xk[8 + e]);
+        }
+    } else if (vthr) {
+        const int t2 = tid - 64 * kHpw;
+        reinterpret_cast<uint4*>(vbs_all + (t2 >> 7) * 8 * 128)[t2 & 127] = vcopy;
+    }
+    __syncthreads();
+
+    const uint16_t* qlds = qs + m32 * kQStride + 64 * hl;  // this lane's Q^T operand row
+    bf16x8 qreg[8];
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) qreg[kb] = *reinterpret_cast<const bf16x8*>(qlds + 8 * kb);
+    const float sl2 = kLog2e * 0.08838834764831845f;      // log2(e) / sqrt(128)
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[db] = (f32x16){};
+    float m_run = -INFINITY, l_run = 0.f;
 
     // Scores, online softmax and P.V for one loaded tile.  `blk` marks the
     // block's own 8 keys (rows 0..7 valid).
@@ -309,9 +377,8 @@ __device__ __forceinline__ void attend(const AttnParams& p, int b, int hp, const
     };
 
     {
-        uint4 ka[8], va[2][4];
         for (int it = wl; it < ntiles; it += kWaves) {
-            load(it, ka, va);
+            if (it != wl) load(it, ka, va);   // tile wl was issued in the prologue
             process(it, false, ka, va);
         }
         // The block's own 8 keys / values: one masked tile for the wave next
@@ -441,14 +508,19 @@ __device__ __forceinline__ int seq_tiles(const SeqRange& sr) {
 }
 
 // s_pref[b] = first global tile of sequence b, s_pref[B] = all tiles (the
-// return value); every thread of the workgroup takes part.
-__device__ int tile_prefix(const AttnParams& p, int* s_pref, int* s_tmp) {
+// return value), s_len[b] = ctx_len[b] (so a segment's range needs no global
+// read); every thread of the workgroup takes part.
+__device__ int tile_prefix(const AttnParams& p, int* s_pref, int* s_len, int* s_tmp) {
     const int nt = blockDim.x, tid = threadIdx.x;
     const int per = (p.B + nt - 1) / nt;
     const int b0 = tid * per;
     int sum = 0;
     for (int i = 0; i < per; ++i)
-        if (b0 + i < p.B) sum += seq_tiles(seq_range(p, b0 + i));
+        if (b0 + i < p.B) {
+            const int S = p.ctx_len[b0 + i];
+            s_len[b0 + i] = S;
+            sum += seq_tiles(seq_range_of(p, S));
+        }
     s_tmp[tid] = sum;
     __syncthreads();
     for (int o = 1; o < nt; o <<= 1) {   // inclusive scan over the threads' sums
@@ -461,7 +533,7 @@ __device__ int tile_prefix(const AttnParams& p, int* s_pref, int* s_tmp) {
     for (int i = 0; i < per; ++i)
         if (b0 + i < p.B) {
             s_pref[b0 + i] = run;
-            run += seq_tiles(seq_range(p, b0 + i));
+            run += seq_tiles(seq_range_of(p, s_len[b0 + i]));
         }
     if (tid == nt - 1) s_pref[p.B] = s_tmp[nt - 1];
     __syncthreads();
@@ -478,8 +550,9 @@ __global__ __launch_bounds__(kWgThreads, 1) void attn_bf16_balanced_kernel(AttnP
     const int piece = blockIdx.x, hp = blockIdx.y;
     __shared__ __attribute__((aligned(16))) float smem[kSmemFloats];
     __shared__ int s_pref[kMaxBalancedB + 1];
+    __shared__ int s_len[kMaxBalancedB];
     __shared__ int s_tmp[kWgThreads];
-    const int TT = tile_prefix(p, s_pref, s_tmp);
+    const int TT = tile_prefix(p, s_pref, s_len, s_tmp);
     if (piece == 0 && hp == 0) {
         int* table = reinterpret_cast<int*>(p.part + kBalancedPartFloats);
         for (int b = threadIdx.x; b < p.B; b += blockDim.x) {
@@ -497,7 +570,7 @@ __global__ __launch_bounds__(kWgThreads, 1) void attn_bf16_balanced_kernel(AttnP
         else top = mid - 1;
     }
     for (int b = first; b < p.B && s_pref[b] < hi; ++b) {
-        const SeqRange sr = seq_range(p, b);
+        const SeqRange sr = seq_range_of(p, s_len[b]);
         const int nt = seq_tiles(sr) - 1;   // context tiles; the block tile is local tile nt
         const int g0 = max(lo, s_pref[b]) - s_pref[b], g1 = min(hi, s_pref[b + 1]) - s_pref[b];
         const int tb = sr.a0 + kTile * g0;

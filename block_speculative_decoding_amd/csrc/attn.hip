@@ -540,10 +540,25 @@ __device__ int tile_prefix(const AttnParams& p, int* s_pref, int* s_len, int* s_
     return s_pref[p.B];
 }
 
-__device__ __forceinline__ int piece_lo(int piece, int TT) { return (int)((int64_t)piece * TT / kPieces); }
+// Piece p of KV-head pair hp runs as workgroup p + 64 hp, on XCD p mod 8.
+// Workgroups on odd XCDs read these random 8-KiB page blocks 5-10% slower
+// than those on even XCDs (per-workgroup timings over many launches, on
+// several boards), so even pieces take 27 shares of the tiles and odd ones 25.
+constexpr int kPieceWEven = 27, kPieceWOdd = 25;
+constexpr int kPieceWSum = kPieces / 2 * (kPieceWEven + kPieceWOdd);
+__host__ __device__ __forceinline__ int piece_lo(int piece, int TT) {
+    const int64_t w = (int64_t)(piece >> 1) * (kPieceWEven + kPieceWOdd) + (piece & 1) * kPieceWEven;
+    return (int)(w * TT / kPieceWSum);
+}
 // The piece holding global tile t: the last one that starts at or before t.
 __device__ __forceinline__ int piece_of(int t, int TT) {
-    return min(kPieces - 1, (int)(((int64_t)(t + 1) * kPieces - 1) / TT));
+    int lo = 0, hi = kPieces - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (piece_lo(mid, TT) <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
 }
 
 __global__ __launch_bounds__(kWgThreads, 1) void attn_bf16_balanced_kernel(AttnParams p) {
@@ -845,7 +860,7 @@ AttnPlan attn_plan(const dflash_attn_args& a) {
         // Balanced pieces, while every piece fits the page-id staging of one
         // split (a piece spans at most its share of the tiles, plus one).
         const int64_t tiles = (int64_t)a.B * (cap / kTile + 2);
-        const int64_t piece_tokens = (tiles / kPieces + 2) * kTile;
+        const int64_t piece_tokens = (tiles * kPieceWEven / kPieceWSum + 2) * kTile;
         if (a.B <= kMaxBalancedB && piece_tokens <= kMaxSplit) {
             pl.balanced = true;
             pl.split_tokens = 0;

@@ -3,7 +3,9 @@
 
 * sequence b contributes ceil((S_b - a0_b) / 32) context tiles plus its
   block tile; the tiles of all sequences lie end to end, TT in all;
-* piece p (of 64) spans global tiles [floor(p TT / 64), floor((p+1) TT / 64));
+* piece p (of 64) spans global tiles [floor(W_p TT / 1664), floor(W_(p+1) TT / 1664)),
+  W_p = 52 floor(p / 2) + 27 (p mod 2): pieces on even XCDs (p even) take 27
+  shares of the tiles, those on odd XCDs 25;
 * a segment that holds a whole sequence is written directly; any other
   segment leaves a partial in slot 0 of its piece if its sequence is the
   piece's first, else slot 1;
@@ -20,6 +22,10 @@ import random
 K = 64
 
 
+def _w(p):
+    return 52 * (p // 2) + 27 * (p % 2)
+
+
 def _tiles(S):
     return (S + 31) // 32 + 1 if S > 0 else 1
 
@@ -32,7 +38,10 @@ def _check(lens):
     TT = pref[-1]
 
     def lo(p):
-        return p * TT // K
+        return _w(p) * TT // 1664
+
+    def piece_of(t):                         # the last piece starting at or before t
+        return max(p for p in range(K) if lo(p) <= t)
 
     writes, direct = {}, set()
     for piece in range(K):
@@ -54,8 +63,7 @@ def _check(lens):
     reads = {}
     for b in range(B):
         t0, t1 = pref[b], pref[b + 1] - 1
-        P0 = min(K - 1, ((t0 + 1) * K - 1) // TT)
-        P1 = min(K - 1, ((t1 + 1) * K - 1) // TT)
+        P0, P1 = piece_of(t0), piece_of(t1)
         if P0 == P1:
             assert b in direct
             continue
@@ -82,3 +90,17 @@ def test_balanced_plan_random_lengths():
         n = rng.randint(1, 200)
         top = rng.choice([40, 700, 9000])
         _check([rng.randint(0, top) for _ in range(n)])
+
+
+def test_piece_shares_follow_the_xcd_weights():
+    # 64 pieces cover every tile once; even pieces hold 27/26 and odd ones
+    # 25/26 of the mean share, to within a tile, and no piece exceeds the
+    # bound the host plan sizes the page-id staging for (TT * 27 / 1664 + 2).
+    for TT in (64, 1000, 16448, 262144):
+        lo = [_w(p) * TT // 1664 for p in range(K + 1)]
+        assert lo[0] == 0 and lo[K] == TT
+        for p in range(K):
+            size = lo[p + 1] - lo[p]
+            share = TT / K * (27 if p % 2 == 0 else 25) / 26
+            assert abs(size - share) <= 1
+            assert size <= TT * 27 // 1664 + 2

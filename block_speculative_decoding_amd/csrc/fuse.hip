@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
         sk_u = (int64_t)sk_pos * p.sk_q;
         sk_end = min((int64_t)tiles_m * tiles_n * nk, sk_u + p.sk_q);
         if (sk_u >= sk_end) return;
-    } else {
+    } else if (MODE != 2) {
         t = tile_id(p, tiles_m, tiles_n);
         if (!t.valid) return;
     }
@@ -173,12 +173,18 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
         b[0] = lds_read16<0>(bb);
         b[1] = lds_read16<kBstep * kBigPitch>(bb);
     };
+    // The head (mode 2) multiplies with the operands swapped: each 32 x 32
+    // block comes out transposed, a lane holding one row of the tile and
+    // registers running along its columns, which its epilogue stores directly.
+    auto mf = [&](const bf16x8& a, const bf16x8& b, const f32x16& c) {
+        return MODE == 2 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0)
+                         : __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    };
     auto mm = [&](const bf16x8* a, const bf16x8* b) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < 2; ++j) acc[i][j] = mf(a[i], b[j], acc[i][j]);
     };
 
     // Prologue and main loop over k-tiles [kb, ke) of the tile at (m0, n0);
@@ -237,8 +243,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int t2 = 0; t2 < 8; ++t2) {
-                acc[t2 >> 1][t2 & 1] =
-                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][t2 >> 1], fb[1][t2 & 1], acc[t2 >> 1][t2 & 1], 0, 0, 0);
+                acc[t2 >> 1][t2 & 1] = mf(fa[1][t2 >> 1], fb[1][t2 & 1], acc[t2 >> 1][t2 & 1]);
                 __builtin_amdgcn_sched_barrier(0);
                 load_part(nsrc, slot, t2);  // stage i+2 into the slot stage i used
                 __builtin_amdgcn_sched_barrier(0);
@@ -275,18 +280,14 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
         }
         return;
     }
-    const int m0 = t.tm * BMB, n0 = t.tn * BNB;
-    run(m0, n0, 0, nk);
-
-    // Lane holds column lr of each 32x32 block, rows 8*(r/4) + 4*lh + (r%4).
-    if (MODE == 2) {
-        // Round the tile to bf16 into LDS ([256 rows][256 columns]; 16-byte
-        // chunk c of row r at c ^ (r % 32)), then read it back in 16-byte
-        // chunks: each is stored to the logits and its 8 keys
-        // (head_sample.h) are folded into one (key, index) per row of the
-        // tile.
-        // The temperatures of the tile's 32 sequences, read once (after the
-        // operand stages, in the 4 KiB the K/V epilogue uses for row sums).
+    auto head_epilogue = [&](const int m0, const int n0, const int tn) {
+        // Block (i, j) of a lane holds row wr + 32 i + lr of the tile at columns
+        // wc + 32 j + 8 g + 4 lh + s in register 4 g + s.  Rounded to bf16 and
+        // traded with the lane 32 away (groups 1, 3 for 0, 2), each lane holds
+        // whole 8-column chunks g = lh, lh + 2 of its row: each goes to the
+        // logits as a 16-byte store straight from registers, and to LDS
+        // ([256 rows][256 columns]; 16-byte chunk c of row r at c ^ (r % 32))
+        // for the keys.
         float* s_temp = reinterpret_cast<float*>(lds + 2 * kBigStageBytes / 16);
         if (tid < BMB / 8) {
             const int bq = (m0 >> 3) + tid;
@@ -295,16 +296,35 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
         __syncthreads();  // every wave is done with the operand stages
         uint16_t* st = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+            const int row = wr + 32 * i + lr;
+            const int gm = m0 + row;
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 2; ++j) {
+                uint32_t w[4][2];   // group g: bf16 pairs of its 4 columns
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = wr + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    const int col = wc + kBstep * j + lr;
-                    st[row * 256 + 8 * ((col >> 3) ^ (row & 31)) + (col & 7)] =
-                        (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
+                for (int g = 0; g < 4; ++g) {
+                    w[g][0] = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+                    w[g][1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
                 }
+                // Send the groups the partner completes (lh 0: 1, 3; lh 1: 0, 2).
+                uint32_t r[2][2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+                        r[h][e] = (uint32_t)__shfl_xor((int)(lh ? w[2 * h][e] : w[2 * h + 1][e]), 32);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t o0 = lh ? w[2 * h + 1][0] : w[2 * h][0];   // own half of group 2 h + lh
+                    const uint32_t o1 = lh ? w[2 * h + 1][1] : w[2 * h][1];
+                    const uint4 c = lh ? make_uint4(r[h][0], r[h][1], o0, o1) : make_uint4(o0, o1, r[h][0], r[h][1]);
+                    const int cg = (wc + 32 * j) / 8 + 2 * h + lh;   // chunk of the tile's 32
+                    if (gm < p.M) *reinterpret_cast<uint4*>(p.out_bf16 + (int64_t)gm * p.N + n0 + 8 * cg) = c;
+                    *reinterpret_cast<uint4*>(st + row * 256 + 8 * (cg ^ (row & 31))) = c;
+                }
+            }
+        }
         __syncthreads();
         // Four threads per row, 64 columns (eight chunks) each; two passes of
         // 128 rows.  The row's four threads are a quad: two DPP swaps reduce it.
@@ -321,13 +341,12 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
             const StatScale sc = stat_scale(greedy ? 1.f : Tb);
             float best = -INFINITY, sm = -INFINITY, ss = 0.f;
             int bi = 0x7FFFFFFF;
+            if (active) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int cg = 8 * q + c;
-                const int64_t i0 = (int64_t)n0 + 8 * cg;
-                const uint4 w = *reinterpret_cast<const uint4*>(st + row * 256 + 8 * (cg ^ (row & 31)));
-                if (gm < p.M) *reinterpret_cast<uint4*>(p.out_bf16 + (int64_t)gm * p.N + i0) = w;
-                if (active) {
+                for (int c = 0; c < 8; ++c) {
+                    const int cg = 8 * q + c;
+                    const int64_t i0 = (int64_t)n0 + 8 * cg;
+                    const uint4 w = *reinterpret_cast<const uint4*>(st + row * 256 + 8 * (cg ^ (row & 31)));
                     float f[8];
                     f[0] = lo_bf16(w.x); f[1] = hi_bf16(w.x); f[2] = lo_bf16(w.y); f[3] = hi_bf16(w.y);
                     f[4] = lo_bf16(w.z); f[5] = hi_bf16(w.z); f[6] = lo_bf16(w.w); f[7] = hi_bf16(w.w);
@@ -342,13 +361,36 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParam
                 stat_merge(sm, ss, dpp_f<kDppXor2>(sm, -INFINITY), dpp_f<kDppXor2>(ss, 0.f), sc);
             }
             if (active && q == 0) {
-                const int64_t pi = ((int64_t)b * 7 + k - 1) * hp.nparts + t.tn;
+                const int64_t pi = ((int64_t)b * 7 + k - 1) * hp.nparts + tn;
                 hp.part[pi] = {best, bi};
                 if (stats) hp.spart[pi] = {sm, ss};
             }
         }
+    };
+    if (MODE == 2) {
+        // Persistent over the tiles: XCD x owns the tile range
+        // [x * per, (x + 1) * per) and its K workgroups take every K-th tile of
+        // it, so a tile's logit stores drain while the next tile multiplies.
+        const int T = tiles_m * tiles_n, per = (T + kXcds - 1) / kXcds, K = gridDim.x / kXcds;
+        const int x = blockIdx.x % kXcds;
+        for (int loc = blockIdx.x / kXcds; loc < per; loc += K) {
+            const int L = x * per + loc;
+            if (L >= T) break;
+            const int in_group = kGemmGroupM * tiles_n;
+            const int first_m = L / in_group * kGemmGroupM;
+            const int gm = min(tiles_m - first_m, kGemmGroupM);
+            const int q = L % in_group;
+            const int tm = first_m + q % gm, tn = q / gm;
+            run(tm * BMB, tn * BNB, 0, nk);
+            head_epilogue(tm * BMB, tn * BNB, tn);
+            __syncthreads();  // every wave is done with the LDS before the next tile's loads
+        }
         return;
     }
+    const int m0 = t.tm * BMB, n0 = t.tn * BNB;
+    run(m0, n0, 0, nk);
+
+    // Lane holds column lr of each 32x32 block, rows 8*(r/4) + 4*lh + (r%4).
     if (!KV) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -751,7 +793,8 @@ FusePlan fuse_plan(const dflash_fuse_args& a) {
 
 hipError_t launch_gemm_big_head(const GemmParams& g, const HeadEpilogue& hp, hipStream_t s) {
     const int tiles = ((g.M + BMB - 1) / BMB) * (g.N / BNB);
-    gemm_bf16_big_kernel<2><<<(tiles + kXcds - 1) / kXcds * kXcds, kBigThreads, 0, s>>>(g, KvEpilogue{}, hp);
+    const int grid = std::min((tiles + kXcds - 1) / kXcds * kXcds, kSkWorkgroups);
+    gemm_bf16_big_kernel<2><<<grid, kBigThreads, 0, s>>>(g, KvEpilogue{}, hp);
     return hipGetLastError();
 }
 

@@ -93,8 +93,8 @@ __host__ __device__ __forceinline__ int sk_tile_index(int tm, int tn, int tiles_
 
 
 // MODE 0: fp32 partials to p.part (the fusion GEMM); 1: the K/V epilogue
-// (ep); 2: the shared head's epilogue (hp): bf16 logits through LDS and the
-// draft keys of its rows.
+// (ep); 2: the shared head's epilogue (hp): bf16 logits stored from
+// registers and the draft keys of its rows (persistent over the tiles).
 template <int MODE, bool SK = false>
 __global__ __launch_bounds__(kBigThreads, 1) void gemm_bf16_big_kernel(GemmParams p, KvEpilogue ep, HeadEpilogue hp) {
     static_assert(!SK || MODE == 0, "stream-K only for the fp32-partial GEMM");

@@ -112,8 +112,9 @@ struct HeadEpilogue {
 };
 
 // bf16 projection of the head rows with the sampling epilogue: 256 x 256
-// tiles (N % 256 == 0, ks = 1), logits stored through LDS as 16-byte
-// chunks to out_bf16.  (Defined with the fusion kernels.)
+// tiles (N % 256 == 0, ks = 1), at most one workgroup per CU looping over
+// them, logits stored from registers as 16-byte chunks to out_bf16.
+// (Defined with the fusion kernels.)
 hipError_t launch_gemm_big_head(const GemmParams& g, const HeadEpilogue& ep, hipStream_t s);
 
 }  // namespace dflash

@@ -486,7 +486,7 @@ int dflash_spec_verify(const dflash_verify_args* args, void* workspace,
  * array of dflash_verify_scratch_bytes() bytes (4 MiB) that the library holds
  * on every GPU it runs on until the process ends.  It calls no allocating
  * routine.  Calls whose dflash_verify_workspace_size exceeds that size are
- * rejected with DFLASH_EWORKSPACE (e.g. B = 1048 at V = 262144 still fits).
+ * rejected with DFLASH_EWORKSPACE (e.g. B = 1409 at V = 262144 still fits).
  * Every allocation-free call on a GPU uses that GPU's one array: calls that
  * overlap on one GPU (concurrent streams, or threads without ordering) race
  * and must not be issued; calls ordered on one stream are fine.  The first

@@ -146,17 +146,17 @@ def test_verify_noalloc_validation(lib):
     n = ctypes.c_size_t()
     assert lib.dflash_verify_scratch_bytes(ctypes.byref(n)) == 0 and n.value == 4 << 20
     cap = n.value
-    assert _ws(lib, "verify", _verify_args(B=1048, V=262144))[1] <= cap
-    assert _ws(lib, "verify", _verify_args(B=1049, V=262144))[1] > cap
+    assert _ws(lib, "verify", _verify_args(B=1409, V=262144))[1] <= cap
+    assert _ws(lib, "verify", _verify_args(B=1410, V=262144))[1] > cap
 
     def call(a):
         return lib.dflash_spec_verify_noalloc(ctypes.byref(a), None)
 
     def big(B, V):
         return _verify_args(B=B, V=V, t_batch_stride=8 * V, t_row_stride=V, d_batch_stride=7 * V, d_row_stride=V)
-    assert call(big(1049, 262144)) == -4
+    assert call(big(1410, 262144)) == -4
     msg = lib.dflash_last_error().decode()
-    assert "dflash_spec_verify_noalloc" in msg and str(cap) in msg and "B = 1049" in msg
+    assert "dflash_spec_verify_noalloc" in msg and str(cap) in msg and "B = 1410" in msg
     assert call(big(4096, 1 << 20)) == -4
     assert call(_verify_args(target_logits=None)) == -1
     assert call(_verify_args(V=4100)) == -1

@@ -101,7 +101,7 @@ extern "C" {
 #define DFLASH_MAX_LAYERS 5      /* draft layers */
 #define DFLASH_INTER      5120   /* SwiGLU width (derived from the parameter count) */
 
-#define DFLASH_VERSION 10500     /* 1.5.0 */
+#define DFLASH_VERSION 10501     /* 1.5.1: verification workspace sized for 4096-entry draw chunks */
 
 /* dflash_attn_args.split_tokens: cut the context tiles of all sequences,
  * laid end to end (each sequence's 32-token tiles, then its block's keys as

@@ -55,7 +55,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_struct_sizes_and_version(lib):
     from block_speculative_decoding_amd import _lib
-    assert lib.dflash_version() == 10500
+    assert lib.dflash_version() == 10501
     for kind, st in enumerate(_lib.ARG_STRUCTS):
         assert lib.dflash_args_size(kind) == ctypes.sizeof(st)
     assert lib.dflash_args_size(len(_lib.ARG_STRUCTS)) == 0

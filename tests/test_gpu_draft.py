@@ -106,7 +106,7 @@ def _mlp_check(x_in, o_in, w, g_final, h, x_out, y, chained):
     return errs
 
 
-@pytest.mark.parametrize("B,final", [(1, False), (3, True), (40, True)])
+@pytest.mark.parametrize("B,final", [(1, False), (3, True), (40, True), (65, False), (128, True)])
 def test_draft_mlp_bf16_ragged_rows(B, final):
     import block_speculative_decoding_amd as dfl
     w = _weights(14, BF16)

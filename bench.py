@@ -74,6 +74,10 @@ def parse():
                     help="only time ctx_fuse on the serving batch's new rows in its place in the cycle, "
                          "back to back (weights left in the MALL) and cold (MALL flushed before each "
                          "call), and torch's bf16 matmul on the same two GEMM shapes warm and cold")
+    ap.add_argument("--head-gemm-probe", action="store_true",
+                    help="only time torch's bf16 matmul (hipBLASLt) on the shared head's shape at the serving "
+                         "batch, [512,2560] x [262144,2560]^T with bf16 out, for comparison with the head's "
+                         "greedy call")
     return ap.parse_args()
 
 
@@ -374,6 +378,22 @@ def cpu_baseline(wl):
                    f"sequences, 32 greedy + 32 sampled ({t_ver:.2f}s); "
                    f"{t_fuse + t_attn + t_ver:.1f}s measured, {cycle:.1f}s per scaled cycle"),
     }
+
+
+def head_gemm_probe():
+    """torch's bf16 matmul (hipBLASLt) on the shared LM head's product at the
+    serving batch: 64 sequences x 8 block rows against a 262144-row head of
+    width 2560, bf16 out (268 MB), with no sampling fold."""
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(SEED)
+    a = torch.randn(512, 2560, device=dev, generator=g).to(torch.bfloat16)
+    w = (torch.randn(262144, 2560, device=dev, generator=g) * 0.02).to(torch.bfloat16)
+    out = torch.empty(512, 262144, device=dev, dtype=torch.bfloat16)
+    ms = timed(torch, lambda: torch.matmul(a, w.t(), out=out), warmup=3, reps=20)
+    fl = 2 * 512 * 262144 * 2560
+    print(json.dumps({"head_gemm_probe": {"shape": "[512,2560] x [262144,2560]^T -> bf16", "torch_matmul_ms": round(ms, 4),
+                                          "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1)}}), flush=True)
 
 
 def timed(torch, fn, warmup=2, reps=5):
@@ -820,6 +840,9 @@ def main():
         return
     if args.serving_gemm_probe:
         serving_gemm_probe()
+        return
+    if args.head_gemm_probe:
+        head_gemm_probe()
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",

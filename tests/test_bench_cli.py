@@ -27,7 +27,8 @@ def test_measurement_modes_are_offered():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 0
-    for flag in ("--steps", "--warmup", "--no-cpu-baseline", "--copy-probe", "--gemm-probe", "--serving-gemm-probe"):
+    for flag in ("--steps", "--warmup", "--no-cpu-baseline", "--copy-probe", "--gemm-probe", "--serving-gemm-probe",
+                 "--head-gemm-probe"):
         assert flag in r.stdout
 
 
